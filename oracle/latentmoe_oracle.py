@@ -1,0 +1,324 @@
+"""CPU oracle of the Stable LatentMoE forward.  TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check of ``__graft_entry__`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or run this module.  The
+product path (the HIP library and its Python binding) never touches it.  It
+shares no code with the GPU path; its only dependency besides numpy is the
+seeded input generator ``lmoe_synth`` (used to regenerate large weights
+lazily, never for arithmetic).
+
+Everything is plain numpy in fp64.  Stored inputs (fp32, or bf16 bit
+patterns) convert to fp64 exactly and no intermediate is rounded.  Library
+primitives used as single steps: matrix products, a stable argsort, bincount,
+cumsum and ``np.add.at`` (scatter-add).
+
+Citation keys (pages of the K3 repository):
+  [sec-07]  raw ``notes/sections/sec-07.tex`` @47c72e5, chapter "SiTU-GLU
+            and Stable LatentMoE": the SiTU-GLU equation and property table,
+            the component table, the five-step compute flow, the routing code
+            and its three notes, the sparse-execution section (permute-
+            dispatch + padded bmm) and the load-balancing section.
+  [diff]    compare page 584f7e9...main, ``kda/layers/latent_moe.py`` hunks
+            (``_routed_u``, ``_route``, ``_balancing_losses``, ``forward``).
+  [tests]   same compare page, ``tests/integration/test_k3_arch.py``
+            (``_dense_moe_forward`` helper and the MoE tests).
+
+Readings where the pages are silent (each listed in the design notes):
+  * RMSNorm is imported but never defined on the pages: here
+    ``w * u / sqrt(mean(u^2) + eps)`` with eps inside the square root.
+  * Top-k ties: larger ``s+b`` first; equal values go to the lower expert id.
+  * The denominator clamp ``max(sum, 1e-9)`` of the routing code is kept.
+
+Pins (tests marked ``not gpu`` in tests/test_oracle_*.py):
+  router   closed-form case of the pages' zero-grad test, brute-force sort,
+           bias-only-in-selection, all-equal scores (tie rule), k = R.
+  dispatch brute-force sort on tiny inputs, counts/offsets/C invariants.
+  routed   sparse == dense-then-mask (two independent code paths), identical
+           experts, k = R mixture, W_g = 0.
+  SiTU     |gate * up| < beta1*beta2, near-origin SwiGLU series bound,
+           large-beta limit == SwiGLU (torch.nn.functional.silu).
+  layer    large-beta layer == a torch library composition (F.linear, F.silu,
+           F.rms_norm, torch.topk), token-permutation equivariance,
+           linearity in the shared down projection.
+  No golden output values are printed on the pages, so absolute outputs of
+  the configured layers are pinned only through the above.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Callable
+
+import numpy as np
+
+# ---------------------------------------------------------------- SiTU-GLU
+
+
+def sigmoid(x: np.ndarray) -> np.ndarray:
+    """Logistic function in fp64, evaluated without overflow for large |x|."""
+    x = np.asarray(x, dtype=np.float64)
+    out = np.empty_like(x)
+    pos = x >= 0
+    out[pos] = 1.0 / (1.0 + np.exp(-x[pos]))
+    ex = np.exp(x[~pos])
+    out[~pos] = ex / (1.0 + ex)
+    return out
+
+
+def situ_hidden(a_g: np.ndarray, a_u: np.ndarray, beta1: float, beta2: float) -> np.ndarray:
+    """Gated hidden of SiTU-GLU, [sec-07] SiTU-GLU equation:
+    gate = beta1*tanh(a_g/beta1)*sigmoid(a_g), up = beta2*tanh(a_u/beta2),
+    hidden = gate * up, with a_g = W_g v and a_u = W_u v."""
+    gate = beta1 * np.tanh(a_g / beta1) * sigmoid(a_g)
+    up = beta2 * np.tanh(a_u / beta2)
+    return gate * up
+
+
+def situ(v: np.ndarray, w_g: np.ndarray, w_u: np.ndarray, w_o: np.ndarray,
+         beta1: float, beta2: float) -> np.ndarray:
+    """SiTU-GLU expert on rows of v ([M, in] -> [M, in]); weights are
+    nn.Linear-shaped [out, in]: w_g, w_u [ff, in], w_o [in, ff]
+    ([sec-07] SiTU-GLU equation and listing; no biases)."""
+    return situ_hidden(v @ w_g.T, v @ w_u.T, beta1, beta2) @ w_o.T
+
+
+# ----------------------------------------------------------------- routing
+
+
+@dataclass
+class Routes:
+    logits: np.ndarray  # [N, R]  W_r x
+    s: np.ndarray       # [N, R]  sigmoid(logits)
+    ids: np.ndarray     # [N, k]  int64, descending s+b, ties to the lower id
+    p: np.ndarray       # [N, k]  s_i / sum_{j in T} s_j
+    margin: np.ndarray  # [N]     (s+b)_(k) - (s+b)_(k+1), +inf when k == R
+
+
+def route_from_logits(logits: np.ndarray, bias: np.ndarray, k: int) -> Routes:
+    """K3 sigmoid routing ("K3 eq.13"), [sec-07] compute-flow step 2 and the
+    routing code with its three notes: s = sigmoid(l); T = TopK(s + b, k);
+    p_i = s_i / sum_{j in T} s_j.  The bias enters the selection only, p uses
+    the raw s; the sum is clamped below at 1e-9 as in the routing code."""
+    logits = np.asarray(logits, dtype=np.float64)
+    N, R = logits.shape
+    if not 1 <= k <= R:
+        raise ValueError("need 1 <= k <= R")
+    s = sigmoid(logits)
+    v = s + np.asarray(bias, dtype=np.float64)[None, :]
+    # stable sort of -v: equal values keep ascending expert order
+    order = np.argsort(-v, axis=1, kind="stable")
+    ids = order[:, :k]
+    sel = np.take_along_axis(s, ids, axis=1)
+    p = sel / np.maximum(sel.sum(axis=1, keepdims=True), 1e-9)
+    if k < R:
+        vs = np.take_along_axis(v, order[:, k - 1:k + 1], axis=1)
+        margin = vs[:, 0] - vs[:, 1]
+    else:
+        margin = np.full(N, np.inf)
+    return Routes(logits, s, ids.astype(np.int64), p, margin)
+
+
+def route(x: np.ndarray, w_router: np.ndarray, bias: np.ndarray, k: int) -> Routes:
+    """Router on the full-width input: logits = W_r x ([sec-07] component
+    table: the router maps d -> n_routed and reads x, not the latent z)."""
+    return route_from_logits(x @ w_router.T, bias, k)
+
+
+def route_softmax_topk(logits: np.ndarray, k: int) -> tuple[np.ndarray, np.ndarray]:
+    """Legacy router removed by the [diff] forward hunk: ids = top-k of the
+    raw logits, weights = softmax over the k selected logits (ties to the
+    lower id, as above)."""
+    logits = np.asarray(logits, dtype=np.float64)
+    order = np.argsort(-logits, axis=1, kind="stable")
+    ids = order[:, :k]
+    sel = np.take_along_axis(logits, ids, axis=1)
+    e = np.exp(sel - sel.max(axis=1, keepdims=True))
+    return ids.astype(np.int64), e / e.sum(axis=1, keepdims=True)
+
+
+def balancing_losses(logits: np.ndarray, ids: np.ndarray, n_routed: int) -> tuple[float, float]:
+    """Unscaled Switch/GShard auxiliary loss and router z-loss, [sec-07]
+    load-balancing section: f_e = (#pairs routed to e) / (N k),
+    P_e = mean over tokens of sigmoid(l)_e, L_aux = R * sum_e f_e P_e,
+    L_z = mean over tokens of (logsumexp_j l_j)^2.  (The layer multiplies
+    them by its coefficients, 1e-2 and 1e-3 by default.)"""
+    logits = np.asarray(logits, dtype=np.float64)
+    counts = np.bincount(np.asarray(ids).reshape(-1), minlength=n_routed).astype(np.float64)
+    frac = counts / max(counts.sum(), 1.0)
+    prob_mean = sigmoid(logits).mean(axis=0)
+    aux = n_routed * float((frac * prob_mean).sum())
+    m = logits.max(axis=1, keepdims=True)
+    lse = (m + np.log(np.exp(logits - m).sum(axis=1, keepdims=True)))[:, 0]
+    return aux, float(np.mean(lse ** 2))
+
+
+# ---------------------------------------------------------------- dispatch
+
+
+@dataclass
+class Dispatch:
+    counts: np.ndarray     # [R]      pairs per expert
+    offsets: np.ndarray    # [R]      exclusive prefix sum of counts
+    order: np.ndarray      # [N*k]    flat pair index q = n*k + j, stably sorted by expert
+    local_pos: np.ndarray  # [N*k]    position of sorted pair inside its expert
+    capacity: int          # C = max counts
+
+
+def dispatch(ids: np.ndarray, n_routed: int) -> Dispatch:
+    """Permute-dispatch bookkeeping, [sec-07] sparse-execution section and
+    the [diff] ``_routed_u`` hunk: flatten the (token, slot) pairs in token
+    order, stable-sort them by expert id, count pairs per expert, take the
+    exclusive prefix sum as offsets, the position inside the expert as
+    local_pos and the largest count as the capacity C."""
+    eid = np.asarray(ids, dtype=np.int64).reshape(-1)
+    order = np.argsort(eid, kind="stable")
+    counts = np.bincount(eid, minlength=n_routed)
+    offsets = np.cumsum(counts) - counts
+    local_pos = np.arange(eid.size) - offsets[eid[order]]
+    C = int(counts.max()) if eid.size else 0
+    return Dispatch(counts, offsets, order, local_pos, C)
+
+
+def padded_layout(z: np.ndarray, ids: np.ndarray, n_routed: int, disp: Dispatch | None = None) -> np.ndarray:
+    """The [R, C, l] tensor of the sparse-execution section: row local_pos of
+    expert e holds z of the token behind that sorted pair; unused rows are 0."""
+    if disp is None:
+        disp = dispatch(ids, n_routed)
+    k = np.asarray(ids).shape[1]
+    N, ell = z.shape
+    padded = np.zeros((n_routed, disp.capacity, ell), dtype=z.dtype)
+    eid = np.asarray(ids, dtype=np.int64).reshape(-1)[disp.order]
+    tok = disp.order // k
+    padded[eid, disp.local_pos] = z[tok]
+    return padded
+
+
+# ------------------------------------------------------------ routed experts
+
+ExpertFn = Callable[[int], tuple[np.ndarray, np.ndarray, np.ndarray]]
+
+
+def routed_sparse(z: np.ndarray, ids: np.ndarray, p: np.ndarray, experts: ExpertFn,
+                  n_routed: int, beta1: float, beta2: float) -> np.ndarray:
+    """u = sum_{i in T} p_i E_i(z), executed the sparse way of the
+    sparse-execution section: sort pairs by expert, run each expert on the
+    padded block of its pairs, read back only the valid rows, weight them by
+    p and scatter-add into token order.  Experts with no pair are skipped
+    (their rows would be all padding)."""
+    z = np.asarray(z, dtype=np.float64)
+    N, ell = z.shape
+    k = np.asarray(ids).shape[1]
+    u = np.zeros((N, ell), dtype=np.float64)
+    if N * k == 0:
+        return u
+    disp = dispatch(ids, n_routed)
+    padded = padded_layout(z, ids, n_routed, disp)
+    pw = np.asarray(p, dtype=np.float64).reshape(-1)[disp.order]
+    tok = disp.order // k
+    eid_sorted = np.asarray(ids, dtype=np.int64).reshape(-1)[disp.order]
+    out = np.zeros_like(padded)
+    for e in range(n_routed):
+        if disp.counts[e] == 0:
+            continue
+        w_g, w_u, w_o = experts(e)
+        out[e] = situ(padded[e], w_g, w_u, w_o, beta1, beta2)
+    weighted = pw[:, None] * out[eid_sorted, disp.local_pos]
+    np.add.at(u, tok, weighted)
+    return u
+
+
+def routed_dense(z: np.ndarray, ids: np.ndarray, p: np.ndarray, experts: ExpertFn,
+                 n_routed: int, beta1: float, beta2: float) -> np.ndarray:
+    """Dense reference of the [tests] ``_dense_moe_forward`` helper: run every
+    expert on every token, then for each slot j take the selected expert's
+    row and add p_j times it.  Cost R*N; tiny inputs only."""
+    z = np.asarray(z, dtype=np.float64)
+    N, ell = z.shape
+    all_out = np.stack([situ(z, *experts(e), beta1, beta2) for e in range(n_routed)], axis=1)
+    u = np.zeros((N, ell), dtype=np.float64)
+    rows = np.arange(N)
+    for j in range(np.asarray(ids).shape[1]):
+        u += np.asarray(p)[:, j:j + 1] * all_out[rows, np.asarray(ids)[:, j]]
+    return u
+
+
+# ------------------------------------------------------------ shared + merge
+
+
+def shared_sum(x: np.ndarray, sh_g: np.ndarray, sh_u: np.ndarray, sh_o: np.ndarray,
+               beta1: float, beta2: float) -> np.ndarray:
+    """s_sh = sum_j E_j^sh(x), full-width SiTU experts applied to every
+    token and summed in index order ([sec-07] compute-flow step 4)."""
+    x = np.asarray(x, dtype=np.float64)
+    out = np.zeros_like(x)
+    for j in range(sh_g.shape[0]):
+        out += situ(x, sh_g[j], sh_u[j], sh_o[j], beta1, beta2)
+    return out
+
+
+def rmsnorm(u: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
+    """RMSNorm over the last axis: w * u / sqrt(mean(u^2) + eps).  (The pages
+    import RMSNorm without defining it; this is the standard definition.)"""
+    u = np.asarray(u, dtype=np.float64)
+    return np.asarray(w, dtype=np.float64) * u / np.sqrt(np.mean(u * u, axis=-1, keepdims=True) + eps)
+
+
+# ------------------------------------------------------------------- layer
+
+
+@dataclass
+class Weights:
+    """fp64 view of the layer's parameters.  ``experts(e)`` returns the routed
+    expert's (w_g [f_r,l], w_u [f_r,l], w_o [l,f_r]); it may regenerate them
+    lazily so that host memory never holds the full routed set."""
+    w_down: np.ndarray    # [l, d]
+    w_router: np.ndarray  # [R, d]
+    bias: np.ndarray      # [R]
+    experts: ExpertFn
+    sh_g: np.ndarray      # [n_s, f_s, d]
+    sh_u: np.ndarray      # [n_s, f_s, d]
+    sh_o: np.ndarray      # [n_s, d, f_s]
+    w_up: np.ndarray      # [d, l]
+    rms_w: np.ndarray     # [l]
+    n_routed: int
+    top_k: int
+    beta1: float = 4.0
+    beta2: float = 25.0
+    rms_eps: float = 1e-6
+
+
+def weights_from_arrays(a: dict, top_k: int, beta1=4.0, beta2=25.0, rms_eps=1e-6) -> Weights:
+    """Weights from in-memory fp64 arrays (keys as the input generator names them)."""
+    f = lambda n: np.asarray(a[n], dtype=np.float64)  # noqa: E731
+    w_g, w_u, w_o = f("w_g"), f("w_u"), f("w_o")
+    d = f("w_down").shape[1]
+    sh = {n: (f(n) if n in a else np.zeros((0, 1, d))) for n in ("sh_g", "sh_u")}
+    sh_o = f("sh_o") if "sh_o" in a else np.zeros((0, d, 1))
+    return Weights(f("w_down"), f("w_router"), f("bias"), lambda e: (w_g[e], w_u[e], w_o[e]),
+                   sh["sh_g"], sh["sh_u"], sh_o, f("w_up"), f("rms_w"), w_g.shape[0], top_k,
+                   beta1, beta2, rms_eps)
+
+
+def forward(x: np.ndarray, W: Weights, ids: np.ndarray | None = None, dense: bool = False) -> dict:
+    """One Stable LatentMoE forward, the five steps of [sec-07] compute flow:
+      1. z = W_down x
+      2. s = sigmoid(W_r x), T = TopK(s + b, k), p_i = s_i / sum_T s
+      3. u = sum_{i in T} p_i E_i^rt(z)          (routed SiTU experts, width l)
+      4. s_sh = sum_j E_j^sh(x)                    (shared SiTU experts, width d)
+      5. y = s_sh + W_up RMSNorm(u)
+    ``ids`` substitutes externally chosen routes (p is then taken from this
+    oracle's own s over those ids).  ``dense`` selects the dense-then-mask
+    routed path instead of the sparse one."""
+    x = np.asarray(x, dtype=np.float64)
+    z = x @ W.w_down.T
+    r = route(x, W.w_router, W.bias, W.top_k)
+    if ids is None:
+        ids, p = r.ids, r.p
+    else:
+        ids = np.asarray(ids, dtype=np.int64)
+        sel = np.take_along_axis(r.s, ids, axis=1)
+        p = sel / np.maximum(sel.sum(axis=1, keepdims=True), 1e-9)
+    fn = routed_dense if dense else routed_sparse
+    u = fn(z, ids, p, W.experts, W.n_routed, W.beta1, W.beta2)
+    s_sh = shared_sum(x, W.sh_g, W.sh_u, W.sh_o, W.beta1, W.beta2)
+    y = s_sh + rmsnorm(u, W.rms_w, W.rms_eps) @ W.w_up.T
+    return {"y": y, "z": z, "u": u, "s_sh": s_sh, "ids": ids, "p": p, "routes": r}

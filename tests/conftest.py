@@ -1,0 +1,18 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (HIP device) to run")
+    config.addinivalue_line("markers", "slow: long-running (full-size shapes)")
+
+
+def pytest_collection_modifyitems(config, items):
+    # run GPU parity tests in a stable, cheap-first order
+    items.sort(key=lambda it: 1 if it.get_closest_marker("slow") else 0)
