@@ -1,0 +1,188 @@
+"""Throughput of the MI355X Stable LatentMoE forward on one GPU.
+
+One step = one whole-layer forward (latent GEMM, routing, dispatch, shared and
+routed SiTU experts, RMSNorm merge) over one batch of seeded synthetic input
+already resident in HBM.  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import lmoe_synth as S  # noqa: E402
+
+METRIC = "LatentMoE fwd tokens/s + TFLOP/s at 1 MI355X; % of bf16 MFMA / HBM roofline"
+PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # dense matrix peaks (fp16 == bf16)
+PEAK_HBM_GBS = 8000.0
+
+
+def step_models(cfg, counts):
+    """Algorithmic FLOPs and HBM bytes of each timed step (2 FLOP per multiply-add;
+    each needed weight read once, only experts with pairs; activations in/out
+    once at their stored width).  Returns {step: (flops, bytes)}."""
+    N, d, l, R, k = cfg.n_tokens, cfg.d_model, cfg.d_latent, cfg.n_routed, cfg.top_k
+    fr, fs, ns = cfg.ff_routed, cfg.ff_shared, cfg.n_shared
+    es = 2 if cfg.dtype == "bf16" else 4
+    P = N * k
+    U = int((counts > 0).sum())
+    return {
+        "latent_gemm": (2.0 * N * d * l, es * (N * d + l * d + N * l)),
+        "router": (2.0 * N * d * R, es * (N * d + R * d) + 4 * N * R + 8 * N * k),
+        "dispatch": (0.0, 4 * P * 2 + 8 * R),
+        "shared_gateup": (4.0 * N * d * fs * ns, es * (N * d + 2 * ns * fs * d + N * ns * fs)),
+        "routed_gateup": (4.0 * P * l * fr, es * (2 * U * fr * l + P * l + P * fr)),
+        "routed_down": (2.0 * P * fr * l, es * (U * l * fr + P * fr) + 4 * P * l),
+        "combine_rmsnorm": (0.0, 4 * P * l + es * N * l),
+        "merge_gemm": (2.0 * N * (ns * fs + l) * d, es * (N * (ns * fs + l) + d * (ns * fs + l) + N * d)),
+    }
+
+
+def cpu_baseline(cfg, n_sample: int):
+    """The oracle (test infrastructure, untuned) on the first n_sample tokens of
+    the workload, on this host's cores.  Weights the sample needs are
+    generated beforehand (untimed); the timed region is the oracle forward."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle as O
+
+    W = O.config_weights(cfg, cache_experts=0)
+    x = O.config_x(cfg, rows=np.arange(n_sample))
+    routes = O.route(x, W.w_router, W.bias, cfg.top_k)
+    need = sorted(set(routes.ids.reshape(-1).tolist()))
+    per = cfg.ff_routed * cfg.d_latent
+    stored = {e: tuple(S.host_tensor(cfg, n, e * per, per) for n in ("w_g", "w_u", "w_o")) for e in need}
+    fr, l = cfg.ff_routed, cfg.d_latent
+
+    def experts(e):  # the oracle reads stored (bf16 / fp32) weights as exact fp64
+        g, u, o = stored[e]
+        return (S.to_f64(g, cfg.dtype).reshape(fr, l), S.to_f64(u, cfg.dtype).reshape(fr, l),
+                S.to_f64(o, cfg.dtype).reshape(l, fr))
+
+    W.experts = experts
+    t0 = time.perf_counter()
+    O.forward(x, W)
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": n_sample / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n_sample} tokens of {cfg.name} (all five steps, fp64 numpy; "
+                      f"{len(need)} routed experts touched); {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="k3full_n8192", choices=sorted(S.CONFIGS))
+    ap.add_argument("--cpu-sample", type=int, default=8, help="tokens for the CPU oracle baseline (0: skip)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the layer would shard tokens or experts; see the design notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mixture_experts_ffn_sigmoid_amd as M
+    from tests.gpu_util import alloc_forward, device_layer_inputs
+
+    cfg = S.CONFIGS[args.workload]
+    M.load()
+    dev = device_layer_inputs(cfg)  # generated in HBM by the seeded generator
+    bufs = alloc_forward(cfg)
+    W = M.weights_struct(dev)
+    torch.cuda.synchronize()
+
+    def fwd_plain():
+        M.latentmoe_forward(bufs["dims"], W, dev["x"], bufs["y"], bufs["ids"], bufs["probs"],
+                            bufs["counts"], want_capacity=False, workspace=bufs["ws"])
+
+    for _ in range(args.warmup):
+        fwd_plain()
+    torch.cuda.synchronize()
+
+    ev_sets = [[torch.cuda.Event(enable_timing=True) for _ in range(M.TIMING_EVENTS)]
+               for _ in range(args.steps)]
+    for evs in ev_sets:  # torch creates the underlying hipEvent on first record
+        for e in evs:
+            e.record()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record()
+    for s in range(args.steps):
+        M.latentmoe_forward_timed(bufs["dims"], W, dev["x"], bufs["y"], bufs["ids"], bufs["probs"],
+                                  bufs["counts"], ev_sets[s], workspace=bufs["ws"])
+    end.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_total = start.elapsed_time(end)
+    ms_step = ms_total / args.steps
+
+    step_ms = {name: float(np.mean([ev[i].elapsed_time(ev[i + 1]) for ev in ev_sets]))
+               for i, name in enumerate(M.STEP_NAMES)}
+    counts = bufs["counts"].cpu().numpy()
+    C = int(counts.max())
+    models = step_models(cfg, counts)
+    peak_tf = PEAK_MFMA_TFLOPS[cfg.dtype]
+    steps_out = {}
+    for name, ms in step_ms.items():
+        fl, by = models[name]
+        steps_out[name] = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1),
+                           "gbs": round(by / ms / 1e6, 1)}
+    dominant = max(step_ms, key=step_ms.get)
+    fl, by = models[dominant]
+    t_dom = step_ms[dominant] / 1e3
+    mfma_bound = fl / (peak_tf * 1e12) >= by / (PEAK_HBM_GBS * 1e9)
+    if mfma_bound:
+        roof = {"kernel": dominant, "bound": "mfma", "achieved": round(fl / t_dom / 1e12, 1),
+                "peak": peak_tf, "unit": "TFLOP/s"}
+    else:
+        roof = {"kernel": dominant, "bound": "hbm", "achieved": round(by / t_dom / 1e9, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = None
+
+    flops = cfg.flops()
+    tok_s = cfg.n_tokens / (ms_step / 1e3)
+    out = {
+        "metric": METRIC,
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "n_tokens": cfg.n_tokens, "d_model": cfg.d_model,
+                   "d_latent": cfg.d_latent, "n_routed": cfg.n_routed, "top_k": cfg.top_k,
+                   "n_shared": cfg.n_shared, "ff_routed": cfg.ff_routed, "ff_shared": cfg.ff_shared,
+                   "parallelism": "none (1 GPU)"},
+        "tflops": round(flops / (ms_step / 1e3) / 1e12, 1),
+        "mfma_frac": round(flops / (ms_step / 1e3) / 1e12 / peak_tf, 4),
+        "capacity": C,
+        "wall_s": round(t_wall, 3),
+        "steps_breakdown": steps_out,
+        "roofline": roof,
+    }
+    if args.cpu_sample > 0:
+        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_sample)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

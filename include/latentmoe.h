@@ -1,0 +1,185 @@
+/* latentmoe.h - C ABI of the MI355X (gfx950) Stable LatentMoE forward.
+ *
+ * The layer (K3 notes, raw notes/sections/sec-07.tex @47c72e5, chapter
+ * "SiTU-GLU and Stable LatentMoE", five-step compute flow):
+ *   1. z    = W_down x                                   latent compression, width l
+ *   2. s    = sigmoid(W_r x), T = TopK(s + b, k),        K3 sigmoid routing; the bias b
+ *      p_i  = s_i / sum_{j in T} s_j                     only affects which experts win
+ *   3. u    = sum_{i in T} p_i E_i(z)                    routed SiTU-GLU experts, width l,
+ *                                                        run as permute-dispatch -> grouped
+ *                                                        GEMMs -> p-weighted scatter-add
+ *   4. s_sh = sum_j E_j^sh(x)                            shared SiTU-GLU experts, width d
+ *   5. y    = s_sh + W_up RMSNorm(u)
+ * with SiTU-GLU E(v) = W_o [beta1 tanh(W_g v / beta1) sigmoid(W_g v) * beta2 tanh(W_u v / beta2)]
+ * (same chapter, SiTU-GLU equation).
+ *
+ * Conventions shared by every entry point
+ *  - Every tensor argument is device memory allocated and owned by the caller,
+ *    row-major and contiguous, 16-byte aligned.  Matrices are stored like
+ *    nn.Linear weights, [out, in].
+ *  - Storage type: dims->dtype selects fp32 (LMOE_F32) or bf16 (LMOE_BF16) for
+ *    x, every weight matrix, the padded tensor and y.  bias, rms_w, probs,
+ *    logits and u are always fp32.  Accumulation is always fp32.  In bf16 mode
+ *    the intermediates that feed a second matrix product -- z, the SiTU hidden
+ *    h and RMSNorm(u) -- are held in fp16 (11-bit significand), and the bf16
+ *    weights they meet are widened to fp16 (exact for |w| >= 2^-14).  fp16's
+ *    range is safe for them: |h| < beta1*beta2 by the SiTU bound, |RMSNorm(u)|
+ *    <= sqrt(l) * max|rms_w|, and z = W_down x stays far below 65504 for
+ *    unit-scale (pre-normed) x.
+ *  - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL = the
+ *    default stream) and is asynchronous unless an entry point says otherwise.
+ *  - `workspace` is caller-owned device scratch of at least
+ *    latentmoe_workspace_bytes(dims, entry) bytes; the library allocates no
+ *    device memory and keeps no state between calls.  Calls that share a
+ *    workspace must be ordered on one stream.
+ *  - Errors: a status code, never an abort.  Arguments are validated before
+ *    anything is enqueued; on any error the outputs are unspecified.
+ *    latentmoe_last_error() returns a thread-local description of the last
+ *    failure on the calling thread.
+ *  - Supported shapes: d, l, f_r and f_s multiples of 64; 1 <= k <= R <= 4096,
+ *    k <= 64; 0 <= n_shared <= 16; n_tokens >= 0 (0 is a no-op).
+ */
+#ifndef LATENTMOE_H
+#define LATENTMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LMOE_OK = 0,
+  LMOE_ERR_INVALID_ARGUMENT = 1, /* null pointer, k < 1, k > R, non-positive width, beta <= 0, eps < 0 */
+  LMOE_ERR_UNSUPPORTED = 2,      /* a shape outside the limits listed above */
+  LMOE_ERR_CAPACITY = 3,         /* padded buffer too small for C (C is still reported) */
+  LMOE_ERR_WORKSPACE = 4,        /* workspace smaller than latentmoe_workspace_bytes() */
+  LMOE_ERR_HIP = 5               /* a HIP runtime call or launch failed */
+} lmoe_status;
+
+typedef enum { LMOE_F32 = 0, LMOE_BF16 = 1 } lmoe_dtype;
+
+/* Which entry point a workspace size is asked for. */
+typedef enum {
+  LMOE_ENTRY_ROUTE = 0,
+  LMOE_ENTRY_DISPATCH = 1,
+  LMOE_ENTRY_EXPERTS = 2,
+  LMOE_ENTRY_FORWARD = 3
+} lmoe_entry;
+
+/* Layer sizes (names after the chapter's component table). */
+typedef struct {
+  int64_t n_tokens;  /* N = B*T; tokens are independent, batch structure is irrelevant */
+  int32_t d_model;   /* d */
+  int32_t d_latent;  /* l (the chapter uses l = d/2; any multiple of 64 is accepted) */
+  int32_t n_routed;  /* R */
+  int32_t top_k;     /* k */
+  int32_t n_shared;  /* n_s (0 allowed) */
+  int32_t ff_routed; /* f_r, inner width of a routed expert */
+  int32_t ff_shared; /* f_s, inner width of a shared expert (f_r == f_s gives the pages' single d_ff) */
+  float beta1;       /* SiTU gate cap, 4 on the pages */
+  float beta2;       /* SiTU up cap, 25 on the pages */
+  float rms_eps;     /* RMSNorm eps (inside the square root) */
+  int32_t dtype;     /* lmoe_dtype */
+} lmoe_dims;
+
+/* Parameters of one layer (all device pointers, storage dtype unless fp32 is stated). */
+typedef struct {
+  const void* w_down;   /* [l, d]          W_down */
+  const void* w_router; /* [R, d]          W_r */
+  const float* bias;    /* [R] fp32        expert bias b (selection only); NULL = zeros */
+  const void* w_g;      /* [R, f_r, l]     routed gate projections */
+  const void* w_u;      /* [R, f_r, l]     routed up projections */
+  const void* w_o;      /* [R, l, f_r]     routed output projections */
+  const void* sh_g;     /* [n_s, f_s, d]   shared gate projections (unused if n_s = 0) */
+  const void* sh_u;     /* [n_s, f_s, d]   shared up projections */
+  const void* sh_o;     /* [n_s, d, f_s]   shared output projections */
+  const float* rms_w;   /* [l] fp32        RMSNorm weight; NULL = ones */
+  const void* w_up;     /* [d, l]          W_up */
+} lmoe_weights;
+
+/* Bytes of workspace an entry point needs for these dims. */
+size_t latentmoe_workspace_bytes(const lmoe_dims* dims, int32_t entry);
+
+const char* latentmoe_status_string(lmoe_status status);
+const char* latentmoe_last_error(void);
+
+/* K3 sigmoid routing (chapter step 2 and its routing code with the three
+ * notes that follow it):
+ *   logits = W_r x (fp32 accumulation), s = sigmoid(logits), T = the k experts
+ *   with the largest s + b (equal values: lower id first), p_i = s_i / max(sum_T s, 1e-9).
+ * x [N, d] and w_router [R, d] in the storage dtype, bias [R] fp32 (NULL = zeros).
+ * Outputs: ids [N, k] int32 in descending s + b order, probs [N, k] fp32 in the
+ * same order, and optionally logits [N, R] fp32 (NULL to skip; the Switch
+ * auxiliary and z losses are computed from them).  Asynchronous. */
+lmoe_status latentmoe_route(const lmoe_dims* dims, const void* x, const void* w_router,
+                            const float* bias, int32_t* ids, float* probs, float* logits,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Permute-dispatch (chapter section on sparse execution: permute-dispatch
+ * + padded bmm).  The N*k (token, slot) pairs, numbered q = n*k + j, are
+ * sorted stably by expert id:
+ *   counts [R]   pairs per expert               offsets [R]  exclusive prefix sum of counts
+ *   order [N*k]  q of the pair at each sorted position (expert-major, ascending q inside an expert)
+ *   *C_out       capacity C = max counts (host int64, required)
+ * If padded is not NULL, padded [R, C, l] (storage dtype, stride C, the first
+ * R*C*l elements of a buffer of capacity*R*l elements) receives row
+ * padded[e, r] = z[order[offsets[e] + r] / k] for r < counts[e] and zeros
+ * for r >= counts[e].  If C > capacity nothing is written to padded and
+ * LMOE_ERR_CAPACITY is returned with *C_out set.
+ * Synchronous: waits on `stream` to read C (the pages' layout needs C on the host). */
+lmoe_status latentmoe_dispatch(const lmoe_dims* dims, const int32_t* ids, const void* z,
+                               int32_t* counts, int32_t* offsets, int32_t* order, void* padded,
+                               int64_t capacity, int64_t* C_out, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* Routed SiTU-GLU experts on the padded layout (chapter step 3 and the three
+ * batched products of the sparse-execution section), with the p-weighted
+ * scatter-add back to token order:
+ *   u[n] = sum_j probs[n, j] * E_{ids[n, j]}(z[n])
+ * padded [R, C, l] as written by latentmoe_dispatch, counts/offsets/order as
+ * returned by it, probs [N, k] fp32 (the router's p), w_g/w_u [R, f_r, l],
+ * w_o [R, l, f_r].  Padding rows are never read.  Output u [N, l] fp32,
+ * overwritten.  Asynchronous. */
+lmoe_status latentmoe_experts(const lmoe_dims* dims, const void* padded, int64_t C,
+                              const int32_t* counts, const int32_t* offsets, const int32_t* order,
+                              const float* probs, const void* w_g, const void* w_u,
+                              const void* w_o, float* u, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/* The whole layer, steps 1-5.  x [N, d] in, y [N, d] out (storage dtype).
+ * Side outputs (the pages' route bookkeeping): ids [N, k] int32 and
+ * probs [N, k] fp32 as from latentmoe_route, counts [R] int32 pairs per
+ * expert.  If C_host is not NULL the call waits on `stream` and writes
+ * C = max counts there; with C_host NULL the call is fully asynchronous.
+ * The routed experts read their rows straight from z through the sorted
+ * pair order (the padded tensor is not materialised), skip empty experts and
+ * padding rows, and the scatter-add is deterministic (each pair writes its own
+ * slot; slots are summed in slot order). */
+lmoe_status latentmoe_forward(const lmoe_dims* dims, const lmoe_weights* weights, const void* x,
+                              void* y, int32_t* ids, float* probs, int32_t* counts,
+                              int64_t* C_host, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/* latentmoe_forward with timing marks, for profiling: `events` holds
+ * LMOE_FORWARD_TIMING_EVENTS hipEvent_t handles (created by the caller);
+ * events[0] is recorded on `stream` before the first step and events[i]
+ * after step i, in this order:
+ *   1 latent compression GEMM         5 routed gate/up grouped GEMM (+ tile list)
+ *   2 router logits GEMM + top-k      6 routed down grouped GEMM -> slots
+ *   3 dispatch (hist, scan, scatter)  7 slot sum + RMSNorm
+ *   4 shared gate/up GEMM             8 merge GEMM [h_shared | RMSNorm(u)] -> y
+ * The elapsed time between events[i-1] and events[i] is step i's device time.
+ * C is not read back.  Otherwise identical to latentmoe_forward. */
+#define LMOE_FORWARD_TIMING_EVENTS 9
+lmoe_status latentmoe_forward_timed(const lmoe_dims* dims, const lmoe_weights* weights,
+                                    const void* x, void* y, int32_t* ids, float* probs,
+                                    int32_t* counts, void* workspace, size_t workspace_bytes,
+                                    void* stream, void* const* events, int32_t n_events);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LATENTMOE_H */

@@ -1,0 +1,597 @@
+// C ABI of the gfx950 Stable LatentMoE forward: argument checks, workspace
+// carving and the launch sequence of each entry point (see latentmoe.h).
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "latentmoe.h"
+#include "gemm_kernel.h"
+#include "merge_kernels.h"
+#include "route_kernels.h"
+
+using namespace lmoe;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+lmoe_status fail(lmoe_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+#define LMOE_HIP(call)                                                                      \
+  do {                                                                                      \
+    hipError_t e_ = (call);                                                                 \
+    if (e_ != hipSuccess)                                                                   \
+      return fail(LMOE_ERR_HIP, "%s failed: %s (%s:%d)", #call, hipGetErrorString(e_), __FILE__, \
+                  __LINE__);                                                                \
+  } while (0)
+
+// ----------------------------------------------------------------- sizes
+struct Plan {
+  int64_t N, pairs;
+  int d, l, R, k, ns, fr, fs;
+  bool bf16;
+  int es;  // bytes per stored element
+  int nchunks;
+  int tile_m;  // rows per grouped-GEMM tile
+  int64_t tile_bound;
+  int64_t ldh;  // elements per row of the [h_shared | u_normed] buffer
+};
+
+// Row-tile height of the grouped expert GEMMs: 32 for a handful of rows per
+// expert (weight streaming), 128 otherwise.
+int routed_tile_m(int64_t pairs, int R) { return pairs < (int64_t)48 * R ? 32 : 128; }
+
+lmoe_status check_dims(const lmoe_dims* dm, Plan* p) {
+  if (!dm) return fail(LMOE_ERR_INVALID_ARGUMENT, "dims is NULL");
+  if (dm->n_tokens < 0) return fail(LMOE_ERR_INVALID_ARGUMENT, "n_tokens < 0");
+  if (dm->d_model <= 0 || dm->d_latent <= 0 || dm->n_routed <= 0 || dm->ff_routed <= 0)
+    return fail(LMOE_ERR_INVALID_ARGUMENT, "non-positive layer width");
+  if (dm->n_shared < 0 || (dm->n_shared > 0 && dm->ff_shared <= 0))
+    return fail(LMOE_ERR_INVALID_ARGUMENT, "bad shared expert sizes");
+  if (dm->top_k < 1 || dm->top_k > dm->n_routed)
+    return fail(LMOE_ERR_INVALID_ARGUMENT, "top_k must satisfy 1 <= k <= R (k=%d, R=%d)", dm->top_k,
+                dm->n_routed);
+  if (!(dm->beta1 > 0.f) || !(dm->beta2 > 0.f)) return fail(LMOE_ERR_INVALID_ARGUMENT, "beta <= 0");
+  if (!(dm->rms_eps >= 0.f)) return fail(LMOE_ERR_INVALID_ARGUMENT, "rms_eps < 0");
+  if (dm->dtype != LMOE_F32 && dm->dtype != LMOE_BF16)
+    return fail(LMOE_ERR_INVALID_ARGUMENT, "unknown dtype %d", dm->dtype);
+  if (dm->d_model % 64 || dm->d_latent % 64 || dm->ff_routed % 64 ||
+      (dm->n_shared > 0 && dm->ff_shared % 64))
+    return fail(LMOE_ERR_UNSUPPORTED, "d, l, f_r, f_s must be multiples of 64");
+  if (dm->n_routed > kMaxRouted) return fail(LMOE_ERR_UNSUPPORTED, "n_routed > %d", kMaxRouted);
+  if (dm->top_k > kMaxTopK) return fail(LMOE_ERR_UNSUPPORTED, "top_k > %d", kMaxTopK);
+  if (dm->n_shared > kMaxSeg - 1) return fail(LMOE_ERR_UNSUPPORTED, "n_shared > %d", kMaxSeg - 1);
+  if (dm->d_latent > kMaxLatent) return fail(LMOE_ERR_UNSUPPORTED, "d_latent > %d", kMaxLatent);
+  const int64_t pairs = dm->n_tokens * dm->top_k;
+  if (pairs > (int64_t)INT32_MAX / 2 || dm->n_tokens > (int64_t)INT32_MAX / 2)
+    return fail(LMOE_ERR_UNSUPPORTED, "too many tokens");
+  p->N = dm->n_tokens;
+  p->pairs = pairs;
+  p->d = dm->d_model;
+  p->l = dm->d_latent;
+  p->R = dm->n_routed;
+  p->k = dm->top_k;
+  p->ns = dm->n_shared;
+  p->fr = dm->ff_routed;
+  p->fs = dm->n_shared > 0 ? dm->ff_shared : 0;
+  p->bf16 = dm->dtype == LMOE_BF16;
+  p->es = p->bf16 ? 2 : 4;
+  p->nchunks = (int)((pairs + kDispatchChunk - 1) / kDispatchChunk);
+  p->tile_m = routed_tile_m(pairs, p->R);
+  p->tile_bound = (pairs + (int64_t)p->R * (p->tile_m - 1)) / p->tile_m;
+  p->ldh = (int64_t)p->ns * p->fs + p->l;
+  return LMOE_OK;
+}
+
+// Bump allocator over the caller's workspace (256-byte aligned regions).
+struct Carver {
+  char* base;
+  size_t off = 0;
+  template <typename X>
+  X* take(size_t bytes) {
+    off = (off + 255) & ~(size_t)255;
+    X* r = base ? (X*)(base + off) : nullptr;
+    off += bytes;
+    return r;
+  }
+};
+
+struct RouteWs {
+  float* logits;
+};
+struct DispatchWs {
+  int32_t* chunk_hist;
+  int32_t* chunk_bad;
+  int32_t* meta;
+};
+struct ExpertsWs {
+  int32_t* tile_list;
+  int32_t* meta;
+  char* h;
+  float* slots;
+};
+struct ForwardWs {
+  char* z;
+  float* logits;
+  int32_t* chunk_hist;
+  int32_t* chunk_bad;
+  int32_t* meta;
+  int32_t* offsets;
+  int32_t* order;
+  int32_t* tile_list;
+  char* h;
+  float* slots;
+  char* hcat;
+};
+
+size_t carve_route(const Plan& p, char* b, RouteWs* w) {
+  Carver c{b};
+  w->logits = c.take<float>((size_t)p.N * p.R * 4);
+  return c.off;
+}
+size_t carve_dispatch(const Plan& p, char* b, DispatchWs* w) {
+  Carver c{b};
+  w->chunk_hist = c.take<int32_t>((size_t)p.nchunks * p.R * 4);
+  w->chunk_bad = c.take<int32_t>((size_t)p.nchunks * 4);
+  w->meta = c.take<int32_t>(64);
+  return c.off;
+}
+size_t carve_experts(const Plan& p, char* b, ExpertsWs* w) {
+  Carver c{b};
+  w->tile_list = c.take<int32_t>((size_t)p.tile_bound * 8);
+  w->meta = c.take<int32_t>(64);
+  w->h = c.take<char>((size_t)p.pairs * p.fr * p.es);
+  w->slots = c.take<float>((size_t)p.pairs * p.l * 4);
+  return c.off;
+}
+size_t carve_forward(const Plan& p, char* b, ForwardWs* w) {
+  Carver c{b};
+  w->z = c.take<char>((size_t)p.N * p.l * p.es);
+  w->logits = c.take<float>((size_t)p.N * p.R * 4);
+  w->chunk_hist = c.take<int32_t>((size_t)p.nchunks * p.R * 4);
+  w->chunk_bad = c.take<int32_t>((size_t)p.nchunks * 4);
+  w->meta = c.take<int32_t>(64);
+  w->offsets = c.take<int32_t>((size_t)p.R * 4);
+  w->order = c.take<int32_t>((size_t)p.pairs * 4);
+  w->tile_list = c.take<int32_t>((size_t)p.tile_bound * 8);
+  w->h = c.take<char>((size_t)p.pairs * p.fr * p.es);
+  w->slots = c.take<float>((size_t)p.pairs * p.l * 4);
+  w->hcat = c.take<char>((size_t)p.N * p.ldh * p.es);
+  return c.off;
+}
+
+// ------------------------------------------------------------ GEMM launches
+template <typename TA, typename TB, typename OutT, int BM, int BN, int WGM, int WGN, int AM, int BMD,
+          int EM>
+lmoe_status launch_gemm(GemmArgs a, hipStream_t st) {
+  const int64_t grid = (int64_t)a.m_tiles * a.n_tiles;
+  if (grid <= 0) return LMOE_OK;
+  if (grid > INT32_MAX) return fail(LMOE_ERR_UNSUPPORTED, "GEMM grid too large");
+  gemm_kernel<TA, TB, OutT, BM, BN, WGM, WGN, AM, BMD, EM><<<(unsigned)grid, 256, 0, st>>>(a);
+  LMOE_HIP(hipGetLastError());
+  return LMOE_OK;
+}
+
+// Tile shapes: "small" = 32-row tiles for few-token products, "large" = 128x128.
+template <typename TA, typename TB, typename OutT, int AM, int BMD, int EM>
+lmoe_status gemm(GemmArgs a, bool small, hipStream_t st) {
+  constexpr bool dual = BMD == B_DUAL;
+  if (small) {
+    constexpr int BM = 32, BN = dual ? 256 : 128;
+    a.n_tiles = (a.N + (dual ? BN / 2 : BN) - 1) / (dual ? BN / 2 : BN);
+    if (AM == A_DENSE) a.m_tiles = (a.M + BM - 1) / BM;
+    return launch_gemm<TA, TB, OutT, BM, BN, 1, 4, AM, BMD, EM>(a, st);
+  } else {
+    constexpr int BM = 128, BN = 128;
+    a.n_tiles = (a.N + (dual ? BN / 2 : BN) - 1) / (dual ? BN / 2 : BN);
+    if (AM == A_DENSE) a.m_tiles = (a.M + BM - 1) / BM;
+    return launch_gemm<TA, TB, OutT, BM, BN, 2, 2, AM, BMD, EM>(a, st);
+  }
+}
+
+GemmArgs base_args(const lmoe_dims* dm) {
+  GemmArgs a;
+  memset(&a, 0, sizeof(a));
+  a.beta1 = dm->beta1;
+  a.beta2 = dm->beta2;
+  a.nseg = 1;
+  return a;
+}
+
+#define LMOE_TRY(x)                       \
+  do {                                    \
+    lmoe_status s_ = (x);                 \
+    if (s_ != LMOE_OK) return s_;         \
+  } while (0)
+
+// ---------------------------------------------------------- step launchers
+// logits = x W_r^T (fp32), then the sigmoid / top-k / renormalisation kernel.
+template <typename T>
+lmoe_status run_route(const Plan& p, const lmoe_dims* dm, const void* x, const void* w_router,
+                      const float* bias, int32_t* ids, float* probs, float* logits, hipStream_t st) {
+  GemmArgs a = base_args(dm);
+  a.M = (int)p.N;
+  a.N = p.R;
+  a.K = p.d;
+  a.a = (const char*)x;
+  a.lda = (int64_t)p.d * p.es;
+  a.b0 = (const char*)w_router;
+  a.ldb = (int64_t)p.d * p.es;
+  a.nb_rows = p.R;
+  a.out = (char*)logits;
+  a.ldo = (int64_t)p.R * 4;
+  LMOE_TRY((gemm<T, T, float, A_DENSE, B_SINGLE, E_STORE>(a, p.N <= 64, st)));
+  const unsigned blocks = (unsigned)((p.N + 3) / 4);
+  topk_route_kernel<<<blocks, 256, 4 * p.R * sizeof(float), st>>>(logits, bias, p.N, p.R, p.k, ids,
+                                                                  probs);
+  LMOE_HIP(hipGetLastError());
+  return LMOE_OK;
+}
+
+// counts / offsets / stable order (+ C in meta[0]).
+lmoe_status run_dispatch(const Plan& p, const int32_t* ids, int32_t* chunk_hist, int32_t* chunk_bad,
+                         int32_t* counts, int32_t* offsets, int32_t* order, int32_t* meta,
+                         hipStream_t st) {
+  dispatch_hist_kernel<<<p.nchunks, 256, (p.R + 1) * sizeof(int32_t), st>>>(ids, p.pairs, p.R,
+                                                                            chunk_hist, chunk_bad);
+  LMOE_HIP(hipGetLastError());
+  dispatch_scan_kernel<<<1, 1024, 0, st>>>(chunk_hist, p.nchunks, p.R, counts, offsets, chunk_bad, meta);
+  LMOE_HIP(hipGetLastError());
+  dispatch_scatter_kernel<<<p.nchunks, 64, (p.R + 64) * sizeof(int32_t), st>>>(ids, p.pairs, p.R,
+                                                                              chunk_hist, order);
+  LMOE_HIP(hipGetLastError());
+  return LMOE_OK;
+}
+
+// Routed experts: tile list, gate/up grouped GEMM with the SiTU epilogue into
+// h (sorted pair rows, type TH), down grouped GEMM with the p-weighted slot
+// epilogue.  TA: type of the gathered rows, TW: weight storage type.
+template <typename TA, typename TW, typename TH, int AM, typename Mark = lmoe_status (*)()>
+lmoe_status run_experts(const Plan& p, const lmoe_dims* dm, const void* a_src, int64_t cap,
+                        const int32_t* counts, const int32_t* offsets, const int32_t* order,
+                        const float* probs, const void* w_g, const void* w_u, const void* w_o,
+                        int32_t* tile_list, int32_t* meta, char* h, float* slots, hipStream_t st,
+                        Mark* mark = nullptr) {
+  tile_list_kernel<<<1, 1024, 0, st>>>(counts, p.R, p.tile_m, tile_list, meta);
+  LMOE_HIP(hipGetLastError());
+  const bool small = p.tile_m == 32;
+  GemmArgs a = base_args(dm);
+  a.N = p.fr;
+  a.K = p.l;
+  a.m_tiles = (int)p.tile_bound;
+  a.a = (const char*)a_src;
+  a.lda = (int64_t)p.l * sizeof(TA);
+  a.order = order;
+  a.top_k = p.k;
+  a.cap = cap;
+  a.tile_list = tile_list;
+  a.tile_count = meta + 1;
+  a.counts = counts;
+  a.offsets = offsets;
+  a.b0 = (const char*)w_g;
+  a.b1 = (const char*)w_u;
+  a.ldb = (int64_t)p.l * p.es;
+  a.b_expert_stride = (int64_t)p.fr * p.l * p.es;
+  a.nb_rows = p.fr;
+  a.out = h;
+  a.ldo = (int64_t)p.fr * p.es;
+  LMOE_TRY((gemm<TA, TW, TH, AM, B_DUAL, E_SITU>(a, small, st)));
+  if (mark) LMOE_TRY((*mark)());
+
+  GemmArgs b = base_args(dm);
+  b.N = p.l;
+  b.K = p.fr;
+  b.m_tiles = (int)p.tile_bound;
+  b.a = h;
+  b.lda = (int64_t)p.fr * p.es;
+  b.order = order;
+  b.top_k = p.k;
+  b.tile_list = tile_list;
+  b.tile_count = meta + 1;
+  b.counts = counts;
+  b.offsets = offsets;
+  b.b0 = (const char*)w_o;
+  b.ldb = (int64_t)p.fr * p.es;
+  b.b_expert_stride = (int64_t)p.l * p.fr * p.es;
+  b.nb_rows = p.l;
+  b.out = (char*)slots;
+  b.ldo = (int64_t)p.l * 4;
+  b.probs = probs;
+  return gemm<TH, TW, float, A_SORTED, B_SINGLE, E_SLOTS>(b, small, st);
+}
+
+// T: storage type (x, weights, y); TI: intermediate type of z, h and the
+// normalised u (fp32 with fp32 storage, fp16 with bf16 storage).
+template <typename T, typename TI>
+lmoe_status run_forward(const Plan& p, const lmoe_dims* dm, const lmoe_weights* W, const void* x,
+                        void* y, int32_t* ids, float* probs, int32_t* counts, const ForwardWs& w,
+                        hipStream_t st, hipEvent_t* ev) {
+  const bool small = p.N <= 64;
+  int step = 0;
+  auto mark = [&]() -> lmoe_status {  // optional per-step timing events
+    if (ev) LMOE_HIP(hipEventRecord(ev[step], st));
+    ++step;
+    return LMOE_OK;
+  };
+  LMOE_TRY(mark());
+  // 1. z = W_down x
+  GemmArgs a = base_args(dm);
+  a.M = (int)p.N;
+  a.N = p.l;
+  a.K = p.d;
+  a.a = (const char*)x;
+  a.lda = (int64_t)p.d * p.es;
+  a.b0 = (const char*)W->w_down;
+  a.ldb = (int64_t)p.d * p.es;
+  a.nb_rows = p.l;
+  a.out = w.z;
+  a.ldo = (int64_t)p.l * p.es;
+  LMOE_TRY((gemm<T, T, TI, A_DENSE, B_SINGLE, E_STORE>(a, small, st)));
+  LMOE_TRY(mark());
+  // 2. routing
+  LMOE_TRY(run_route<T>(p, dm, x, W->w_router, W->bias, ids, probs, w.logits, st));
+  LMOE_TRY(mark());
+  // 3a. dispatch bookkeeping
+  LMOE_TRY(run_dispatch(p, ids, w.chunk_hist, w.chunk_bad, counts, w.offsets, w.order, w.meta, st));
+  LMOE_TRY(mark());
+  // 4. shared experts gate/up -> h_shared = hcat[:, :n_s f_s]
+  if (p.ns > 0) {
+    GemmArgs s = base_args(dm);
+    s.M = (int)p.N;
+    s.N = p.ns * p.fs;
+    s.K = p.d;
+    s.a = (const char*)x;
+    s.lda = (int64_t)p.d * p.es;
+    s.b0 = (const char*)W->sh_g;
+    s.b1 = (const char*)W->sh_u;
+    s.ldb = (int64_t)p.d * p.es;
+    s.nb_rows = p.ns * p.fs;
+    s.out = w.hcat;
+    s.ldo = p.ldh * p.es;
+    LMOE_TRY((gemm<T, T, TI, A_DENSE, B_DUAL, E_SITU>(s, small, st)));
+  }
+  LMOE_TRY(mark());
+  // 3b. routed experts straight from z -> slots
+  LMOE_TRY((run_experts<TI, T, TI, A_GATHER>(p, dm, w.z, 0, counts, w.offsets, w.order, probs, W->w_g,
+                                     W->w_u, W->w_o, w.tile_list, w.meta, w.h, w.slots, st,
+                                     ev ? &mark : nullptr)));
+  LMOE_TRY(mark());
+  // 5a. u = sum of slots, RMSNorm -> hcat[:, n_s f_s:]
+  combine_rmsnorm_kernel<TI><<<(unsigned)p.N, 256, 0, st>>>(
+      w.slots, p.k, p.l, nullptr, W->rms_w, dm->rms_eps,
+      (TI*)(w.hcat + (int64_t)p.ns * p.fs * p.es), p.ldh);
+  LMOE_HIP(hipGetLastError());
+  LMOE_TRY(mark());
+  // 5b. y = [h_shared | RMSNorm(u)] [sh_o_0 | ... | sh_o_{n_s-1} | W_up]^T
+  GemmArgs f = base_args(dm);
+  f.M = (int)p.N;
+  f.N = p.d;
+  f.K = (int)p.ldh;
+  f.a = w.hcat;
+  f.lda = p.ldh * p.es;
+  f.nb_rows = p.d;
+  const int kt_per_fs = p.fs * p.es / 128;
+  f.nseg = p.ns + 1;
+  for (int j = 0; j < p.ns; ++j) {
+    f.seg_base[j] = (const char*)W->sh_o + (int64_t)j * p.d * p.fs * p.es;
+    f.seg_ld[j] = (int64_t)p.fs * p.es;
+    f.seg_kt0[j] = j * kt_per_fs;
+  }
+  f.seg_base[p.ns] = (const char*)W->w_up;
+  f.seg_ld[p.ns] = (int64_t)p.l * p.es;
+  f.seg_kt0[p.ns] = p.ns * kt_per_fs;
+  f.seg_kt0[p.ns + 1] = (int)(p.ldh * p.es / 128);
+  f.out = (char*)y;
+  f.ldo = (int64_t)p.d * p.es;
+  LMOE_TRY((gemm<TI, T, T, A_DENSE, B_KSEG, E_STORE>(f, small, st)));
+  return mark();
+}
+
+}  // namespace
+
+// =================================================================== C ABI
+extern "C" {
+
+const char* latentmoe_status_string(lmoe_status s) {
+  switch (s) {
+    case LMOE_OK: return "ok";
+    case LMOE_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case LMOE_ERR_UNSUPPORTED: return "unsupported shape";
+    case LMOE_ERR_CAPACITY: return "padded capacity smaller than C";
+    case LMOE_ERR_WORKSPACE: return "workspace too small";
+    case LMOE_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* latentmoe_last_error(void) { return g_err; }
+
+size_t latentmoe_workspace_bytes(const lmoe_dims* dims, int32_t entry) {
+  Plan p;
+  if (check_dims(dims, &p) != LMOE_OK) return 0;
+  switch (entry) {
+    case LMOE_ENTRY_ROUTE: {
+      RouteWs w;
+      return carve_route(p, nullptr, &w);
+    }
+    case LMOE_ENTRY_DISPATCH: {
+      DispatchWs w;
+      return carve_dispatch(p, nullptr, &w);
+    }
+    case LMOE_ENTRY_EXPERTS: {
+      ExpertsWs w;
+      return carve_experts(p, nullptr, &w);
+    }
+    case LMOE_ENTRY_FORWARD: {
+      ForwardWs w;
+      return carve_forward(p, nullptr, &w);
+    }
+  }
+  return 0;
+}
+
+lmoe_status latentmoe_route(const lmoe_dims* dims, const void* x, const void* w_router,
+                            const float* bias, int32_t* ids, float* probs, float* logits,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  Plan p;
+  LMOE_TRY(check_dims(dims, &p));
+  if (p.N == 0) return LMOE_OK;
+  if (!x || !w_router || !ids || !probs) return fail(LMOE_ERR_INVALID_ARGUMENT, "NULL tensor");
+  RouteWs w{};
+  if (!logits) {
+    const size_t need = carve_route(p, nullptr, &w);
+    if (!workspace || workspace_bytes < need)
+      return fail(LMOE_ERR_WORKSPACE, "route needs %zu workspace bytes", need);
+    carve_route(p, (char*)workspace, &w);
+    logits = w.logits;
+  }
+  hipStream_t st = (hipStream_t)stream;
+  if (p.bf16) return run_route<bf16_t>(p, dims, x, w_router, bias, ids, probs, logits, st);
+  return run_route<float>(p, dims, x, w_router, bias, ids, probs, logits, st);
+}
+
+lmoe_status latentmoe_dispatch(const lmoe_dims* dims, const int32_t* ids, const void* z,
+                               int32_t* counts, int32_t* offsets, int32_t* order, void* padded,
+                               int64_t capacity, int64_t* C_out, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  Plan p;
+  LMOE_TRY(check_dims(dims, &p));
+  if (!C_out || !counts || !offsets || (p.N > 0 && (!ids || !order)))
+    return fail(LMOE_ERR_INVALID_ARGUMENT, "NULL argument");
+  if (padded && !z) return fail(LMOE_ERR_INVALID_ARGUMENT, "padded output needs z");
+  if (capacity < 0) return fail(LMOE_ERR_INVALID_ARGUMENT, "capacity < 0");
+  hipStream_t st = (hipStream_t)stream;
+  *C_out = 0;
+  if (p.N == 0) {
+    LMOE_HIP(hipMemsetAsync(counts, 0, (size_t)p.R * 4, st));
+    LMOE_HIP(hipMemsetAsync(offsets, 0, (size_t)p.R * 4, st));
+    LMOE_HIP(hipStreamSynchronize(st));
+    return LMOE_OK;
+  }
+  DispatchWs w{};
+  const size_t need = carve_dispatch(p, nullptr, &w);
+  if (!workspace || workspace_bytes < need)
+    return fail(LMOE_ERR_WORKSPACE, "dispatch needs %zu workspace bytes", need);
+  carve_dispatch(p, (char*)workspace, &w);
+  LMOE_TRY(run_dispatch(p, ids, w.chunk_hist, w.chunk_bad, counts, offsets, order, w.meta, st));
+  int32_t meta[4] = {0, 0, 0, 0};
+  LMOE_HIP(hipMemcpyAsync(meta, w.meta, sizeof(meta), hipMemcpyDeviceToHost, st));
+  LMOE_HIP(hipStreamSynchronize(st));
+  const int32_t C = meta[0];
+  *C_out = C;
+  if (meta[2] != 0)
+    return fail(LMOE_ERR_INVALID_ARGUMENT, "%d expert ids outside [0, R)", meta[2]);
+  if (!padded) return LMOE_OK;
+  if (C > capacity) return fail(LMOE_ERR_CAPACITY, "C = %d exceeds capacity %lld", C, (long long)capacity);
+  if (C == 0) return LMOE_OK;
+  const unsigned rows = (unsigned)((int64_t)p.R * C);
+  if (p.bf16)
+    padded_gather_kernel<bf16_t><<<rows, 256, 0, st>>>((const bf16_t*)z, p.l, counts, offsets, order,
+                                                       p.k, C, (bf16_t*)padded);
+  else
+    padded_gather_kernel<float><<<rows, 256, 0, st>>>((const float*)z, p.l, counts, offsets, order, p.k,
+                                                      C, (float*)padded);
+  LMOE_HIP(hipGetLastError());
+  return LMOE_OK;
+}
+
+lmoe_status latentmoe_experts(const lmoe_dims* dims, const void* padded, int64_t C,
+                              const int32_t* counts, const int32_t* offsets, const int32_t* order,
+                              const float* probs, const void* w_g, const void* w_u,
+                              const void* w_o, float* u, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  Plan p;
+  LMOE_TRY(check_dims(dims, &p));
+  if (p.N == 0) return LMOE_OK;
+  if (!padded || !counts || !offsets || !order || !probs || !w_g || !w_u || !w_o || !u)
+    return fail(LMOE_ERR_INVALID_ARGUMENT, "NULL tensor");
+  if (C < 1 || C > p.N) return fail(LMOE_ERR_INVALID_ARGUMENT, "C must be in [1, N]");
+  ExpertsWs w{};
+  const size_t need = carve_experts(p, nullptr, &w);
+  if (!workspace || workspace_bytes < need)
+    return fail(LMOE_ERR_WORKSPACE, "experts needs %zu workspace bytes", need);
+  carve_experts(p, (char*)workspace, &w);
+  hipStream_t st = (hipStream_t)stream;
+  if (p.bf16)
+    LMOE_TRY((run_experts<bf16_t, bf16_t, f16_t, A_PADDED>(p, dims, padded, C, counts, offsets, order, probs, w_g,
+                                            w_u, w_o, w.tile_list, w.meta, w.h, w.slots, st)));
+  else
+    LMOE_TRY((run_experts<float, float, float, A_PADDED>(p, dims, padded, C, counts, offsets, order, probs, w_g, w_u,
+                                           w_o, w.tile_list, w.meta, w.h, w.slots, st)));
+  if (p.bf16)
+    combine_rmsnorm_kernel<f16_t><<<(unsigned)p.N, 256, 0, st>>>(w.slots, p.k, p.l, u, nullptr, 0.f,
+                                                                 nullptr, 0);
+  else
+    combine_rmsnorm_kernel<float><<<(unsigned)p.N, 256, 0, st>>>(w.slots, p.k, p.l, u, nullptr, 0.f,
+                                                                 nullptr, 0);
+  LMOE_HIP(hipGetLastError());
+  return LMOE_OK;
+}
+
+}  // extern "C"
+
+namespace {
+lmoe_status forward_impl(const lmoe_dims* dims, const lmoe_weights* weights, const void* x, void* y,
+                         int32_t* ids, float* probs, int32_t* counts, int64_t* C_host,
+                         void* workspace, size_t workspace_bytes, void* stream, hipEvent_t* ev) {
+  Plan p;
+  LMOE_TRY(check_dims(dims, &p));
+  if (C_host) *C_host = 0;
+  if (p.N == 0) return LMOE_OK;
+  if (!weights || !x || !y || !ids || !probs || !counts)
+    return fail(LMOE_ERR_INVALID_ARGUMENT, "NULL tensor");
+  const lmoe_weights* W = weights;
+  if (!W->w_down || !W->w_router || !W->w_g || !W->w_u || !W->w_o || !W->w_up)
+    return fail(LMOE_ERR_INVALID_ARGUMENT, "NULL weight");
+  if (p.ns > 0 && (!W->sh_g || !W->sh_u || !W->sh_o))
+    return fail(LMOE_ERR_INVALID_ARGUMENT, "NULL shared expert weight");
+  ForwardWs w{};
+  const size_t need = carve_forward(p, nullptr, &w);
+  if (!workspace || workspace_bytes < need)
+    return fail(LMOE_ERR_WORKSPACE, "forward needs %zu workspace bytes", need);
+  carve_forward(p, (char*)workspace, &w);
+  hipStream_t st = (hipStream_t)stream;
+  if (p.bf16) LMOE_TRY((run_forward<bf16_t, f16_t>(p, dims, W, x, y, ids, probs, counts, w, st, ev)));
+  else LMOE_TRY((run_forward<float, float>(p, dims, W, x, y, ids, probs, counts, w, st, ev)));
+  if (C_host) {
+    int32_t C = 0;
+    LMOE_HIP(hipMemcpyAsync(&C, w.meta, sizeof(int32_t), hipMemcpyDeviceToHost, st));
+    LMOE_HIP(hipStreamSynchronize(st));
+    *C_host = C;
+  }
+  return LMOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+lmoe_status latentmoe_forward(const lmoe_dims* dims, const lmoe_weights* weights, const void* x,
+                              void* y, int32_t* ids, float* probs, int32_t* counts,
+                              int64_t* C_host, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  return forward_impl(dims, weights, x, y, ids, probs, counts, C_host, workspace, workspace_bytes,
+                      stream, nullptr);
+}
+
+lmoe_status latentmoe_forward_timed(const lmoe_dims* dims, const lmoe_weights* weights,
+                                    const void* x, void* y, int32_t* ids, float* probs,
+                                    int32_t* counts, void* workspace, size_t workspace_bytes,
+                                    void* stream, void* const* events, int32_t n_events) {
+  if (!events || n_events != LMOE_FORWARD_TIMING_EVENTS)
+    return fail(LMOE_ERR_INVALID_ARGUMENT, "need %d events", LMOE_FORWARD_TIMING_EVENTS);
+  for (int i = 0; i < n_events; ++i)
+    if (!events[i]) return fail(LMOE_ERR_INVALID_ARGUMENT, "NULL event");
+  return forward_impl(dims, weights, x, y, ids, probs, counts, nullptr, workspace, workspace_bytes,
+                      stream, (hipEvent_t*)events);
+}
+
+}  // extern "C"

@@ -1,0 +1,57 @@
+// Sum of the p-weighted routed slots of each token (the deterministic form of
+// the scatter-add) fused with the latent RMSNorm that feeds W_up.
+#pragma once
+
+#include "lmoe_common.h"
+
+namespace lmoe {
+
+constexpr int kMaxLatent = 8192;  // 8 float4 per thread of a 256-thread workgroup
+
+// One workgroup per token n:
+//   u[c] = sum_{j < k} slots[(n k + j) l + c]      (slot order, fp32)
+//   u_out[n, c] = u[c]                               (if u_out)
+//   dst[n, c]   = T(w[c] u[c] / sqrt(mean(u^2) + eps)) (if dst; w = 1 when rms_w is NULL)
+template <typename T>
+__global__ __launch_bounds__(256) void combine_rmsnorm_kernel(const float* __restrict__ slots, int k,
+                                                              int ell, float* __restrict__ u_out,
+                                                              const float* __restrict__ rms_w,
+                                                              float eps, T* __restrict__ dst,
+                                                              int64_t ld_dst) {
+  constexpr int kVec = kMaxLatent / 1024;
+  __shared__ float red[4];
+  const int64_t n = blockIdx.x;
+  const int t = threadIdx.x;
+  f32x4 u[kVec];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < kVec; ++i) {
+    const int c = 4 * t + 1024 * i;
+    u[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (c < ell) {
+      for (int j = 0; j < k; ++j) u[i] += *(const f32x4*)(slots + ((n * k + j) * ell + c));
+      ss += u[i][0] * u[i][0] + u[i][1] * u[i][1] + u[i][2] * u[i][2] + u[i][3] * u[i][3];
+      if (u_out) *(f32x4*)(u_out + n * ell + c) = u[i];
+    }
+  }
+  if (!dst) return;  // uniform
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+  if ((t & 63) == 0) red[t >> 6] = ss;
+  __syncthreads();
+  const float total = (red[0] + red[1]) + (red[2] + red[3]);
+  const float r = 1.0f / sqrtf(total / (float)ell + eps);
+#pragma unroll
+  for (int i = 0; i < kVec; ++i) {
+    const int c = 4 * t + 1024 * i;
+    if (c < ell) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float w = rms_w ? rms_w[c + q] : 1.f;
+        Elem<T>::store(dst + n * ld_dst + c + q, u[i][q] * r * w);
+      }
+    }
+  }
+}
+
+}  // namespace lmoe

@@ -1,0 +1,241 @@
+// K3 sigmoid routing after the logits GEMM, and the permute-dispatch
+// bookkeeping (histogram -> scan -> stable scatter) on the device.
+#pragma once
+
+#include "lmoe_common.h"
+
+namespace lmoe {
+
+constexpr int kMaxRouted = 4096;
+constexpr int kMaxTopK = 64;
+constexpr int kDispatchChunk = 1024;  // pairs per histogram / scatter chunk
+
+// ---------------------------------------------------------------------------
+// One wave64 per token: s = sigmoid(l) over the R experts, k rounds of a
+// wave-wide arg-max of v = s + b (larger v first, equal v -> lower id), then
+// p_i = s_i / max(sum_T s, 1e-9).  v lives in LDS (R floats per wave), each
+// lane keeps the best of its own experts so that a round rescans one lane.
+__global__ __launch_bounds__(256) void topk_route_kernel(const float* __restrict__ logits,
+                                                         const float* __restrict__ bias, int64_t N,
+                                                         int R, int k, int32_t* __restrict__ ids,
+                                                         float* __restrict__ probs) {
+  extern __shared__ float vbuf[];  // [4][R]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t n = (int64_t)blockIdx.x * 4 + wave;
+  if (n >= N) return;  // no block-level barrier below: waves are independent
+  float* v = vbuf + wave * R;
+  const float* lrow = logits + n * R;
+
+  float best = -INFINITY;
+  int best_id = 0x7fffffff;
+  for (int e = lane; e < R; e += 64) {
+    const float s = sigmoidf_(lrow[e]);
+    const float ve = s + (bias ? bias[e] : 0.f);
+    v[e] = ve;
+    if (ve > best) {  // ascending e per lane: strict > keeps the lower id on ties
+      best = ve;
+      best_id = e;
+    }
+  }
+
+  int my_id = 0;  // lane j keeps the j-th winner
+  float ssum = 0.f;
+  for (int j = 0; j < k; ++j) {
+    float bv = best;
+    int bi = best_id;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oi = __shfl_xor(bi, off);
+      if (ov > bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if (bi >= R) bi = 0;  // only reachable with NaN scores; keeps every index in range
+    if (lane == j) my_id = bi;
+    ssum += sigmoidf_(lrow[bi]);
+    if ((bi & 63) == lane) {  // owner lane removes the winner and rescans its experts
+      v[bi] = -INFINITY;
+      best = -INFINITY;
+      best_id = 0x7fffffff;
+      for (int e = lane; e < R; e += 64) {
+        const float ve = v[e];
+        if (ve > best) {
+          best = ve;
+          best_id = e;
+        }
+      }
+    }
+  }
+  if (lane < k) {
+    ids[n * k + lane] = my_id;
+    probs[n * k + lane] = sigmoidf_(lrow[my_id]) / fmaxf(ssum, 1e-9f);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Dispatch step 1: per-chunk expert histogram of the flattened pair ids.
+// Expert ids outside [0, R) are not counted; chunk_bad[chunk] records how many.
+__global__ __launch_bounds__(256) void dispatch_hist_kernel(const int32_t* __restrict__ ids,
+                                                            int64_t pairs, int R,
+                                                            int32_t* __restrict__ chunk_hist,
+                                                            int32_t* __restrict__ chunk_bad) {
+  extern __shared__ int32_t hist[];  // [R] + 1 bad counter
+  for (int e = threadIdx.x; e <= R; e += 256) hist[e] = 0;
+  __syncthreads();
+  const int64_t q0 = (int64_t)blockIdx.x * kDispatchChunk;
+  const int64_t q1 = min(q0 + kDispatchChunk, pairs);
+  for (int64_t q = q0 + threadIdx.x; q < q1; q += 256) {
+    const int e = ids[q];
+    atomicAdd(&hist[(e >= 0 && e < R) ? e : R], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < R; e += 256) chunk_hist[(int64_t)blockIdx.x * R + e] = hist[e];
+  if (threadIdx.x == 0) chunk_bad[blockIdx.x] = hist[R];
+}
+
+// Dispatch step 2 (one workgroup of 1024 threads): per expert, a running sum
+// over chunks turns chunk_hist into each chunk's first sorted position;
+// counts, offsets (exclusive scan over experts), meta[0] = C = max counts and
+// meta[2] = number of ids outside [0, R).
+__global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t* __restrict__ chunk_hist,
+                                                             int nchunks, int R,
+                                                             int32_t* __restrict__ counts,
+                                                             int32_t* __restrict__ offsets,
+                                                             const int32_t* __restrict__ chunk_bad,
+                                                             int32_t* __restrict__ meta) {
+  __shared__ int32_t part[1024];
+  __shared__ int32_t cmax[1024];
+  const int t = threadIdx.x;
+  if (t == 0) {
+    int bad = 0;
+    for (int c = 0; c < nchunks; ++c) bad += chunk_bad[c];
+    meta[2] = bad;
+  }
+  const int ept = (R + 1023) / 1024;  // experts per thread, contiguous
+  const int e0 = min(t * ept, R), e1 = min(e0 + ept, R);
+  int my_total = 0, my_max = 0;
+  for (int e = e0; e < e1; ++e) {
+    int run = 0;
+    for (int c = 0; c < nchunks; ++c) {
+      const int h = chunk_hist[(int64_t)c * R + e];
+      chunk_hist[(int64_t)c * R + e] = run;
+      run += h;
+    }
+    counts[e] = run;
+    my_total += run;
+    my_max = max(my_max, run);
+  }
+  part[t] = my_total;
+  cmax[t] = my_max;
+  __syncthreads();
+  for (int s = 1; s < 1024; s <<= 1) {  // inclusive scan (sum) and suffix max
+    const int a = t >= s ? part[t - s] : 0;
+    const int m = t + s < 1024 ? cmax[t + s] : 0;
+    __syncthreads();
+    part[t] += a;
+    cmax[t] = max(cmax[t], m);
+    __syncthreads();
+  }
+  int base = part[t] - my_total;
+  for (int e = e0; e < e1; ++e) {
+    offsets[e] = base;
+    for (int c = 0; c < nchunks; ++c) chunk_hist[(int64_t)c * R + e] += base;
+    base += counts[e];
+  }
+  if (t == 0) meta[0] = cmax[0];
+}
+
+// Grouped-GEMM work list (one workgroup of 1024 threads): every expert with
+// pairs contributes ceil(counts[e] / tile_m) row tiles (expert, first row), in
+// expert order.  meta[1] = number of tiles.
+__global__ __launch_bounds__(1024) void tile_list_kernel(const int32_t* __restrict__ counts, int R,
+                                                         int tile_m, int32_t* __restrict__ tile_list,
+                                                         int32_t* __restrict__ meta) {
+  __shared__ int32_t part[1024];
+  const int t = threadIdx.x;
+  const int ept = (R + 1023) / 1024;
+  const int e0 = min(t * ept, R), e1 = min(e0 + ept, R);
+  int mine = 0;
+  for (int e = e0; e < e1; ++e) mine += (counts[e] + tile_m - 1) / tile_m;
+  part[t] = mine;
+  __syncthreads();
+  for (int s = 1; s < 1024; s <<= 1) {
+    const int a = t >= s ? part[t - s] : 0;
+    __syncthreads();
+    part[t] += a;
+    __syncthreads();
+  }
+  int tb = part[t] - mine;
+  for (int e = e0; e < e1; ++e) {
+    for (int m = 0; m < counts[e]; m += tile_m) {
+      tile_list[2 * tb] = e;
+      tile_list[2 * tb + 1] = m;
+      ++tb;
+    }
+  }
+  if (t == 1023) meta[1] = part[1023];
+}
+
+// Dispatch step 3: stable scatter.  One wave per chunk walks its pairs in
+// order, 64 at a time; a pair's rank among equal experts of its batch is the
+// number of lower lanes with the same expert, and a per-expert cursor in LDS
+// (seeded with the chunk's first positions) carries the order across batches.
+__global__ __launch_bounds__(64) void dispatch_scatter_kernel(const int32_t* __restrict__ ids,
+                                                              int64_t pairs, int R,
+                                                              const int32_t* __restrict__ chunk_base,
+                                                              int32_t* __restrict__ order) {
+  extern __shared__ int32_t cursor[];  // [R] then [64] batch experts
+  int32_t* batch = cursor + R;
+  const int lane = threadIdx.x;
+  for (int e = lane; e < R; e += 64) cursor[e] = chunk_base[(int64_t)blockIdx.x * R + e];
+  __syncthreads();
+  const int64_t q0 = (int64_t)blockIdx.x * kDispatchChunk;
+  const int64_t q1 = min(q0 + kDispatchChunk, pairs);
+  for (int64_t qb = q0; qb < q1; qb += 64) {
+    const int64_t q = qb + lane;
+    const bool valid = q < q1;
+    int e = valid ? ids[q] : -1;
+    if (e < 0 || e >= R) e = -1;  // not counted by the histogram either
+    batch[lane] = e;
+    __syncthreads();
+    int before = 0, after = 0;
+    for (int j = 0; j < 64; ++j) {
+      const int ej = batch[j];
+      before += (j < lane && ej == e) ? 1 : 0;
+      after += (j > lane && ej == e) ? 1 : 0;
+    }
+    int pos = 0;
+    if (e >= 0) {
+      pos = cursor[e] + before;
+      order[pos] = (int32_t)q;
+    }
+    __syncthreads();
+    if (e >= 0 && after == 0) cursor[e] = pos + 1;
+    __syncthreads();
+  }
+}
+
+// Padded copy of the pages' layout: padded[e, r] = z[order[offsets[e] + r] / k]
+// for r < counts[e], zeros up to C.  One workgroup per padded row.
+template <typename T>
+__global__ __launch_bounds__(256) void padded_gather_kernel(const T* __restrict__ z, int ell,
+                                                            const int32_t* __restrict__ counts,
+                                                            const int32_t* __restrict__ offsets,
+                                                            const int32_t* __restrict__ order,
+                                                            int k, int64_t C, T* __restrict__ padded) {
+  const int64_t row = blockIdx.x;  // e * C + r
+  const int e = (int)(row / C), r = (int)(row % C);
+  T* dst = padded + row * ell;
+  const int vec = 16 / (int)sizeof(T);
+  if (r < counts[e]) {
+    const int64_t tok = order[offsets[e] + r] / k;
+    const T* src = z + tok * ell;
+    for (int c = threadIdx.x * vec; c < ell; c += 256 * vec) *(u32x4*)(dst + c) = *(const u32x4*)(src + c);
+  } else {
+    for (int c = threadIdx.x * vec; c < ell; c += 256 * vec) *(u32x4*)(dst + c) = u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+}  // namespace lmoe

@@ -1,0 +1,86 @@
+"""The C ABI library without a GPU: it loads, exports every symbol the header
+declares, sizes workspaces, and rejects bad arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import lmoe_synth as S
+import mixture_experts_ffn_sigmoid_amd as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "latentmoe.h")).read()
+    return sorted(set(re.findall(r"\b(latentmoe_\w+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    lib = M.load()
+    names = _declared()
+    assert set(names) == set(M.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_workspace_sizes_grow_with_tokens():
+    for cfg in S.CONFIGS.values():
+        d1 = M.dims_of(cfg)
+        d2 = M.dims_of(cfg, n_tokens=2 * cfg.n_tokens)
+        for e in range(4):
+            assert M.workspace_bytes(d1, e) > 0
+            assert M.workspace_bytes(d2, e) >= M.workspace_bytes(d1, e)
+    # forward needs at least z, slots and the expert hidden of every pair
+    c = S.CONFIGS["k3full_n8192"]
+    need = c.n_tokens * c.d_latent * 2 + c.pairs * c.d_latent * 4 + c.pairs * c.ff_routed * 2
+    assert M.workspace_bytes(M.dims_of(c), M.ENTRY_FORWARD) >= need
+
+
+def _call_forward(dims, ws_bytes=1 << 40, weights=True):
+    lib = M.load()
+    fake = 4096  # never dereferenced: validation fails first
+    W = M.Weights(*([fake] * 11)) if weights else None
+    C = ctypes.c_int64(-1)
+    return lib.latentmoe_forward(ctypes.byref(dims), ctypes.byref(W) if W else None, fake, fake, fake,
+                                 fake, fake, ctypes.byref(C), fake, ws_bytes, None)
+
+
+@pytest.mark.parametrize("mutate,status", [
+    (dict(top_k=0), 1), (dict(top_k=17), 1), (dict(d_model=0), 1), (dict(beta1=0.0), 1),
+    (dict(rms_eps=-1.0), 1), (dict(dtype=7), 1), (dict(n_tokens=-5), 1),
+    (dict(d_model=100), 2), (dict(ff_routed=96), 2), (dict(n_routed=5000, top_k=2), 2),
+    (dict(top_k=65, n_routed=100), 2), (dict(n_shared=17), 2), (dict(d_latent=8256), 2),
+])
+def test_argument_errors(mutate, status):
+    c = S.CONFIGS["toy_n128"]
+    kw = dict(n_tokens=c.n_tokens, d_model=c.d_model, d_latent=c.d_latent, n_routed=c.n_routed,
+              top_k=c.top_k, n_shared=c.n_shared, ff_routed=c.ff_routed, ff_shared=c.ff_shared,
+              dtype=c.dtype)
+    dims = M.make_dims(**{**kw, **{k: v for k, v in mutate.items() if k in kw}})
+    for k, v in mutate.items():
+        setattr(dims, k, v)
+    assert _call_forward(dims) == status
+    assert M.load().latentmoe_last_error()
+
+
+def test_workspace_and_null_errors():
+    dims = M.dims_of(S.CONFIGS["toy_n128"])
+    assert _call_forward(dims, ws_bytes=10) == 4
+    assert b"workspace" in M.load().latentmoe_last_error()
+    assert _call_forward(dims, weights=False) == 1
+    lib = M.load()
+    C = ctypes.c_int64(0)
+    # dispatch without C_out / route with NULL ids
+    assert lib.latentmoe_dispatch(ctypes.byref(dims), 16, None, 16, 16, 16, None, 0, None, 16, 1 << 30, None) == 1
+    assert lib.latentmoe_route(ctypes.byref(dims), 16, 16, None, None, 16, None, 16, 1 << 30, None) == 1
+    # experts: C outside [1, N]
+    assert lib.latentmoe_experts(ctypes.byref(dims), 16, 0, 16, 16, 16, 16, 16, 16, 16, 16, 16, 1 << 40, None) == 1
+    assert lib.latentmoe_dispatch(ctypes.byref(dims), 16, 16, 16, 16, 16, 16, -1, ctypes.byref(C), 16, 1 << 30, None) == 1
+
+
+def test_status_strings():
+    lib = M.load()
+    for s in range(6):
+        assert lib.latentmoe_status_string(s)

@@ -1,0 +1,245 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 CPU oracle.
+
+Bars: routing ids equal as sets where the oracle's top-k margin exceeds 1e-4
+(valid near-ties otherwise), counts/offsets/order/C and the padded layout
+bit-exact on equal routes, y within max|dy|/rms(y_ref) <= 1e-4 (fp32
+storage) or 2e-2 (bf16 storage)."""
+import numpy as np
+import pytest
+import torch
+
+import lmoe_synth as S
+import mixture_experts_ffn_sigmoid_amd as M
+import oracle as O
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+
+def setup_module(module):
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    M.load()  # fails loudly when the library is missing
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _small_cfgs():
+    base = S.CONFIGS
+    return [
+        base["toy_n128"],
+        base["b05_n4096"],
+        base["b05skew_n4096"],
+        base["toy_n128"].with_(name="toy_n77_ragged", n_tokens=77),
+        base["b05_n4096"].with_(name="b05_n1000_ragged", n_tokens=1000),
+        base["toy_n128"].with_(name="toy_noshared", n_shared=0),
+        base["toy_n128"].with_(name="toy_n1", n_tokens=1),
+        S.LayerConfig("kR_f32", 50, 128, 64, 8, 8, 1, 64, 128, "f32", seed=7),
+        S.LayerConfig("kR_bf16", 70, 128, 64, 6, 6, 3, 128, 64, "bf16", seed=8, bias="uniform"),
+        S.LayerConfig("wide_k_bf16", 333, 256, 128, 40, 9, 1, 192, 256, "bf16", seed=9, bias="uniform"),
+    ]
+
+
+def _forward_parity(cfg, host=None, sample=None):
+    """Run the GPU forward and compare with the oracle; return summary."""
+    _say(f"[forward] {cfg.name} N={cfg.n_tokens}")
+    if host is None and cfg.n_tokens * cfg.d_model < 50_000_000 and cfg.n_routed * cfg.ff_routed * cfg.d_latent < 100_000_000:
+        host = S.host_inputs(cfg)
+    dev = G.device_layer_inputs(cfg, host=host)
+    bufs = G.alloc_forward(cfg)
+    C = G.run_forward(cfg, dev, bufs)
+    ids = bufs["ids"].cpu().numpy()
+    counts = bufs["counts"].cpu().numpy()
+    probs = bufs["probs"].cpu().numpy().astype(np.float64)
+    y = G.download_f64(bufs["y"])
+
+    W = O.config_weights(cfg)
+    x = O.config_x(cfg)
+    routes = O.route(x, W.w_router, W.bias, cfg.top_k)
+    near = G.check_routes(ids, routes, W.bias, cfg.top_k)
+    assert (counts == np.bincount(ids.reshape(-1), minlength=cfg.n_routed)).all()
+    assert C == counts.max()
+    if not near.any():
+        assert (counts == np.bincount(routes.ids.reshape(-1), minlength=cfg.n_routed)).all()
+    # p for the GPU's ids, from the oracle's s
+    sel = np.take_along_axis(routes.s, ids.astype(np.int64), axis=1)
+    np.testing.assert_allclose(probs, sel / sel.sum(1, keepdims=True), rtol=0, atol=2e-5)
+    rows = np.arange(cfg.n_tokens) if sample is None else np.asarray(sample)
+    ref = O.forward(x[rows], W, ids=ids[rows])["y"]
+    err = G.rel_err(y[rows], ref)
+    _say(f"   C={C} near_ties={int(near.sum())} err={err:.3e}")
+    assert err <= G.TOL[cfg.dtype], err
+    return dict(y=bufs["y"], C=C, err=err, dev=dev, bufs=bufs)
+
+
+@pytest.mark.parametrize("cfg", _small_cfgs(), ids=lambda c: c.name)
+def test_forward_parity_small(cfg):
+    _forward_parity(cfg)
+
+
+def test_forward_is_deterministic():
+    cfg = S.CONFIGS["b05skew_n4096"]
+    host = S.host_inputs(cfg)
+    dev = G.device_layer_inputs(cfg, host=host)
+    bufs = G.alloc_forward(cfg)
+    G.run_forward(cfg, dev, bufs)
+    y1 = bufs["y"].clone()
+    G.run_forward(cfg, dev, bufs)
+    assert torch.equal(y1.view(torch.int16), bufs["y"].view(torch.int16))
+
+
+def test_empty_batch_is_noop():
+    cfg = S.CONFIGS["toy_n128"].with_(n_tokens=0)
+    dims = M.dims_of(cfg)
+    dev = G.device_layer_inputs(S.CONFIGS["toy_n128"], host=S.host_inputs(S.CONFIGS["toy_n128"]))
+    z = torch.empty(0, device="cuda")
+    C = M.latentmoe_forward(dims, dev, z, z, z, z, torch.empty(16, dtype=torch.int32, device="cuda"))
+    assert C == 0
+
+
+@pytest.mark.parametrize("name", ["toy_n128", "b05skew_n4096"])
+def test_route_entry(name):
+    cfg = S.CONFIGS[name]
+    _say(f"[route] {name}")
+    host = S.host_inputs(cfg)
+    dev = G.device_layer_inputs(cfg, host=host)
+    N, R, k = cfg.n_tokens, cfg.n_routed, cfg.top_k
+    dims = M.dims_of(cfg)
+    ids = torch.empty((N, k), dtype=torch.int32, device="cuda")
+    probs = torch.empty((N, k), dtype=torch.float32, device="cuda")
+    logits = torch.empty((N, R), dtype=torch.float32, device="cuda")
+    M.latentmoe_route(dims, dev["x"], dev["w_router"], dev["bias"], ids, probs, logits)
+    torch.cuda.synchronize()
+    W = O.config_weights(cfg)
+    x = O.config_x(cfg)
+    routes = O.route(x, W.w_router, W.bias, k)
+    l = logits.cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(l - routes.logits)) <= 1e-5 * max(1.0, np.max(np.abs(routes.logits)))
+    G.check_routes(ids.cpu().numpy(), routes, W.bias, k)
+    # the workspace variant (no logits out) gives the same routes
+    ws = torch.empty(M.workspace_bytes(dims, M.ENTRY_ROUTE), dtype=torch.uint8, device="cuda")
+    ids2, probs2 = torch.empty_like(ids), torch.empty_like(probs)
+    M.latentmoe_route(dims, dev["x"], dev["w_router"], dev["bias"], ids2, probs2, None, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids2) and torch.equal(probs, probs2)
+
+
+def _ids_case(rng, N, R, k, skew=False):
+    if skew:  # most tokens pick the same experts
+        ids = np.stack([np.arange(k) if rng.random() < 0.8 else rng.permutation(R)[:k] for _ in range(N)])
+    else:
+        ids = np.stack([rng.permutation(R)[:k] for _ in range(N)])
+    return ids.astype(np.int32)
+
+
+@pytest.mark.parametrize("case", [
+    dict(N=128, R=16, k=2, l=128, dt="f32"),
+    dict(N=4096, R=16, k=2, l=384, dt="bf16"),
+    dict(N=1500, R=37, k=5, l=64, dt="bf16", skew=True),
+    dict(N=33, R=4, k=4, l=64, dt="f32"),
+    dict(N=1, R=896, k=16, l=128, dt="bf16"),
+    dict(N=3000, R=896, k=16, l=64, dt="bf16"),
+], ids=lambda c: "N{N}_R{R}_k{k}_{dt}".format(**c))
+def test_dispatch_entry_bit_exact(case):
+    _say(f"[dispatch] {case}")
+    rng = np.random.default_rng(case["N"] + case["R"])
+    N, R, k, l, dt = case["N"], case["R"], case["k"], case["l"], case["dt"]
+    ids = _ids_case(rng, N, R, k, case.get("skew", False))
+    z_host = rng.normal(size=(N, l)).astype(np.float32)
+    if dt == "bf16":
+        z_host = S.bf16_bits_to_f32(S.f32_to_bf16_bits(z_host))
+    dims = M.make_dims(N, 64, l, R, k, 0, 64, 0, dt)
+    d_ids = torch.from_numpy(ids).cuda()
+    z = torch.from_numpy(z_host).cuda().to(G.torch_dtype(dt))
+    counts = torch.empty(R, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(R, dtype=torch.int32, device="cuda")
+    order = torch.empty(N * k, dtype=torch.int32, device="cuda")
+    ws = torch.empty(M.workspace_bytes(dims, M.ENTRY_DISPATCH), dtype=torch.uint8, device="cuda")
+    C = M.latentmoe_dispatch(dims, d_ids, None, counts, offsets, order, workspace=ws)
+    ref = O.dispatch(ids, R)
+    assert C == ref.capacity
+    np.testing.assert_array_equal(counts.cpu().numpy(), ref.counts)
+    np.testing.assert_array_equal(offsets.cpu().numpy(), ref.offsets)
+    np.testing.assert_array_equal(order.cpu().numpy(), ref.order)
+    padded = torch.full((R * (C + 3) * l,), float("nan"), dtype=G.torch_dtype(dt), device="cuda")
+    C2 = M.latentmoe_dispatch(dims, d_ids, z, counts, offsets, order, padded, C + 3, workspace=ws)
+    torch.cuda.synchronize()
+    assert C2 == C
+    want = O.padded_layout(z_host.astype(np.float64), ids, R, ref)
+    got = padded[: R * C * l].float().cpu().numpy().reshape(R, C, l)
+    np.testing.assert_array_equal(got, want)
+    assert torch.isnan(padded[R * C * l:]).all()  # beyond R*C*l untouched
+    if C > 1:
+        with pytest.raises(M.LatentMoEError) as ei:
+            M.latentmoe_dispatch(dims, d_ids, z, counts, offsets, order, padded, C - 1, workspace=ws)
+        assert ei.value.status == 3 and f"C={C}" in str(ei.value)
+
+
+@pytest.mark.parametrize("name", ["toy_n128", "b05_n4096", "b05skew_n4096"])
+def test_experts_entry(name):
+    cfg = S.CONFIGS[name]
+    _say(f"[experts] {name}")
+    rng = np.random.default_rng(3)
+    N, R, k, l = cfg.n_tokens, cfg.n_routed, cfg.top_k, cfg.d_latent
+    host = S.host_inputs(cfg)
+    W = O.config_weights(cfg)
+    x = O.config_x(cfg)
+    routes = O.route(x, W.w_router, W.bias, k)
+    ids = routes.ids.astype(np.int32)
+    p = routes.p
+    z_host = rng.normal(size=(N, l)).astype(np.float32)
+    if cfg.dtype == "bf16":
+        z_host = S.bf16_bits_to_f32(S.f32_to_bf16_bits(z_host))
+    dims = M.dims_of(cfg)
+    dt = G.torch_dtype(cfg.dtype)
+    d_ids = torch.from_numpy(ids).cuda()
+    z = torch.from_numpy(z_host).cuda().to(dt)
+    counts = torch.empty(R, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(R, dtype=torch.int32, device="cuda")
+    order = torch.empty(N * k, dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(M.workspace_bytes(dims, M.ENTRY_DISPATCH), M.workspace_bytes(dims, M.ENTRY_EXPERTS)),
+                     dtype=torch.uint8, device="cuda")
+    C = M.latentmoe_dispatch(dims, d_ids, None, counts, offsets, order, workspace=ws)
+    padded = torch.empty((R, C, l), dtype=dt, device="cuda")
+    M.latentmoe_dispatch(dims, d_ids, z, counts, offsets, order, padded, C, workspace=ws)
+    probs = torch.from_numpy(p.astype(np.float32)).cuda()
+    u = torch.empty((N, l), dtype=torch.float32, device="cuda")
+    dev = G.device_layer_inputs(cfg, host=host)
+    M.latentmoe_experts(dims, padded, C, counts, offsets, order, probs, dev["w_g"], dev["w_u"], dev["w_o"],
+                        u, workspace=ws)
+    torch.cuda.synchronize()
+    ref = O.routed_sparse(z_host.astype(np.float64), routes.ids, p.astype(np.float32).astype(np.float64),
+                          W.experts, R, cfg.beta1, cfg.beta2)
+    err = G.rel_err(u.cpu().numpy().astype(np.float64), ref)
+    _say(f"   C={C} err={err:.3e}")
+    assert err <= G.TOL[cfg.dtype]
+
+
+def test_device_generator_matches_host():
+    for name, tensors in [("toy_n128", ["x", "w_g"]), ("b05skew_n4096", ["w_router", "sh_o"]),
+                          ("k3full_n64", ["bias", "w_up"])]:
+        cfg = S.CONFIGS[name]
+        for t in tensors:
+            dev = S.gen.device_tensor(cfg, t)
+            host = S.host_tensor(cfg, t)
+            sdt = S.tensor_spec(cfg, t)[1]
+            got = dev.view(torch.int16).cpu().numpy().view(np.uint16).reshape(-1) if sdt == "bf16" \
+                else dev.cpu().numpy().reshape(-1)
+            mism = int((got != host).sum())
+            _say(f"[synth] {name}.{t}: {mism} mismatches of {host.size}")
+            assert mism == 0
+
+
+@pytest.mark.slow
+def test_forward_parity_k3_decode():
+    cfg = S.CONFIGS["k3full_n64"]
+    _forward_parity(cfg, host=None, sample=[0, 21, 42, 63])
+
+
+@pytest.mark.slow
+def test_forward_parity_k3_prefill():
+    cfg = S.CONFIGS["k3full_n8192"]
+    r = _forward_parity(cfg, host=None, sample=[0, 4097, 8191])
+    assert r["C"] >= 131072 // 896
