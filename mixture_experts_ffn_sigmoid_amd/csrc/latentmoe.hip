@@ -45,9 +45,13 @@ struct Plan {
   int64_t ldh;  // elements per row of the [h_shared | u_normed] buffer
 };
 
-// Row-tile height of the grouped expert GEMMs: 32 for a handful of rows per
-// expert (weight streaming), 128 otherwise.
-int routed_tile_m(int64_t pairs, int R) { return pairs < (int64_t)48 * R ? 32 : 128; }
+// Row-tile height of the grouped expert GEMMs from the mean rows per expert:
+// 64 for a handful (weight streaming), 256 from ~100 rows on (one tile holds a
+// whole expert's rows, so its weights are read once), 128 in between.
+int routed_tile_m(int64_t pairs, int R) {
+  const int64_t mean = pairs / R;
+  return mean < 48 ? 64 : mean < 96 ? 128 : 256;
+}
 
 lmoe_status check_dims(const lmoe_dims* dm, Plan* p) {
   if (!dm) return fail(LMOE_ERR_INVALID_ARGUMENT, "dims is NULL");
@@ -71,8 +75,10 @@ lmoe_status check_dims(const lmoe_dims* dm, Plan* p) {
   if (dm->n_shared > kMaxSeg - 1) return fail(LMOE_ERR_UNSUPPORTED, "n_shared > %d", kMaxSeg - 1);
   if (dm->d_latent > kMaxLatent) return fail(LMOE_ERR_UNSUPPORTED, "d_latent > %d", kMaxLatent);
   const int64_t pairs = dm->n_tokens * dm->top_k;
-  if (pairs > (int64_t)INT32_MAX / 2 || dm->n_tokens > (int64_t)INT32_MAX / 2)
-    return fail(LMOE_ERR_UNSUPPORTED, "too many tokens");
+  const int64_t es = dm->dtype == LMOE_BF16 ? 2 : 4;
+  // gathered expert rows are addressed with 32-bit offsets into z
+  if (pairs > (int64_t)INT32_MAX / 2 || dm->n_tokens * dm->d_latent * es >= ((int64_t)1 << 32))
+    return fail(LMOE_ERR_UNSUPPORTED, "too many tokens (N * l * element size must stay below 4 GiB)");
   p->N = dm->n_tokens;
   p->pairs = pairs;
   p->d = dm->d_model;
@@ -116,7 +122,7 @@ struct ExpertsWs {
   int32_t* tile_list;
   int32_t* meta;
   char* h;
-  float* slots;
+  char* slots;
 };
 struct ForwardWs {
   char* z;
@@ -128,7 +134,7 @@ struct ForwardWs {
   int32_t* order;
   int32_t* tile_list;
   char* h;
-  float* slots;
+  char* slots;
   char* hcat;
 };
 
@@ -149,7 +155,7 @@ size_t carve_experts(const Plan& p, char* b, ExpertsWs* w) {
   w->tile_list = c.take<int32_t>((size_t)p.tile_bound * 8);
   w->meta = c.take<int32_t>(64);
   w->h = c.take<char>((size_t)p.pairs * p.fr * p.es);
-  w->slots = c.take<float>((size_t)p.pairs * p.l * 4);
+  w->slots = c.take<char>((size_t)p.pairs * p.l * p.es);
   return c.off;
 }
 size_t carve_forward(const Plan& p, char* b, ForwardWs* w) {
@@ -163,7 +169,7 @@ size_t carve_forward(const Plan& p, char* b, ForwardWs* w) {
   w->order = c.take<int32_t>((size_t)p.pairs * 4);
   w->tile_list = c.take<int32_t>((size_t)p.tile_bound * 8);
   w->h = c.take<char>((size_t)p.pairs * p.fr * p.es);
-  w->slots = c.take<float>((size_t)p.pairs * p.l * 4);
+  w->slots = c.take<char>((size_t)p.pairs * p.l * p.es);
   w->hcat = c.take<char>((size_t)p.N * p.ldh * p.es);
   return c.off;
 }
@@ -175,26 +181,41 @@ lmoe_status launch_gemm(GemmArgs a, hipStream_t st) {
   const int64_t grid = (int64_t)a.m_tiles * a.n_tiles;
   if (grid <= 0) return LMOE_OK;
   if (grid > INT32_MAX) return fail(LMOE_ERR_UNSUPPORTED, "GEMM grid too large");
-  gemm_kernel<TA, TB, OutT, BM, BN, WGM, WGN, AM, BMD, EM><<<(unsigned)grid, 256, 0, st>>>(a);
+  gemm_kernel<TA, TB, OutT, BM, BN, WGM, WGN, AM, BMD, EM><<<(unsigned)grid, 64 * WGM * WGN, 0, st>>>(a);
   LMOE_HIP(hipGetLastError());
   return LMOE_OK;
 }
 
-// Tile shapes: "small" = 32-row tiles for few-token products, "large" = 128x128.
+// Block tiles: S = 64 x 128 (x 256 for gate/up pairs) for few-row products
+// (weight streaming), M = 128 x 128 (4 waves), L = 256 x 256 (8 waves, wave tile 128 x 64).
+enum Tile { TILE_S = 0, TILE_M = 1, TILE_L = 2 };
+constexpr int tile_rows(Tile t) { return t == TILE_S ? 64 : t == TILE_M ? 128 : 256; }
+
+template <typename TA, typename TB, typename OutT, int AM, int BMD, int EM, int BM, int BN, int WGM,
+          int WGN>
+lmoe_status gemm_cfg(GemmArgs a, hipStream_t st) {
+  constexpr int cols = BMD == B_DUAL ? BN / 2 : BN;
+  a.n_tiles = (a.N + cols - 1) / cols;
+  if (AM == A_DENSE) a.m_tiles = (a.M + BM - 1) / BM;
+  return launch_gemm<TA, TB, OutT, BM, BN, WGM, WGN, AM, BMD, EM>(a, st);
+}
+
 template <typename TA, typename TB, typename OutT, int AM, int BMD, int EM>
-lmoe_status gemm(GemmArgs a, bool small, hipStream_t st) {
+lmoe_status gemm(GemmArgs a, Tile t, hipStream_t st) {
   constexpr bool dual = BMD == B_DUAL;
-  if (small) {
-    constexpr int BM = 32, BN = dual ? 256 : 128;
-    a.n_tiles = (a.N + (dual ? BN / 2 : BN) - 1) / (dual ? BN / 2 : BN);
-    if (AM == A_DENSE) a.m_tiles = (a.M + BM - 1) / BM;
-    return launch_gemm<TA, TB, OutT, BM, BN, 1, 4, AM, BMD, EM>(a, st);
-  } else {
-    constexpr int BM = 128, BN = 128;
-    a.n_tiles = (a.N + (dual ? BN / 2 : BN) - 1) / (dual ? BN / 2 : BN);
-    if (AM == A_DENSE) a.m_tiles = (a.M + BM - 1) / BM;
-    return launch_gemm<TA, TB, OutT, BM, BN, 2, 2, AM, BMD, EM>(a, st);
+  switch (t) {
+    case TILE_S: return gemm_cfg<TA, TB, OutT, AM, BMD, EM, 64, dual ? 256 : 128, 1, 4>(a, st);
+    case TILE_M: return gemm_cfg<TA, TB, OutT, AM, BMD, EM, 128, 128, 2, 2>(a, st);
+    default: return gemm_cfg<TA, TB, OutT, AM, BMD, EM, 256, 256, 2, 4>(a, st);
   }
+}
+
+// Dense products: 32-row tiles for a handful of tokens, 256 x 256 when that
+// still gives about one tile per compute unit, else 128 x 128.
+Tile dense_tile(int64_t M, int64_t cols, bool dual) {
+  if (M <= 64) return TILE_S;
+  const int64_t big = ((M + 255) / 256) * ((cols + (dual ? 127 : 255)) / (dual ? 128 : 256));
+  return big >= 240 ? TILE_L : TILE_M;
 }
 
 GemmArgs base_args(const lmoe_dims* dm) {
@@ -228,7 +249,7 @@ lmoe_status run_route(const Plan& p, const lmoe_dims* dm, const void* x, const v
   a.nb_rows = p.R;
   a.out = (char*)logits;
   a.ldo = (int64_t)p.R * 4;
-  LMOE_TRY((gemm<T, T, float, A_DENSE, B_SINGLE, E_STORE>(a, p.N <= 64, st)));
+  LMOE_TRY((gemm<T, T, float, A_DENSE, B_SINGLE, E_STORE>(a, dense_tile(p.N, p.R, false), st)));
   const unsigned blocks = (unsigned)((p.N + 3) / 4);
   topk_route_kernel<<<blocks, 256, 4 * p.R * sizeof(float), st>>>(logits, bias, p.N, p.R, p.k, ids,
                                                                   probs);
@@ -258,11 +279,11 @@ template <typename TA, typename TW, typename TH, int AM, typename Mark = lmoe_st
 lmoe_status run_experts(const Plan& p, const lmoe_dims* dm, const void* a_src, int64_t cap,
                         const int32_t* counts, const int32_t* offsets, const int32_t* order,
                         const float* probs, const void* w_g, const void* w_u, const void* w_o,
-                        int32_t* tile_list, int32_t* meta, char* h, float* slots, hipStream_t st,
+                        int32_t* tile_list, int32_t* meta, char* h, char* slots, hipStream_t st,
                         Mark* mark = nullptr) {
   tile_list_kernel<<<1, 1024, 0, st>>>(counts, p.R, p.tile_m, tile_list, meta);
   LMOE_HIP(hipGetLastError());
-  const bool small = p.tile_m == 32;
+  const Tile tile = p.tile_m == 64 ? TILE_S : p.tile_m == 128 ? TILE_M : TILE_L;
   GemmArgs a = base_args(dm);
   a.N = p.fr;
   a.K = p.l;
@@ -283,7 +304,7 @@ lmoe_status run_experts(const Plan& p, const lmoe_dims* dm, const void* a_src, i
   a.nb_rows = p.fr;
   a.out = h;
   a.ldo = (int64_t)p.fr * p.es;
-  LMOE_TRY((gemm<TA, TW, TH, AM, B_DUAL, E_SITU>(a, small, st)));
+  LMOE_TRY((gemm<TA, TW, TH, AM, B_DUAL, E_SITU>(a, tile, st)));
   if (mark) LMOE_TRY((*mark)());
 
   GemmArgs b = base_args(dm);
@@ -302,10 +323,10 @@ lmoe_status run_experts(const Plan& p, const lmoe_dims* dm, const void* a_src, i
   b.ldb = (int64_t)p.fr * p.es;
   b.b_expert_stride = (int64_t)p.l * p.fr * p.es;
   b.nb_rows = p.l;
-  b.out = (char*)slots;
-  b.ldo = (int64_t)p.l * 4;
+  b.out = slots;
+  b.ldo = (int64_t)p.l * sizeof(TH);
   b.probs = probs;
-  return gemm<TH, TW, float, A_SORTED, B_SINGLE, E_SLOTS>(b, small, st);
+  return gemm<TH, TW, TH, A_SORTED, B_SINGLE, E_SLOTS>(b, tile, st);
 }
 
 // T: storage type (x, weights, y); TI: intermediate type of z, h and the
@@ -314,7 +335,6 @@ template <typename T, typename TI>
 lmoe_status run_forward(const Plan& p, const lmoe_dims* dm, const lmoe_weights* W, const void* x,
                         void* y, int32_t* ids, float* probs, int32_t* counts, const ForwardWs& w,
                         hipStream_t st, hipEvent_t* ev) {
-  const bool small = p.N <= 64;
   int step = 0;
   auto mark = [&]() -> lmoe_status {  // optional per-step timing events
     if (ev) LMOE_HIP(hipEventRecord(ev[step], st));
@@ -334,7 +354,7 @@ lmoe_status run_forward(const Plan& p, const lmoe_dims* dm, const lmoe_weights* 
   a.nb_rows = p.l;
   a.out = w.z;
   a.ldo = (int64_t)p.l * p.es;
-  LMOE_TRY((gemm<T, T, TI, A_DENSE, B_SINGLE, E_STORE>(a, small, st)));
+  LMOE_TRY((gemm<T, T, TI, A_DENSE, B_SINGLE, E_STORE>(a, dense_tile(p.N, p.l, false), st)));
   LMOE_TRY(mark());
   // 2. routing
   LMOE_TRY(run_route<T>(p, dm, x, W->w_router, W->bias, ids, probs, w.logits, st));
@@ -356,7 +376,7 @@ lmoe_status run_forward(const Plan& p, const lmoe_dims* dm, const lmoe_weights* 
     s.nb_rows = p.ns * p.fs;
     s.out = w.hcat;
     s.ldo = p.ldh * p.es;
-    LMOE_TRY((gemm<T, T, TI, A_DENSE, B_DUAL, E_SITU>(s, small, st)));
+    LMOE_TRY((gemm<T, T, TI, A_DENSE, B_DUAL, E_SITU>(s, dense_tile(p.N, s.N, true), st)));
   }
   LMOE_TRY(mark());
   // 3b. routed experts straight from z -> slots
@@ -365,8 +385,8 @@ lmoe_status run_forward(const Plan& p, const lmoe_dims* dm, const lmoe_weights* 
                                      ev ? &mark : nullptr)));
   LMOE_TRY(mark());
   // 5a. u = sum of slots, RMSNorm -> hcat[:, n_s f_s:]
-  combine_rmsnorm_kernel<TI><<<(unsigned)p.N, 256, 0, st>>>(
-      w.slots, p.k, p.l, nullptr, W->rms_w, dm->rms_eps,
+  combine_rmsnorm_kernel<TI, TI><<<(unsigned)p.N, 256, 0, st>>>(
+      (const TI*)w.slots, p.k, p.l, nullptr, W->rms_w, dm->rms_eps,
       (TI*)(w.hcat + (int64_t)p.ns * p.fs * p.es), p.ldh);
   LMOE_HIP(hipGetLastError());
   LMOE_TRY(mark());
@@ -378,7 +398,7 @@ lmoe_status run_forward(const Plan& p, const lmoe_dims* dm, const lmoe_weights* 
   f.a = w.hcat;
   f.lda = p.ldh * p.es;
   f.nb_rows = p.d;
-  const int kt_per_fs = p.fs * p.es / 128;
+  const int kt_per_fs = p.fs * p.es / kKStepBytes;
   f.nseg = p.ns + 1;
   for (int j = 0; j < p.ns; ++j) {
     f.seg_base[j] = (const char*)W->sh_o + (int64_t)j * p.d * p.fs * p.es;
@@ -388,10 +408,10 @@ lmoe_status run_forward(const Plan& p, const lmoe_dims* dm, const lmoe_weights* 
   f.seg_base[p.ns] = (const char*)W->w_up;
   f.seg_ld[p.ns] = (int64_t)p.l * p.es;
   f.seg_kt0[p.ns] = p.ns * kt_per_fs;
-  f.seg_kt0[p.ns + 1] = (int)(p.ldh * p.es / 128);
+  f.seg_kt0[p.ns + 1] = (int)(p.ldh * p.es / kKStepBytes);
   f.out = (char*)y;
   f.ldo = (int64_t)p.d * p.es;
-  LMOE_TRY((gemm<TI, T, T, A_DENSE, B_KSEG, E_STORE>(f, small, st)));
+  LMOE_TRY((gemm<TI, T, T, A_DENSE, B_KSEG, E_STORE>(f, dense_tile(p.N, p.d, false), st)));
   return mark();
 }
 
@@ -527,11 +547,11 @@ lmoe_status latentmoe_experts(const lmoe_dims* dims, const void* padded, int64_t
     LMOE_TRY((run_experts<float, float, float, A_PADDED>(p, dims, padded, C, counts, offsets, order, probs, w_g, w_u,
                                            w_o, w.tile_list, w.meta, w.h, w.slots, st)));
   if (p.bf16)
-    combine_rmsnorm_kernel<f16_t><<<(unsigned)p.N, 256, 0, st>>>(w.slots, p.k, p.l, u, nullptr, 0.f,
-                                                                 nullptr, 0);
+    combine_rmsnorm_kernel<f16_t, f16_t><<<(unsigned)p.N, 256, 0, st>>>(
+        (const f16_t*)w.slots, p.k, p.l, u, nullptr, 0.f, nullptr, 0);
   else
-    combine_rmsnorm_kernel<float><<<(unsigned)p.N, 256, 0, st>>>(w.slots, p.k, p.l, u, nullptr, 0.f,
-                                                                 nullptr, 0);
+    combine_rmsnorm_kernel<float, float><<<(unsigned)p.N, 256, 0, st>>>(
+        (const float*)w.slots, p.k, p.l, u, nullptr, 0.f, nullptr, 0);
   LMOE_HIP(hipGetLastError());
   return LMOE_OK;
 }

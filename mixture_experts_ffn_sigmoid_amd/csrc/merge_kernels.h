@@ -8,12 +8,12 @@ namespace lmoe {
 
 constexpr int kMaxLatent = 8192;  // 8 float4 per thread of a 256-thread workgroup
 
-// One workgroup per token n:
-//   u[c] = sum_{j < k} slots[(n k + j) l + c]      (slot order, fp32)
+// One workgroup per token n (slots of type TS, summed in fp32):
+//   u[c] = sum_{j < k} slots[(n k + j) l + c]      (slot order)
 //   u_out[n, c] = u[c]                               (if u_out)
 //   dst[n, c]   = T(w[c] u[c] / sqrt(mean(u^2) + eps)) (if dst; w = 1 when rms_w is NULL)
-template <typename T>
-__global__ __launch_bounds__(256) void combine_rmsnorm_kernel(const float* __restrict__ slots, int k,
+template <typename TS, typename T>
+__global__ __launch_bounds__(256) void combine_rmsnorm_kernel(const TS* __restrict__ slots, int k,
                                                               int ell, float* __restrict__ u_out,
                                                               const float* __restrict__ rms_w,
                                                               float eps, T* __restrict__ dst,
@@ -29,7 +29,11 @@ __global__ __launch_bounds__(256) void combine_rmsnorm_kernel(const float* __res
     const int c = 4 * t + 1024 * i;
     u[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (c < ell) {
-      for (int j = 0; j < k; ++j) u[i] += *(const f32x4*)(slots + ((n * k + j) * ell + c));
+      for (int j = 0; j < k; ++j) {
+        const TS* src = slots + ((n * k + j) * ell + c);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) u[i][q] += Elem<TS>::load(src + q);
+      }
       ss += u[i][0] * u[i][0] + u[i][1] * u[i][1] + u[i][2] * u[i][2] + u[i][3] * u[i][3];
       if (u_out) *(f32x4*)(u_out + n * ell + c) = u[i];
     }

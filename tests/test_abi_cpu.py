@@ -32,9 +32,9 @@ def test_workspace_sizes_grow_with_tokens():
         for e in range(4):
             assert M.workspace_bytes(d1, e) > 0
             assert M.workspace_bytes(d2, e) >= M.workspace_bytes(d1, e)
-    # forward needs at least z, slots and the expert hidden of every pair
+    # forward needs at least z, the slots and the expert hidden of every pair (16-bit)
     c = S.CONFIGS["k3full_n8192"]
-    need = c.n_tokens * c.d_latent * 2 + c.pairs * c.d_latent * 4 + c.pairs * c.ff_routed * 2
+    need = c.n_tokens * c.d_latent * 2 + c.pairs * c.d_latent * 2 + c.pairs * c.ff_routed * 2
     assert M.workspace_bytes(M.dims_of(c), M.ENTRY_FORWARD) >= need
 
 
