@@ -77,14 +77,67 @@ def cpu_baseline(cfg, n_sample: int):
                       f"{len(need)} routed experts touched); {dt:.1f} s"}
 
 
+KERNEL_SOURCES = ("mixture_experts_ffn_sigmoid_amd/csrc/gemm_kernel.h",
+                  "mixture_experts_ffn_sigmoid_amd/csrc/lmoe_common.h",
+                  "mixture_experts_ffn_sigmoid_amd/csrc/latentmoe.hip")
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(step: str, workload: str):
+    """HBM bytes per launch of `step` from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE, scaled by the copy-kernel
+    calibration), or None when there is none or the kernels changed since."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{step}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_hash") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(nbytes: int = 1 << 30, reps: int = 5):
+    """A plain device-to-device copy of known size (torch's copy kernel), run
+    under rocprofv3 --pmc to calibrate FETCH_SIZE / WRITE_SIZE."""
+    import torch
+
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "reps": reps}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="k3full_n8192", choices=sorted(S.CONFIGS))
-    ap.add_argument("--cpu-sample", type=int, default=8, help="tokens for the CPU oracle baseline (0: skip)")
+    ap.add_argument("--cpu-sample", type=int, default=24, help="tokens for the CPU oracle baseline (0: skip)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a 1 GiB device copy (FETCH_SIZE / WRITE_SIZE calibration)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        copy_calibration()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the layer would shard tokens or experts; see the design notes).", file=sys.stderr)
@@ -151,7 +204,10 @@ def main():
         roof = {"kernel": dominant, "bound": "hbm", "achieved": round(by / t_dom / 1e9, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = None
+    roof["algorithmic_bytes"] = by
+    roof["algorithmic_flops"] = fl
+    roof["ms"] = round(step_ms[dominant], 4)
+    roof["traffic"] = measured_traffic(dominant, cfg.name)
 
     flops = cfg.flops()
     tok_s = cfg.n_tokens / (ms_step / 1e3)

@@ -84,8 +84,10 @@ constexpr int vmcnt_imm(int n) { return (n & 0xF) | (((n >> 4) & 3) << 14) | (0x
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
+constexpr int gcd_(int a, int b) { return b == 0 ? a : gcd_(b, a % b); }
+
 template <typename TA, typename TB, typename OutT, int BM, int BN, int WGM, int WGN, int AMODE,
-          int BMODE, int EMODE>
+          int BMODE, int EMODE, int SA, int SB>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs args) {
   static_assert(sizeof(TA) == sizeof(TB), "operand element sizes must match");
   constexpr bool kHalf = sizeof(TA) == 2;  // 16-bit operands
@@ -99,14 +101,20 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
   // 64 lanes x 16 bytes = 16 tile rows.
   constexpr int ROWB = kKStepBytes;
   constexpr int A_INST = BM / 16, B_INST = BN / 16;
-  constexpr int INST = (A_INST + B_INST) / NW;  // DMA instructions per wave per K step
-  constexpr int STAGES = 4;
-  constexpr int kStage = (BM + BN) * ROWB;
+  constexpr int A_W = A_INST / NW, B_W = B_INST / NW;  // DMA instructions per wave per K step
+  // Two LDS rings: SA stages of A rows and SB >= SA stages of B rows (the
+  // B ring is deeper where B is the HBM-streamed weight matrix).
+  constexpr int kStageA = BM * ROWB, kStageB = BN * ROWB;
+  constexpr int RING = SA * kStageA + SB * kStageB;
+  constexpr int UNROLL = SA * SB / gcd_(SA, SB);
   static_assert(NW == 4 || NW == 8, "4 or 8 waves per workgroup");
   static_assert(TM >= 1 && TN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "32x32 sub-tiles");
   static_assert(BMODE != B_DUAL || TN % 2 == 0, "dual tile needs gate and up sub-tiles");
-  static_assert((A_INST + B_INST) % NW == 0 && BM % 16 == 0 && BN % 16 == 0, "DMA split");
-  __shared__ __attribute__((aligned(1024))) char smem[STAGES * kStage];
+  static_assert(A_INST % NW == 0 && B_INST % NW == 0 && BM % 16 == 0 && BN % 16 == 0, "DMA split");
+  static_assert(SA >= 2 && SB >= SA && UNROLL <= 8, "ring shape");
+  __shared__ __attribute__((aligned(1024))) char smem[RING];
+  char* const ringA = smem;
+  char* const ringB = smem + SA * kStageA;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
@@ -147,71 +155,65 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
     rows_valid = min(BM, args.M - m0);
   }
 
-  // ---- DMA plan.  Wave `wave` moves tile-row blocks (wave*INST + ii)*16 ...
-  // of the stacked [A rows | B rows] tile.  Lane l carries tile row
-  // block*16 + l/4 and lands at LDS slot l%4 of that row; it fetches global
-  // 16-byte chunk (l%4) ^ ((l>>4)&3), i.e. rows are XOR-swizzled so that the
-  // fragment reads of 16 consecutive rows hit 16 distinct bank groups.
-  // Rows past the valid range are clamped to the last valid row: every DMA
-  // instruction is always issued, which keeps the vmcnt accounting exact.
+  // ---- DMA plan.  For each operand, wave `wave` moves 16-row blocks
+  // wave*X_W + ii of the tile.  Lane l carries tile row block*16 + l/4 and
+  // lands at LDS slot l%4 of that row; it fetches global 16-byte chunk
+  // (l%4) ^ ((l>>4)&3), i.e. rows are XOR-swizzled so that the fragment
+  // reads of 16 consecutive rows hit 16 distinct bank groups.  Rows past the
+  // valid range are clamped to the last valid row: every DMA instruction is
+  // always issued, which keeps the vmcnt accounting exact.
   const uint32_t lane_chunk = (uint32_t)(((lane & 3) ^ ((lane >> 4) & 3)) * 16);
   constexpr int H = BMODE == B_DUAL ? BN / 2 : BN;  // rows of one B matrix per tile
   const int b_rows_here = min(H, args.nb_rows - nt * H);
-  const char* dma_base[INST];  // workgroup-uniform
-  uint32_t dma_off[INST];      // per lane, K step 0
-  int dma_brow[INST];          // B_KSEG: clamped row inside the tile's slice
-  bool dma_is_b[INST];
+  const char* a_base;
+  uint32_t a_off[A_W];
+  if constexpr (AMODE == A_GATHER) a_base = args.a;
+  else if constexpr (AMODE == A_PADDED) a_base = args.a + ((int64_t)e * args.cap + m0) * args.lda;
+  else if constexpr (AMODE == A_SORTED) a_base = args.a + (off + m0) * args.lda;
+  else a_base = args.a + (int64_t)m0 * args.lda;
 #pragma unroll
-  for (int ii = 0; ii < INST; ++ii) {
-    const int blk = wave * INST + ii;
-    const int trow = blk * 16 + (lane >> 2);
-    dma_brow[ii] = 0;
-    if (blk < A_INST) {
-      dma_is_b[ii] = false;
-      const int rr = min(trow, rows_valid - 1);
-      int64_t row = rr;
-      if constexpr (AMODE == A_GATHER) {
-        row = args.order[off + m0 + rr] / args.top_k;
-        dma_base[ii] = args.a;
-      } else if constexpr (AMODE == A_PADDED) {
-        dma_base[ii] = args.a + ((int64_t)e * args.cap + m0) * args.lda;
-      } else if constexpr (AMODE == A_SORTED) {
-        dma_base[ii] = args.a + (off + m0) * args.lda;
-      } else {
-        dma_base[ii] = args.a + (int64_t)m0 * args.lda;
-      }
-      dma_off[ii] = (uint32_t)(row * args.lda) + lane_chunk;
-    } else {
-      dma_is_b[ii] = true;
-      const int r = trow - BM;
-      const bool up = BMODE == B_DUAL && r >= H;
-      const int br = min(up ? r - H : r, b_rows_here - 1);
-      dma_brow[ii] = br;
-      dma_base[ii] = (up ? args.b1 : args.b0) + (int64_t)e * args.b_expert_stride +
-                     (int64_t)nt * H * args.ldb;
-      dma_off[ii] = (uint32_t)(br * args.ldb) + lane_chunk;
-    }
+  for (int ii = 0; ii < A_W; ++ii) {
+    const int rr = min((wave * A_W + ii) * 16 + (lane >> 2), rows_valid - 1);
+    int64_t row = rr;
+    if constexpr (AMODE == A_GATHER) row = args.order[off + m0 + rr] / args.top_k;
+    a_off[ii] = (uint32_t)(row * args.lda) + lane_chunk;
+  }
+  const char* b_base[B_W];  // workgroup-uniform
+  uint32_t b_off[B_W];      // per lane, K step 0
+  int b_brow[B_W];          // clamped row inside the tile's slice of its matrix
+#pragma unroll
+  for (int ii = 0; ii < B_W; ++ii) {
+    const int r = (wave * B_W + ii) * 16 + (lane >> 2);
+    const bool up = BMODE == B_DUAL && r >= H;
+    const int br = min(up ? r - H : r, b_rows_here - 1);
+    b_brow[ii] = br;
+    b_base[ii] = (up ? args.b1 : args.b0) + (int64_t)e * args.b_expert_stride + (int64_t)nt * H * args.ldb;
+    b_off[ii] = (uint32_t)(br * args.ldb) + lane_chunk;
   }
 
-  auto issue_dma = [&](int kt, char* stage) {
+  auto issue_a = [&](int kt, char* stage) {
+#pragma unroll
+    for (int ii = 0; ii < A_W; ++ii) {
+      const char* g = a_base + (a_off[ii] + (uint32_t)kt * ROWB);
+      __builtin_amdgcn_global_load_lds((const void*)g, (lds_void_t*)(stage + (wave * A_W + ii) * 16 * ROWB), 16, 0, 0);
+    }
+  };
+  auto issue_b = [&](int kt, char* stage) {
     if constexpr (BMODE == B_KSEG) {
       int s = 0;
       while (s + 1 < args.nseg && kt >= args.seg_kt0[s + 1]) ++s;
       const int64_t ld = args.seg_ld[s];
       const char* bbase = args.seg_base[s] + (int64_t)nt * BN * ld + (int64_t)(kt - args.seg_kt0[s]) * ROWB;
 #pragma unroll
-      for (int ii = 0; ii < INST; ++ii) {
-        const int blk = wave * INST + ii;
-        const char* g = dma_is_b[ii] ? bbase + ((uint32_t)(dma_brow[ii] * ld) + lane_chunk)
-                                     : dma_base[ii] + (dma_off[ii] + (uint32_t)kt * ROWB);
-        __builtin_amdgcn_global_load_lds((const void*)g, (lds_void_t*)(stage + blk * 16 * ROWB), 16, 0, 0);
+      for (int ii = 0; ii < B_W; ++ii) {
+        const char* g = bbase + ((uint32_t)(b_brow[ii] * ld) + lane_chunk);
+        __builtin_amdgcn_global_load_lds((const void*)g, (lds_void_t*)(stage + (wave * B_W + ii) * 16 * ROWB), 16, 0, 0);
       }
     } else {
 #pragma unroll
-      for (int ii = 0; ii < INST; ++ii) {
-        const int blk = wave * INST + ii;
-        const char* g = dma_base[ii] + (dma_off[ii] + (uint32_t)kt * ROWB);
-        __builtin_amdgcn_global_load_lds((const void*)g, (lds_void_t*)(stage + blk * 16 * ROWB), 16, 0, 0);
+      for (int ii = 0; ii < B_W; ++ii) {
+        const char* g = b_base[ii] + (b_off[ii] + (uint32_t)kt * ROWB);
+        __builtin_amdgcn_global_load_lds((const void*)g, (lds_void_t*)(stage + (wave * B_W + ii) * 16 * ROWB), 16, 0, 0);
       }
     }
   };
@@ -238,9 +240,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
   // Multiply one K step held in LDS.  NA = number of this wave's 32-row
   // sub-tiles that hold valid rows (a wave-uniform constant of the
   // instantiation, so the step is straight-line code).
-  auto compute = [&](const char* As, auto na_c) {
+  auto compute = [&](const char* As, const char* Bs, auto na_c) {
     constexpr int NA = decltype(na_c)::value;
-    const char* Bs = As + BM * ROWB;
     // two fragment chunks per lane per K step:
     //   16-bit: chunk lh holds k 8lh..8lh+7 of step 0, chunk 2+lh those of step 1
     //   fp32:   chunks 2lh and 2lh+1 hold k 8lh..8lh+7, one k per MFMA
@@ -282,46 +283,55 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
     }
   };
 
-  // ---- main loop: a 4-deep LDS ring.  Tile t sits in stage t % 4; the DMA
-  // of tile t + 3 is issued right after the barrier that opens step t, so
-  // three K steps of loads are in flight while one is multiplied.  The
-  // stage it overwrites (t - 1) was released by that same barrier.
+  // ---- main loop.  Tile t of A sits in A stage t % SA, of B in B stage
+  // t % SB.  Step s issues, right after its barrier, the B DMA of tile
+  // s + SB - 1 and then the A DMA of tile s + SA - 1; each overwrites the
+  // stage that step s - 1 read, which that same barrier released.  With B
+  // issued first in every step (and SB >= SA), waiting for A of tile kt also
+  // covers B of tile kt, so one vmcnt per step suffices: the operations
+  // issued after A(kt) are B tiles kt+SB-SA+1 .. kt+SB-2 and A tiles
+  // kt+1 .. kt+SA-2 (SA-2 of each).
   const int KT = args.K * (int)sizeof(TA) / ROWB;
+  constexpr int kNewer = (SA - 2) * (B_W + A_W);  // steady-state vmcnt
 #pragma unroll
-  for (int t = 0; t < STAGES - 1; ++t)
-    if (t < KT) issue_dma(t, smem + t * kStage);
-  // wait for this wave's DMAs of tile kt with `later` newer tiles still in
-  // flight, then make every wave's DMAs of tile kt visible
-  auto sync_tile = [&](auto later_c) {
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(decltype(later_c)::value * INST));
+  for (int s = -(SB - 1); s < 0; ++s) {  // the steps before step 0, issue part only
+    const int tb = s + SB - 1, ta = s + SA - 1;
+    if (tb >= 0 && tb < KT) issue_b(tb, ringB + tb * kStageB);
+    if (ta >= 0 && ta < KT) issue_a(ta, ringA + ta * kStageA);
+  }
+  auto barrier = [&]() {
     asm volatile("" ::: "memory");  // no LDS access may move across the barrier
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
-  using C0 = IntC<0>;
-  using C1 = IntC<1>;
-  using C2 = IntC<2>;
-  const int n_steady = KT > 2 ? KT - 2 : 0;
+  // steady steps: every tile counted in kNewer exists (kt + SB - 2 < KT)
+  const int n_steady = KT - SB + 2 > 0 ? KT - SB + 2 : 0;
   auto main_loop = [&](auto na_c) {
-    // steady steps kt = 0 .. KT-3 (two newer tiles in flight), static stages
-    auto steady = [&](int kt, char* cur, char* refill) {
-      sync_tile(C2{});
-      if (kt + 3 < KT) issue_dma(kt + 3, refill);
-      compute(cur, na_c);
+    auto steady = [&](int kt, auto u_c) {
+      constexpr int u = decltype(u_c)::value;  // kt % UNROLL, stages are static
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kNewer));
+      barrier();
+      if (kt + SB - 1 < KT) issue_b(kt + SB - 1, ringB + ((u + SB - 1) % SB) * kStageB);
+      if (kt + SA - 1 < KT) issue_a(kt + SA - 1, ringA + ((u + SA - 1) % SA) * kStageA);
+      compute(ringA + (u % SA) * kStageA, ringB + (u % SB) * kStageB, na_c);
     };
-    for (int kt = 0; kt < n_steady; kt += STAGES) {
-      steady(kt, smem + 0 * kStage, smem + 3 * kStage);
-      if (kt + 1 < n_steady) steady(kt + 1, smem + 1 * kStage, smem + 0 * kStage);
-      if (kt + 2 < n_steady) steady(kt + 2, smem + 2 * kStage, smem + 1 * kStage);
-      if (kt + 3 < n_steady) steady(kt + 3, smem + 3 * kStage, smem + 2 * kStage);
+    for (int kt = 0; kt < n_steady; kt += UNROLL) {
+      steady(kt, IntC<0>{});
+      if constexpr (UNROLL > 1) if (kt + 1 < n_steady) steady(kt + 1, IntC<1>{});
+      if constexpr (UNROLL > 2) if (kt + 2 < n_steady) steady(kt + 2, IntC<2>{});
+      if constexpr (UNROLL > 3) if (kt + 3 < n_steady) steady(kt + 3, IntC<3>{});
+      if constexpr (UNROLL > 4) if (kt + 4 < n_steady) steady(kt + 4, IntC<4>{});
+      if constexpr (UNROLL > 5) if (kt + 5 < n_steady) steady(kt + 5, IntC<5>{});
+      if constexpr (UNROLL > 6) if (kt + 6 < n_steady) steady(kt + 6, IntC<6>{});
+      if constexpr (UNROLL > 7) if (kt + 7 < n_steady) steady(kt + 7, IntC<7>{});
     }
-    // last two steps: one, then no newer tile in flight
-    if (KT >= 2) {
-      sync_tile(C1{});
-      compute(smem + ((KT - 2) & 3) * kStage, na_c);
+    // last SB-2 steps: full waits (stage indices are no longer static here)
+    for (int kt = n_steady; kt < KT; ++kt) {
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      barrier();
+      if (kt + SA - 1 < KT) issue_a(kt + SA - 1, ringA + ((kt + SA - 1) % SA) * kStageA);
+      compute(ringA + (kt % SA) * kStageA, ringB + (kt % SB) * kStageB, na_c);
     }
-    sync_tile(C0{});
-    compute(smem + ((KT - 1) & 3) * kStage, na_c);
   };
   if constexpr (GROUPED) {
     // sub-tiles of this wave that hold valid rows (uniform across the wave)
@@ -343,30 +353,90 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
     main_loop(IntC<TM>{});
   }
 
-  // ---- epilogue
+  // ---- epilogue.  Each wave stages its finished output tile in LDS (the
+  // operand ring is free once every wave has passed the barrier below) and
+  // writes it back as 16-byte row chunks; falls back to per-element stores
+  // when the staged tile would not fit.
   constexpr int TJ = (BMODE == B_DUAL) ? TN / 2 : TN;
+  constexpr int OCOLS = TJ * 32;  // output columns of one wave
+  constexpr int OES = (int)sizeof(OutT);
+  constexpr int CPR = OCOLS * OES / 16;  // 16-byte chunks per staged row
+  constexpr bool kPad = WTM * (OCOLS * OES + 16) * NW <= RING;
+  constexpr bool kSwz = !kPad && WTM * OCOLS * OES * NW <= RING && CPR >= 8;
+  constexpr bool kStaged = (kPad || kSwz) && (OCOLS * OES) % 16 == 0;
+  constexpr int EROW = OCOLS * OES + (kPad ? 16 : 0);
+  const float inv_b1 = 1.0f / args.beta1, inv_b2 = 1.0f / args.beta2;
+  const int col0 = BMODE == B_DUAL ? nt * (BN / 2) + wn * (WTN / 2) : nt * BN + wn * WTN;
+
+  auto value = [&](int i, int j, int v) -> float {
+    if constexpr (EMODE == E_SITU)
+      return situ_hidden(acc[i][j][v], acc[i][j + TN / 2][v], args.beta1, args.beta2, inv_b1, inv_b2);
+    else
+      return acc[i][j][v];
+  };
+  auto out_row = [&](int r) -> int64_t {  // r: row inside the block tile
+    if constexpr (EMODE == E_SLOTS) return args.order[off + m0 + r];
+    else return GROUPED ? off + m0 + r : (int64_t)(m0 + r);
+  };
+
+  if constexpr (kStaged) {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();  // every wave is done reading the ring
+    asm volatile("" ::: "memory");
+    char* E = smem + wave * (WTM * EROW);
+    auto pos = [](int rl, int c) -> int { return rl * EROW + ((kSwz ? (c ^ (rl & 7)) : c) << 4); };
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-#pragma unroll
-    for (int j = 0; j < TJ; ++j) {
-      int col;
-      if constexpr (BMODE == B_DUAL) col = nt * (BN / 2) + wn * (WTN / 2) + j * 32 + lr;
-      else col = nt * BN + wn * WTN + j * 32 + lr;
-      if (col >= args.N) continue;
+    for (int i = 0; i < TM; ++i) {
+      float ps[16];
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int r = wm * WTM + i * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
-        if (r >= rows_valid) continue;
+        ps[v] = 1.f;
         if constexpr (EMODE == E_SLOTS) {
-          const int q = args.order[off + m0 + r];
-          Elem<OutT>::store((OutT*)(args.out + (int64_t)q * args.ldo) + col, args.probs[q] * acc[i][j][v]);
-        } else {
-          const int64_t orow = GROUPED ? off + m0 + r : (int64_t)(m0 + r);
-          float val;
-          if constexpr (EMODE == E_SITU)
-            val = situ_hidden(acc[i][j][v], acc[i][j + TN / 2][v], args.beta1, args.beta2);
-          else val = acc[i][j][v];
-          Elem<OutT>::store((OutT*)(args.out + orow * args.ldo) + col, val);
+          const int r = wm * WTM + i * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
+          ps[v] = r < rows_valid ? args.probs[args.order[off + m0 + r]] : 0.f;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int cb = (j * 32 + lr) * OES;  // byte column inside the staged row
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int rl = i * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
+          float val = value(i, j, v);
+          if constexpr (EMODE == E_SLOTS) val *= ps[v];
+          Elem<OutT>::store((OutT*)(E + pos(rl, cb >> 4) + (cb & 15)), val);
+        }
+      }
+    }
+    const bool aligned = (((uintptr_t)args.out | (uintptr_t)args.ldo) & 15) == 0;
+    constexpr int EPC = 16 / OES;  // elements per chunk
+    for (int id = lane; id < WTM * CPR; id += 64) {
+      const int rl = id / CPR, c = id % CPR;
+      const int r = wm * WTM + rl;
+      const int col = col0 + c * EPC;
+      if (r >= rows_valid || col >= args.N) continue;
+      const char* src = E + pos(rl, c);
+      OutT* dst = (OutT*)(args.out + out_row(r) * args.ldo) + col;
+      if (aligned && col + EPC <= args.N) {
+        *(u32x4*)dst = *(const u32x4*)src;
+      } else {
+        for (int q = 0; q < EPC && col + q < args.N; ++q) dst[q] = ((const OutT*)src)[q];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int col = col0 + j * 32 + lr;
+        if (col >= args.N) continue;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = wm * WTM + i * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
+          if (r >= rows_valid) continue;
+          float val = value(i, j, v);
+          if constexpr (EMODE == E_SLOTS) val *= args.probs[args.order[off + m0 + r]];
+          Elem<OutT>::store((OutT*)(args.out + out_row(r) * args.ldo) + col, val);
         }
       }
     }

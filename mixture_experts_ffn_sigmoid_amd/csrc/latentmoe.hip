@@ -46,11 +46,11 @@ struct Plan {
 };
 
 // Row-tile height of the grouped expert GEMMs from the mean rows per expert:
-// 64 for a handful (weight streaming), 256 from ~100 rows on (one tile holds a
-// whole expert's rows, so its weights are read once), 128 in between.
+// 64 for a handful (weight streaming), 192 from ~100 rows on (one tile usually
+// holds a whole expert's rows, so its weights are read once), 128 in between.
 int routed_tile_m(int64_t pairs, int R) {
   const int64_t mean = pairs / R;
-  return mean < 48 ? 64 : mean < 96 ? 128 : 256;
+  return mean < 48 ? 64 : mean < 96 ? 128 : 192;
 }
 
 lmoe_status check_dims(const lmoe_dims* dm, Plan* p) {
@@ -176,37 +176,51 @@ size_t carve_forward(const Plan& p, char* b, ForwardWs* w) {
 
 // ------------------------------------------------------------ GEMM launches
 template <typename TA, typename TB, typename OutT, int BM, int BN, int WGM, int WGN, int AM, int BMD,
-          int EM>
+          int EM, int SA, int SB>
 lmoe_status launch_gemm(GemmArgs a, hipStream_t st) {
   const int64_t grid = (int64_t)a.m_tiles * a.n_tiles;
   if (grid <= 0) return LMOE_OK;
   if (grid > INT32_MAX) return fail(LMOE_ERR_UNSUPPORTED, "GEMM grid too large");
-  gemm_kernel<TA, TB, OutT, BM, BN, WGM, WGN, AM, BMD, EM><<<(unsigned)grid, 64 * WGM * WGN, 0, st>>>(a);
+  gemm_kernel<TA, TB, OutT, BM, BN, WGM, WGN, AM, BMD, EM, SA, SB>
+      <<<(unsigned)grid, 64 * WGM * WGN, 0, st>>>(a);
   LMOE_HIP(hipGetLastError());
   return LMOE_OK;
 }
 
-// Block tiles: S = 64 x 128 (x 256 for gate/up pairs) for few-row products
-// (weight streaming), M = 128 x 128 (4 waves), L = 256 x 256 (8 waves, wave tile 128 x 64).
-enum Tile { TILE_S = 0, TILE_M = 1, TILE_L = 2 };
-constexpr int tile_rows(Tile t) { return t == TILE_S ? 64 : t == TILE_M ? 128 : 256; }
+// Block tiles (rows x cols, waves, A / B LDS stages):
+//   S  64 x 128 (256 for gate/up pairs), 4 waves, 4/4: few-row dense products
+//   M 128 x 128, 4 waves, 4/4
+//   L 256 x 256, 8 waves, 4/4 (128 KB of LDS): large dense products
+//   W 192 x 256, 4 waves, 3/6 (132 KB): grouped expert products that stream
+//     their weights (B) from HBM -- the deeper B ring keeps ~80 KB of weights
+//     in flight per CU while the A rows (L2-resident) need only three stages
+//   V  64 x 256, 4 waves, 3/6: the same for a handful of rows per expert
+enum Tile { TILE_S = 0, TILE_M = 1, TILE_L = 2, TILE_W = 3, TILE_V = 4 };
 
 template <typename TA, typename TB, typename OutT, int AM, int BMD, int EM, int BM, int BN, int WGM,
-          int WGN>
+          int WGN, int SA, int SB>
 lmoe_status gemm_cfg(GemmArgs a, hipStream_t st) {
   constexpr int cols = BMD == B_DUAL ? BN / 2 : BN;
   a.n_tiles = (a.N + cols - 1) / cols;
   if (AM == A_DENSE) a.m_tiles = (a.M + BM - 1) / BM;
-  return launch_gemm<TA, TB, OutT, BM, BN, WGM, WGN, AM, BMD, EM>(a, st);
+  return launch_gemm<TA, TB, OutT, BM, BN, WGM, WGN, AM, BMD, EM, SA, SB>(a, st);
 }
 
 template <typename TA, typename TB, typename OutT, int AM, int BMD, int EM>
 lmoe_status gemm(GemmArgs a, Tile t, hipStream_t st) {
   constexpr bool dual = BMD == B_DUAL;
-  switch (t) {
-    case TILE_S: return gemm_cfg<TA, TB, OutT, AM, BMD, EM, 64, dual ? 256 : 128, 1, 4>(a, st);
-    case TILE_M: return gemm_cfg<TA, TB, OutT, AM, BMD, EM, 128, 128, 2, 2>(a, st);
-    default: return gemm_cfg<TA, TB, OutT, AM, BMD, EM, 256, 256, 2, 4>(a, st);
+  if constexpr (AM == A_DENSE) {
+    switch (t) {
+      case TILE_S: return gemm_cfg<TA, TB, OutT, AM, BMD, EM, 64, dual ? 256 : 128, 1, 4, 4, 4>(a, st);
+      case TILE_M: return gemm_cfg<TA, TB, OutT, AM, BMD, EM, 128, 128, 2, 2, 4, 4>(a, st);
+      default: return gemm_cfg<TA, TB, OutT, AM, BMD, EM, 256, 256, 2, 4, 4, 4>(a, st);
+    }
+  } else {
+    switch (t) {
+      case TILE_V: return gemm_cfg<TA, TB, OutT, AM, BMD, EM, 64, 256, 1, 4, 3, 6>(a, st);
+      case TILE_M: return gemm_cfg<TA, TB, OutT, AM, BMD, EM, 128, 128, 2, 2, 4, 4>(a, st);
+      default: return gemm_cfg<TA, TB, OutT, AM, BMD, EM, 192, 256, 2, 2, 3, 6>(a, st);
+    }
   }
 }
 
@@ -283,7 +297,7 @@ lmoe_status run_experts(const Plan& p, const lmoe_dims* dm, const void* a_src, i
                         Mark* mark = nullptr) {
   tile_list_kernel<<<1, 1024, 0, st>>>(counts, p.R, p.tile_m, tile_list, meta);
   LMOE_HIP(hipGetLastError());
-  const Tile tile = p.tile_m == 64 ? TILE_S : p.tile_m == 128 ? TILE_M : TILE_L;
+  const Tile tile = p.tile_m == 64 ? TILE_V : p.tile_m == 128 ? TILE_M : TILE_W;
   GemmArgs a = base_args(dm);
   a.N = p.fr;
   a.K = p.l;
