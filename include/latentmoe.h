@@ -156,11 +156,37 @@ lmoe_status latentmoe_experts(const lmoe_dims* dims, const void* padded, int64_t
  * The routed experts read their rows straight from z through the sorted
  * pair order (the padded tensor is not materialised), skip empty experts and
  * padding rows, and the scatter-add is deterministic (each pair writes its own
- * slot; slots are summed in slot order). */
+ * slot; slots are summed in slot order).  For N <= 2048 the shared experts'
+ * gate/up GEMM runs on a second, library-owned stream of the current device,
+ * forked from and joined back into `stream` with events (capturable as a
+ * fork/join in a HIP graph); all other work is on `stream`. */
 lmoe_status latentmoe_forward(const lmoe_dims* dims, const lmoe_weights* weights, const void* x,
                               void* y, int32_t* ids, float* probs, int32_t* counts,
                               int64_t* C_host, void* workspace, size_t workspace_bytes,
                               void* stream);
+
+/* Legacy router that the K3 sigmoid router replaced (compare page, forward
+ * hunk of latent_moe.py): ids = the k largest raw logits = W_r x (equal values:
+ * lower id first), probs = softmax over those k logits.  Arguments as for
+ * latentmoe_route, without a bias.  Asynchronous. */
+lmoe_status latentmoe_route_softmax(const lmoe_dims* dims, const void* x, const void* w_router,
+                                    int32_t* ids, float* probs, float* logits, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
+/* Switch/GShard auxiliary loss and router z-loss (chapter section on load
+ * balancing), unscaled (the layer multiplies them by its coefficients):
+ *   f_e = counts_e / sum_e counts_e,  P_e = mean over tokens of sigmoid(l_te),
+ *   out[0] = R * sum_e f_e P_e,      out[1] = mean over tokens of (logsumexp_e l_te)^2.
+ * logits [N, R] fp32 as written by latentmoe_route; counts [R] int32 (from
+ * latentmoe_dispatch or latentmoe_forward); out: 2 fp32 in device memory.
+ * N = 0 gives {0, 0}.  Deterministic (fixed summation order).  Workspace:
+ * latentmoe_router_losses_workspace_bytes(dims) bytes of device memory, owned
+ * by the caller.  Errors: INVALID_ARGUMENT for bad dims or a NULL pointer,
+ * WORKSPACE when it is missing or too small.  Asynchronous. */
+size_t latentmoe_router_losses_workspace_bytes(const lmoe_dims* dims);
+lmoe_status latentmoe_router_losses(const lmoe_dims* dims, const float* logits, const int32_t* counts,
+                                    float* out, void* workspace, size_t workspace_bytes,
+                                    void* stream);
 
 /* latentmoe_forward with timing marks, for profiling: `events` holds
  * LMOE_FORWARD_TIMING_EVENTS hipEvent_t handles (created by the caller);
@@ -171,7 +197,9 @@ lmoe_status latentmoe_forward(const lmoe_dims* dims, const lmoe_weights* weights
  *   3 dispatch (hist, scan, scatter)  7 slot sum + RMSNorm
  *   4 shared gate/up GEMM             8 merge GEMM [h_shared | RMSNorm(u)] -> y
  * The elapsed time between events[i-1] and events[i] is step i's device time.
- * C is not read back.  Otherwise identical to latentmoe_forward. */
+ * All steps run in order on `stream` (latentmoe_forward, for N <= 2048,
+ * runs step 4 on a second stream of its own next to steps 1-3 and 5-7).  C is
+ * not read back.  Otherwise identical to latentmoe_forward. */
 #define LMOE_FORWARD_TIMING_EVENTS 9
 lmoe_status latentmoe_forward_timed(const lmoe_dims* dims, const lmoe_weights* weights,
                                     const void* x, void* y, int32_t* ids, float* probs,

@@ -6,6 +6,7 @@ C ABI, include/latentmoe.h); this package is its thin ctypes binding.
 from ._lib import (  # noqa: F401
     ENTRY_DISPATCH, ENTRY_EXPERTS, ENTRY_FORWARD, ENTRY_ROUTE, EXPORTS, LIB_PATH, LMOE_BF16, LMOE_F32,
     Dims, LatentMoEError, Weights, dims_of, latentmoe_dispatch, latentmoe_experts, latentmoe_forward,
-    latentmoe_forward_timed, latentmoe_route, load, make_dims, weights_struct, workspace_bytes,
+    latentmoe_forward_timed, latentmoe_route, latentmoe_route_softmax, latentmoe_router_losses, load,
+    make_dims, router_losses_workspace_bytes, weights_struct, workspace_bytes,
     STEP_NAMES, TIMING_EVENTS,
 )

@@ -20,7 +20,8 @@ STATUS = {0: "OK", 1: "INVALID_ARGUMENT", 2: "UNSUPPORTED", 3: "CAPACITY", 4: "W
 EXPORTS = (
     "latentmoe_workspace_bytes", "latentmoe_status_string", "latentmoe_last_error",
     "latentmoe_route", "latentmoe_dispatch", "latentmoe_experts", "latentmoe_forward",
-    "latentmoe_forward_timed",
+    "latentmoe_forward_timed", "latentmoe_route_softmax", "latentmoe_router_losses_workspace_bytes",
+    "latentmoe_router_losses",
 )
 TIMING_EVENTS = 9
 STEP_NAMES = ("latent_gemm", "router", "dispatch", "shared_gateup", "routed_gateup", "routed_down",
@@ -72,8 +73,12 @@ def load() -> ctypes.CDLL:
                                       ctypes.POINTER(i64), vp, st, vp]
     lib.latentmoe_forward_timed.argtypes = [D, ctypes.POINTER(Weights), vp, vp, vp, vp, vp, vp, st, vp,
                                             ctypes.POINTER(vp), i32]
+    lib.latentmoe_route_softmax.argtypes = [D, vp, vp, vp, vp, vp, vp, st, vp]
+    lib.latentmoe_router_losses_workspace_bytes.argtypes = [D]
+    lib.latentmoe_router_losses_workspace_bytes.restype = st
+    lib.latentmoe_router_losses.argtypes = [D, vp, vp, vp, vp, st, vp]
     for fn in ("latentmoe_route", "latentmoe_dispatch", "latentmoe_experts", "latentmoe_forward",
-               "latentmoe_forward_timed"):
+               "latentmoe_forward_timed", "latentmoe_route_softmax", "latentmoe_router_losses"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -124,6 +129,25 @@ def latentmoe_route(dims, x, w_router, bias, ids, probs, logits=None, workspace=
     check(load().latentmoe_route(ctypes.byref(dims), ptr(x), ptr(w_router), ptr(bias), ptr(ids),
                                  ptr(probs), ptr(logits), ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
                                  stream_handle(stream)))
+
+
+def latentmoe_route_softmax(dims, x, w_router, ids, probs, logits=None, workspace=None, stream=None):
+    ws = workspace
+    check(load().latentmoe_route_softmax(ctypes.byref(dims), ptr(x), ptr(w_router), ptr(ids), ptr(probs),
+                                         ptr(logits), ptr(ws),
+                                         0 if ws is None else ws.numel() * ws.element_size(),
+                                         stream_handle(stream)))
+
+
+def router_losses_workspace_bytes(dims: Dims) -> int:
+    return int(load().latentmoe_router_losses_workspace_bytes(ctypes.byref(dims)))
+
+
+def latentmoe_router_losses(dims, logits, counts, out, workspace=None, stream=None):
+    ws = workspace
+    check(load().latentmoe_router_losses(ctypes.byref(dims), ptr(logits), ptr(counts), ptr(out), ptr(ws),
+                                         0 if ws is None else ws.numel() * ws.element_size(),
+                                         stream_handle(stream)))
 
 
 def latentmoe_dispatch(dims, ids, z, counts, offsets, order, padded=None, capacity=0,

@@ -5,6 +5,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "latentmoe.h"
 #include "gemm_kernel.h"
@@ -174,6 +175,23 @@ size_t carve_forward(const Plan& p, char* b, ForwardWs* w) {
   return c.off;
 }
 
+// Largest batch whose shared-expert GEMM runs on the second stream.
+constexpr int64_t kOverlapMaxTokens = 2048;
+
+// A second stream per device on which the shared-expert GEMM overlaps the
+// routed experts (default priority, non-blocking, created once per device).
+lmoe_status side_stream(hipStream_t* out) {
+  static std::mutex mu;
+  static hipStream_t streams[64] = {};
+  int dev = 0;
+  LMOE_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= 64) return fail(LMOE_ERR_UNSUPPORTED, "device index %d", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!streams[dev]) LMOE_HIP(hipStreamCreateWithFlags(&streams[dev], hipStreamNonBlocking));
+  *out = streams[dev];
+  return LMOE_OK;
+}
+
 // ------------------------------------------------------------ GEMM launches
 template <typename TA, typename TB, typename OutT, int BM, int BN, int WGM, int WGN, int AM, int BMD,
           int EM, int SA, int SB>
@@ -251,7 +269,8 @@ GemmArgs base_args(const lmoe_dims* dm) {
 // logits = x W_r^T (fp32), then the sigmoid / top-k / renormalisation kernel.
 template <typename T>
 lmoe_status run_route(const Plan& p, const lmoe_dims* dm, const void* x, const void* w_router,
-                      const float* bias, int32_t* ids, float* probs, float* logits, hipStream_t st) {
+                      const float* bias, int32_t* ids, float* probs, float* logits, hipStream_t st,
+                      bool softmax = false) {
   GemmArgs a = base_args(dm);
   a.M = (int)p.N;
   a.N = p.R;
@@ -265,8 +284,12 @@ lmoe_status run_route(const Plan& p, const lmoe_dims* dm, const void* x, const v
   a.ldo = (int64_t)p.R * 4;
   LMOE_TRY((gemm<T, T, float, A_DENSE, B_SINGLE, E_STORE>(a, dense_tile(p.N, p.R, false), st)));
   const unsigned blocks = (unsigned)((p.N + 3) / 4);
-  topk_route_kernel<<<blocks, 256, 4 * p.R * sizeof(float), st>>>(logits, bias, p.N, p.R, p.k, ids,
-                                                                  probs);
+  if (softmax)
+    topk_route_kernel<true><<<blocks, 256, 4 * p.R * sizeof(float), st>>>(logits, nullptr, p.N, p.R, p.k,
+                                                                          ids, probs);
+  else
+    topk_route_kernel<false><<<blocks, 256, 4 * p.R * sizeof(float), st>>>(logits, bias, p.N, p.R, p.k,
+                                                                           ids, probs);
   LMOE_HIP(hipGetLastError());
   return LMOE_OK;
 }
@@ -343,6 +366,25 @@ lmoe_status run_experts(const Plan& p, const lmoe_dims* dm, const void* a_src, i
   return gemm<TH, TW, TH, A_SORTED, B_SINGLE, E_SLOTS>(b, tile, st);
 }
 
+// Shared experts' gate/up GEMM with the SiTU epilogue -> hcat[:, :n_s f_s].
+template <typename T, typename TI>
+lmoe_status run_shared(const Plan& p, const lmoe_dims* dm, const lmoe_weights* W, const void* x,
+                       const ForwardWs& w, hipStream_t st) {
+  GemmArgs s = base_args(dm);
+  s.M = (int)p.N;
+  s.N = p.ns * p.fs;
+  s.K = p.d;
+  s.a = (const char*)x;
+  s.lda = (int64_t)p.d * p.es;
+  s.b0 = (const char*)W->sh_g;
+  s.b1 = (const char*)W->sh_u;
+  s.ldb = (int64_t)p.d * p.es;
+  s.nb_rows = p.ns * p.fs;
+  s.out = w.hcat;
+  s.ldo = p.ldh * p.es;
+  return gemm<T, T, TI, A_DENSE, B_DUAL, E_SITU>(s, dense_tile(p.N, s.N, true), st);
+}
+
 // T: storage type (x, weights, y); TI: intermediate type of z, h and the
 // normalised u (fp32 with fp32 storage, fp16 with bf16 storage).
 template <typename T, typename TI>
@@ -356,6 +398,29 @@ lmoe_status run_forward(const Plan& p, const lmoe_dims* dm, const lmoe_weights* 
     return LMOE_OK;
   };
   LMOE_TRY(mark());
+  // The shared experts depend on x only.  For small batches (whose GEMMs
+  // leave most CUs idle) and without timing marks they run on a second
+  // stream, next to steps 1-3 and the routed experts; the merge GEMM waits
+  // for both.  Large batches fill the chip with each GEMM alone, and their
+  // 128-132 KB LDS tiles cannot share a CU, so there they run in order.
+  hipStream_t side = st;
+  struct Events {
+    hipEvent_t fork = nullptr, join = nullptr;
+    ~Events() {
+      if (fork) (void)hipEventDestroy(fork);
+      if (join) (void)hipEventDestroy(join);
+    }
+  } evs;
+  const bool overlap = ev == nullptr && p.ns > 0 && p.N <= kOverlapMaxTokens;
+  if (overlap) {
+    LMOE_TRY(side_stream(&side));
+    LMOE_HIP(hipEventCreateWithFlags(&evs.fork, hipEventDisableTiming));
+    LMOE_HIP(hipEventCreateWithFlags(&evs.join, hipEventDisableTiming));
+    LMOE_HIP(hipEventRecord(evs.fork, st));
+    LMOE_HIP(hipStreamWaitEvent(side, evs.fork, 0));
+    LMOE_TRY((run_shared<T, TI>(p, dm, W, x, w, side)));
+    LMOE_HIP(hipEventRecord(evs.join, side));
+  }
   // 1. z = W_down x
   GemmArgs a = base_args(dm);
   a.M = (int)p.N;
@@ -376,22 +441,8 @@ lmoe_status run_forward(const Plan& p, const lmoe_dims* dm, const lmoe_weights* 
   // 3a. dispatch bookkeeping
   LMOE_TRY(run_dispatch(p, ids, w.chunk_hist, w.chunk_bad, counts, w.offsets, w.order, w.meta, st));
   LMOE_TRY(mark());
-  // 4. shared experts gate/up -> h_shared = hcat[:, :n_s f_s]
-  if (p.ns > 0) {
-    GemmArgs s = base_args(dm);
-    s.M = (int)p.N;
-    s.N = p.ns * p.fs;
-    s.K = p.d;
-    s.a = (const char*)x;
-    s.lda = (int64_t)p.d * p.es;
-    s.b0 = (const char*)W->sh_g;
-    s.b1 = (const char*)W->sh_u;
-    s.ldb = (int64_t)p.d * p.es;
-    s.nb_rows = p.ns * p.fs;
-    s.out = w.hcat;
-    s.ldo = p.ldh * p.es;
-    LMOE_TRY((gemm<T, T, TI, A_DENSE, B_DUAL, E_SITU>(s, dense_tile(p.N, s.N, true), st)));
-  }
+  // 4. shared experts gate/up -> h_shared = hcat[:, :n_s f_s] (in order when timed)
+  if (!overlap && p.ns > 0) LMOE_TRY((run_shared<T, TI>(p, dm, W, x, w, st)));
   LMOE_TRY(mark());
   // 3b. routed experts straight from z -> slots
   LMOE_TRY((run_experts<TI, T, TI, A_GATHER>(p, dm, w.z, 0, counts, w.offsets, w.order, probs, W->w_g,
@@ -404,6 +455,7 @@ lmoe_status run_forward(const Plan& p, const lmoe_dims* dm, const lmoe_weights* 
       (TI*)(w.hcat + (int64_t)p.ns * p.fs * p.es), p.ldh);
   LMOE_HIP(hipGetLastError());
   LMOE_TRY(mark());
+  if (overlap) LMOE_HIP(hipStreamWaitEvent(st, evs.join, 0));
   // 5b. y = [h_shared | RMSNorm(u)] [sh_o_0 | ... | sh_o_{n_s-1} | W_up]^T
   GemmArgs f = base_args(dm);
   f.M = (int)p.N;
@@ -490,6 +542,56 @@ lmoe_status latentmoe_route(const lmoe_dims* dims, const void* x, const void* w_
   hipStream_t st = (hipStream_t)stream;
   if (p.bf16) return run_route<bf16_t>(p, dims, x, w_router, bias, ids, probs, logits, st);
   return run_route<float>(p, dims, x, w_router, bias, ids, probs, logits, st);
+}
+
+lmoe_status latentmoe_route_softmax(const lmoe_dims* dims, const void* x, const void* w_router,
+                                    int32_t* ids, float* probs, float* logits, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+  Plan p;
+  LMOE_TRY(check_dims(dims, &p));
+  if (p.N == 0) return LMOE_OK;
+  if (!x || !w_router || !ids || !probs) return fail(LMOE_ERR_INVALID_ARGUMENT, "NULL tensor");
+  RouteWs w{};
+  if (!logits) {
+    const size_t need = carve_route(p, nullptr, &w);
+    if (!workspace || workspace_bytes < need)
+      return fail(LMOE_ERR_WORKSPACE, "route needs %zu workspace bytes", need);
+    carve_route(p, (char*)workspace, &w);
+    logits = w.logits;
+  }
+  hipStream_t st = (hipStream_t)stream;
+  if (p.bf16) return run_route<bf16_t>(p, dims, x, w_router, nullptr, ids, probs, logits, st, true);
+  return run_route<float>(p, dims, x, w_router, nullptr, ids, probs, logits, st, true);
+}
+
+size_t latentmoe_router_losses_workspace_bytes(const lmoe_dims* dims) {
+  Plan p;
+  if (check_dims(dims, &p) != LMOE_OK) return 0;
+  const int64_t nblk = (p.N + kLossTokens - 1) / kLossTokens;
+  return (size_t)(nblk * p.R + nblk) * sizeof(float) + 256;
+}
+
+lmoe_status latentmoe_router_losses(const lmoe_dims* dims, const float* logits, const int32_t* counts,
+                                    float* out, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  Plan p;
+  LMOE_TRY(check_dims(dims, &p));
+  if (!out || !counts || (p.N > 0 && !logits)) return fail(LMOE_ERR_INVALID_ARGUMENT, "NULL tensor");
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t nblk = (p.N + kLossTokens - 1) / kLossTokens;
+  const size_t need = latentmoe_router_losses_workspace_bytes(dims);
+  if (!workspace || workspace_bytes < need)
+    return fail(LMOE_ERR_WORKSPACE, "router losses need %zu workspace bytes", need);
+  if (nblk > INT32_MAX) return fail(LMOE_ERR_UNSUPPORTED, "too many tokens");
+  float* colsum = (float*)workspace;
+  float* lse2 = colsum + nblk * p.R;
+  if (nblk > 0) {
+    router_stats_kernel<<<(unsigned)nblk, 256, 0, st>>>(logits, p.N, p.R, colsum, lse2);
+    LMOE_HIP(hipGetLastError());
+  }
+  router_losses_kernel<<<1, 1024, 0, st>>>(colsum, lse2, (int)nblk, p.N, p.R, counts, out);
+  LMOE_HIP(hipGetLastError());
+  return LMOE_OK;
 }
 
 lmoe_status latentmoe_dispatch(const lmoe_dims* dims, const int32_t* ids, const void* z,

@@ -15,6 +15,9 @@ constexpr int kDispatchChunk = 1024;  // pairs per histogram / scatter chunk
 // wave-wide arg-max of v = s + b (larger v first, equal v -> lower id), then
 // p_i = s_i / max(sum_T s, 1e-9).  v lives in LDS (R floats per wave), each
 // lane keeps the best of its own experts so that a round rescans one lane.
+// kSoftmax selects the legacy router instead: v = the raw logits, and the k
+// winners are weighted by a softmax over their logits.
+template <bool kSoftmax>
 __global__ __launch_bounds__(256) void topk_route_kernel(const float* __restrict__ logits,
                                                          const float* __restrict__ bias, int64_t N,
                                                          int R, int k, int32_t* __restrict__ ids,
@@ -29,8 +32,7 @@ __global__ __launch_bounds__(256) void topk_route_kernel(const float* __restrict
   float best = -INFINITY;
   int best_id = 0x7fffffff;
   for (int e = lane; e < R; e += 64) {
-    const float s = sigmoidf_(lrow[e]);
-    const float ve = s + (bias ? bias[e] : 0.f);
+    const float ve = kSoftmax ? lrow[e] : sigmoidf_(lrow[e]) + (bias ? bias[e] : 0.f);
     v[e] = ve;
     if (ve > best) {  // ascending e per lane: strict > keeps the lower id on ties
       best = ve;
@@ -39,7 +41,7 @@ __global__ __launch_bounds__(256) void topk_route_kernel(const float* __restrict
   }
 
   int my_id = 0;  // lane j keeps the j-th winner
-  float ssum = 0.f;
+  float ssum = 0.f, lmax = 0.f;
   for (int j = 0; j < k; ++j) {
     float bv = best;
     int bi = best_id;
@@ -54,7 +56,12 @@ __global__ __launch_bounds__(256) void topk_route_kernel(const float* __restrict
     }
     if (bi >= R) bi = 0;  // only reachable with NaN scores; keeps every index in range
     if (lane == j) my_id = bi;
-    ssum += sigmoidf_(lrow[bi]);
+    if constexpr (kSoftmax) {
+      if (j == 0) lmax = lrow[bi];  // the first winner holds the largest logit
+      ssum += expf(lrow[bi] - lmax);
+    } else {
+      ssum += sigmoidf_(lrow[bi]);
+    }
     if ((bi & 63) == lane) {  // owner lane removes the winner and rescans its experts
       v[bi] = -INFINITY;
       best = -INFINITY;
@@ -70,7 +77,86 @@ __global__ __launch_bounds__(256) void topk_route_kernel(const float* __restrict
   }
   if (lane < k) {
     ids[n * k + lane] = my_id;
-    probs[n * k + lane] = sigmoidf_(lrow[my_id]) / fmaxf(ssum, 1e-9f);
+    if constexpr (kSoftmax) probs[n * k + lane] = expf(lrow[my_id] - lmax) / ssum;
+    else probs[n * k + lane] = sigmoidf_(lrow[my_id]) / fmaxf(ssum, 1e-9f);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Router statistics for the Switch/GShard auxiliary loss and the router
+// z-loss.  Pass 1, one workgroup per block of kLossTokens tokens:
+//   colsum[blk, e] = sum over the block's tokens of sigmoid(l_te)
+//   lse2[blk]      = sum over the block's tokens of (logsumexp_e l_te)^2
+// (fixed summation order: deterministic).
+constexpr int kLossTokens = 64;
+__global__ __launch_bounds__(256) void router_stats_kernel(const float* __restrict__ logits, int64_t N,
+                                                           int R, float* __restrict__ colsum,
+                                                           float* __restrict__ lse2) {
+  __shared__ float part[4];
+  const int64_t t0 = (int64_t)blockIdx.x * kLossTokens;
+  const int64_t t1 = min(t0 + kLossTokens, N);
+  for (int e = threadIdx.x; e < R; e += 256) {
+    float acc = 0.f;
+    for (int64_t t = t0; t < t1; ++t) acc += sigmoidf_(logits[t * R + e]);
+    colsum[(int64_t)blockIdx.x * R + e] = acc;
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float wsum = 0.f;
+  for (int64_t t = t0 + wave; t < t1; t += 4) {
+    const float* l = logits + t * R;
+    float m = -INFINITY;
+    for (int e = lane; e < R; e += 64) m = fmaxf(m, l[e]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    float se = 0.f;
+    for (int e = lane; e < R; e += 64) se += expf(l[e] - m);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) se += __shfl_xor(se, off);
+    const float lse = m + logf(se);
+    wsum += lse * lse;  // wave-uniform
+  }
+  if (lane == 0) part[wave] = wsum;
+  __syncthreads();
+  if (threadIdx.x == 0) lse2[blockIdx.x] = (part[0] + part[1]) + (part[2] + part[3]);
+}
+
+// Pass 2 (one workgroup; nblk may be 0): f_e = counts_e / max(sum counts, 1), P_e = colsum_e / N,
+// out[0] = R * sum_e f_e P_e, out[1] = sum lse^2 / N.
+__global__ __launch_bounds__(1024) void router_losses_kernel(const float* __restrict__ colsum,
+                                                             const float* __restrict__ lse2, int nblk,
+                                                             int64_t N, int R,
+                                                             const int32_t* __restrict__ counts,
+                                                             float* __restrict__ out) {
+  __shared__ float red_a[1024], red_z[1024];
+  __shared__ long long red_c[1024];
+  const int t = threadIdx.x;
+  float a = 0.f;
+  long long c = 0;
+  for (int e = t; e < R; e += 1024) {
+    float pe = 0.f;
+    for (int b = 0; b < nblk; ++b) pe += colsum[(int64_t)b * R + e];
+    a += (float)counts[e] * pe;
+    c += counts[e];
+  }
+  float z = 0.f;
+  for (int b = t; b < nblk; b += 1024) z += lse2[b];
+  red_a[t] = a;
+  red_z[t] = z;
+  red_c[t] = c;
+  __syncthreads();
+  for (int s = 512; s >= 1; s >>= 1) {
+    if (t < s) {
+      red_a[t] += red_a[t + s];
+      red_z[t] += red_z[t + s];
+      red_c[t] += red_c[t + s];
+    }
+    __syncthreads();
+  }
+  if (t == 0) {  // an empty batch has both losses 0
+    const double tot = red_c[0] > 0 ? (double)red_c[0] : 1.0;
+    const double n = N > 0 ? (double)N : 1.0;
+    out[0] = (float)((double)R * (double)red_a[0] / (tot * n));
+    out[1] = (float)((double)red_z[0] / n);
   }
 }
 

@@ -84,3 +84,15 @@ def test_status_strings():
     lib = M.load()
     for s in range(6):
         assert lib.latentmoe_status_string(s)
+
+
+def test_router_entry_errors():
+    lib = M.load()
+    dims = M.dims_of(S.CONFIGS["toy_n128"])
+    assert M.router_losses_workspace_bytes(dims) >= 4 * dims.n_routed * (dims.n_tokens // 64)
+    # NULL counts / out, then a too-small workspace: rejected before any HIP call
+    assert lib.latentmoe_router_losses(ctypes.byref(dims), 16, None, 16, 16, 1 << 30, None) == 1
+    assert lib.latentmoe_router_losses(ctypes.byref(dims), 16, 16, None, 16, 1 << 30, None) == 1
+    assert lib.latentmoe_router_losses(ctypes.byref(dims), 16, 16, 16, 16, 8, None) == 4
+    assert lib.latentmoe_route_softmax(ctypes.byref(dims), 16, 16, None, 16, 16, 16, 1 << 30, None) == 1
+    assert lib.latentmoe_route_softmax(ctypes.byref(dims), 16, 16, 16, 16, None, 16, 8, None) == 4

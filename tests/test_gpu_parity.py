@@ -243,3 +243,100 @@ def test_forward_parity_k3_prefill():
     cfg = S.CONFIGS["k3full_n8192"]
     r = _forward_parity(cfg, host=None, sample=[0, 4097, 8191])
     assert r["C"] >= 131072 // 896
+
+
+def _softmax_margin(logits: np.ndarray, k: int) -> np.ndarray:
+    R = logits.shape[1]
+    if k == R:
+        return np.full(logits.shape[0], np.inf)
+    part = -np.sort(-logits, axis=1)
+    return part[:, k - 1] - part[:, k]
+
+
+@pytest.mark.parametrize("name", ["toy_n128", "b05skew_n4096", "k3full_n64"])
+def test_route_softmax_entry(name):
+    """Legacy softmax-top-k router against the oracle's: exact sets where the
+    k-th / (k+1)-th logit margin exceeds the near-tie margin, a valid top-k
+    otherwise, and softmax weights over the chosen logits."""
+    cfg = S.CONFIGS[name]
+    _say(f"[route_softmax] {name}")
+    dev = G.device_layer_inputs(cfg)
+    N, R, k = cfg.n_tokens, cfg.n_routed, cfg.top_k
+    dims = M.dims_of(cfg)
+    ids = torch.empty((N, k), dtype=torch.int32, device="cuda")
+    probs = torch.empty((N, k), dtype=torch.float32, device="cuda")
+    logits = torch.empty((N, R), dtype=torch.float32, device="cuda")
+    M.latentmoe_route_softmax(dims, dev["x"], dev["w_router"], ids, probs, logits)
+    torch.cuda.synchronize()
+    W = O.config_weights(cfg, cache_experts=0)
+    lo = O.config_x(cfg) @ W.w_router.T
+    o_ids, _ = O.route_softmax_topk(lo, k)
+    g_ids = ids.cpu().numpy().astype(np.int64)
+    assert ((g_ids >= 0) & (g_ids < R)).all()
+    near = _softmax_margin(lo, k) <= G.MARGIN
+    assert (np.sort(g_ids[~near], 1) == np.sort(o_ids[~near], 1)).all()
+    for n in np.nonzero(near)[0]:
+        vs = np.sort(lo[n])[::-1]
+        chosen = np.zeros(R, bool)
+        chosen[g_ids[n]] = True
+        assert chosen.sum() == k
+        assert (lo[n][chosen] >= vs[k - 1] - G.MARGIN).all()
+    sel = np.take_along_axis(lo, g_ids, axis=1)
+    e = np.exp(sel - sel.max(1, keepdims=True))
+    np.testing.assert_allclose(probs.cpu().numpy(), e / e.sum(1, keepdims=True), rtol=0, atol=2e-5)
+    # winners come out in descending logit order
+    assert (np.diff(sel[~near], axis=1) <= 1e-6).all()
+    # the workspace variant gives the same routes
+    ws = torch.empty(M.workspace_bytes(dims, M.ENTRY_ROUTE), dtype=torch.uint8, device="cuda")
+    ids2, probs2 = torch.empty_like(ids), torch.empty_like(probs)
+    M.latentmoe_route_softmax(dims, dev["x"], dev["w_router"], ids2, probs2, None, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids2) and torch.equal(probs, probs2)
+
+
+@pytest.mark.parametrize("name,n_tokens", [("toy_n128", None), ("toy_n128", 77), ("b05skew_n4096", None),
+                                           ("b05_n4096", 1000), ("k3full_n64", None)])
+def test_router_losses_entry(name, n_tokens):
+    """Auxiliary and z-loss over the forward's own logits and counts, against
+    the oracle's (its logits in fp64, the GPU's routes, checked valid)."""
+    cfg = S.CONFIGS[name]
+    if n_tokens is not None:
+        cfg = cfg.with_(name=f"{name}_n{n_tokens}", n_tokens=n_tokens)
+    _say(f"[router_losses] {cfg.name}")
+    dev = G.device_layer_inputs(cfg)
+    N, R, k = cfg.n_tokens, cfg.n_routed, cfg.top_k
+    dims = M.dims_of(cfg)
+    ids = torch.empty((N, k), dtype=torch.int32, device="cuda")
+    probs = torch.empty((N, k), dtype=torch.float32, device="cuda")
+    logits = torch.empty((N, R), dtype=torch.float32, device="cuda")
+    M.latentmoe_route(dims, dev["x"], dev["w_router"], dev["bias"], ids, probs, logits)
+    counts = torch.bincount(ids.reshape(-1).long(), minlength=R).to(torch.int32)
+    out = torch.empty(2, dtype=torch.float32, device="cuda")
+    ws = torch.empty(M.router_losses_workspace_bytes(dims), dtype=torch.uint8, device="cuda")
+    M.latentmoe_router_losses(dims, logits, counts, out, ws)
+    torch.cuda.synchronize()
+    W = O.config_weights(cfg, cache_experts=0)
+    routes = O.route(O.config_x(cfg), W.w_router, W.bias, k)
+    g_ids = ids.cpu().numpy()
+    G.check_routes(g_ids, routes, W.bias, k)
+    aux, zl = O.balancing_losses(routes.logits, g_ids, R)
+    got = out.cpu().numpy().astype(np.float64)
+    _say(f"   aux {got[0]:.6f} vs {aux:.6f}  z {got[1]:.6f} vs {zl:.6f}")
+    assert abs(got[0] - aux) <= 1e-4 * abs(aux)
+    assert abs(got[1] - zl) <= 1e-4 * abs(zl) + 1e-6
+    # deterministic
+    out2 = torch.empty_like(out)
+    M.latentmoe_router_losses(dims, logits, counts, out2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+
+
+def test_router_losses_empty_batch():
+    cfg = S.CONFIGS["toy_n128"].with_(n_tokens=0)
+    dims = M.dims_of(cfg)
+    counts = torch.zeros(cfg.n_routed, dtype=torch.int32, device="cuda")
+    out = torch.full((2,), 7.0, device="cuda")
+    ws = torch.empty(max(M.router_losses_workspace_bytes(dims), 1), dtype=torch.uint8, device="cuda")
+    M.latentmoe_router_losses(dims, None, counts, out, ws)
+    torch.cuda.synchronize()
+    assert out.cpu().tolist() == [0.0, 0.0]
