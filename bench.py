@@ -79,6 +79,8 @@ def cpu_baseline(cfg, n_sample: int):
 
 KERNEL_SOURCES = ("mixture_experts_ffn_sigmoid_amd/csrc/gemm_kernel.h",
                   "mixture_experts_ffn_sigmoid_amd/csrc/lmoe_common.h",
+                  "mixture_experts_ffn_sigmoid_amd/csrc/route_kernels.h",
+                  "mixture_experts_ffn_sigmoid_amd/csrc/merge_kernels.h",
                   "mixture_experts_ffn_sigmoid_amd/csrc/latentmoe.hip")
 
 

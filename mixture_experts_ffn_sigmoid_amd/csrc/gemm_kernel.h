@@ -4,9 +4,11 @@
 //                                             B stored like an nn.Linear weight)
 //
 // Workgroup: 4 or 8 wave64s in a WGM x WGN grid; block tile BM x BN;
-// K advances 64 bytes per step (32 bf16/fp16 or 16 fp32).  Operand tiles go
-// straight from global memory into LDS with gfx950's LDS-DMA loads
-// (global_load_lds_dwordx4) through a 4-stage ring, one barrier per K step.
+// K advances KB = 64 or 128 bytes of every tile row per step (KB = 128: each
+// row's step is one whole 128-byte cache line, so every L2 request is a full
+// line).  Operand tiles go straight from global memory into LDS with
+// gfx950's LDS-DMA loads (global_load_lds_dwordx4) through rings of SA (A)
+// and SB (B) stages, one barrier per K step.
 //
 // Matrix cores: v_mfma_f32_32x32x16_bf16 / _f16 (gfx950) for 2-byte operands,
 // v_mfma_f32_32x32x2f32 for fp32.  With an fp16 A operand and bf16 weights the
@@ -42,7 +44,7 @@ struct IntC {
 };
 
 constexpr int kMaxSeg = 17;
-constexpr int kKStepBytes = 64;  // bytes of every tile row consumed per K step
+constexpr int kSegUnit = 64;  // B_KSEG segment boundaries are given in 64-byte units of K
 
 struct GemmArgs {
   int M;        // dense: rows of A / out
@@ -70,7 +72,7 @@ struct GemmArgs {
   int nseg;
   const char* seg_base[kMaxSeg];
   int64_t seg_ld[kMaxSeg];
-  int seg_kt0[kMaxSeg + 1];  // first K step (of kKStepBytes per row) of each segment
+  int seg_kt0[kMaxSeg + 1];  // first K byte of each segment / kSegUnit (a multiple of KB / kSegUnit)
   // out
   char* out;
   int64_t ldo;  // bytes (E_SLOTS: fp32 elements per slot row * 4)
@@ -84,10 +86,44 @@ constexpr int vmcnt_imm(int n) { return (n & 0xF) | (((n >> 4) & 3) << 14) | (0x
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
+// s_waitcnt immediate that also waits for every LDS operation of this wave (lgkmcnt 0).
+constexpr int vmcnt_lgkm0_imm(int n) { return (n & 0xF) | (((n >> 4) & 3) << 14) | (0x7 << 4); }
+
+// Compile-time loop: f(IntC<0>{}), ..., f(IntC<N-1>{}).
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void sfor(F&& f) {
+  if constexpr (I < N) {
+    f(IntC<I>{});
+    sfor<N, I + 1>(f);
+  }
+}
+
+// Instruction order of one scheduling region (scheduling-group barriers;
+// masks 0x008 MFMA, 0x100 LDS read, 0x020 VMEM read = LDS-DMA): NM MFMAs,
+// with the region's NR fragment reads and then its ND DMA instructions (in
+// that program order) spread evenly over them; memory operation m follows
+// MFMA ceil((m + 1) * NM / (NR + ND)) - 1.
+template <int NM, int NR, int ND, int Q = 0>
+__device__ __forceinline__ void sched_interleave() {
+  constexpr int NMEM = NR + ND;
+  if constexpr (NM == 0) {
+    if constexpr (NR > 0) __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+    if constexpr (ND > 0) __builtin_amdgcn_sched_group_barrier(0x020, ND, 0);
+  } else if constexpr (Q < NM) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    constexpr int lo = (Q * NMEM + NM - 1) / NM, hi = ((Q + 1) * NMEM + NM - 1) / NM;
+    constexpr int r_lo = lo < NR ? lo : NR, r_hi = hi < NR ? hi : NR;
+    if constexpr (r_hi > r_lo) __builtin_amdgcn_sched_group_barrier(0x100, r_hi - r_lo, 0);
+    constexpr int d = (hi - lo) - (r_hi - r_lo);  // DMA instructions among them
+    if constexpr (d > 0) __builtin_amdgcn_sched_group_barrier(0x020, d, 0);
+    sched_interleave<NM, NR, ND, Q + 1>();
+  }
+}
+
 constexpr int gcd_(int a, int b) { return b == 0 ? a : gcd_(b, a % b); }
 
 template <typename TA, typename TB, typename OutT, int BM, int BN, int WGM, int WGN, int AMODE,
-          int BMODE, int EMODE, int SA, int SB>
+          int BMODE, int EMODE, int SA, int SB, int KB>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs args) {
   static_assert(sizeof(TA) == sizeof(TB), "operand element sizes must match");
   constexpr bool kHalf = sizeof(TA) == 2;  // 16-bit operands
@@ -97,10 +133,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int TM = WTM / 32, TN = WTN / 32;
   constexpr bool GROUPED = AMODE != A_DENSE;
-  // K step: 64 bytes of every tile row.  One LDS-DMA wave instruction moves
-  // 64 lanes x 16 bytes = 16 tile rows.
-  constexpr int ROWB = kKStepBytes;
-  constexpr int A_INST = BM / 16, B_INST = BN / 16;
+  // K step: KB bytes of every tile row = NCH 16-byte chunks.  One LDS-DMA
+  // wave instruction moves 64 lanes x 16 bytes = RPI tile rows.
+  static_assert(KB == 64 || KB == 128, "K step of 64 or 128 bytes");
+  constexpr int ROWB = KB;
+  constexpr int NCH = KB / 16, RPI = 64 / NCH;
+  constexpr int RSH = 16 / NCH;  // consecutive rows sharing one chunk swizzle
+  constexpr int A_INST = BM / RPI, B_INST = BN / RPI;
   constexpr int A_W = A_INST / NW, B_W = B_INST / NW;  // DMA instructions per wave per K step
   // Two LDS rings: SA stages of A rows and SB >= SA stages of B rows (the
   // B ring is deeper where B is the HBM-streamed weight matrix).
@@ -110,7 +149,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
   static_assert(NW == 4 || NW == 8, "4 or 8 waves per workgroup");
   static_assert(TM >= 1 && TN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "32x32 sub-tiles");
   static_assert(BMODE != B_DUAL || TN % 2 == 0, "dual tile needs gate and up sub-tiles");
-  static_assert(A_INST % NW == 0 && B_INST % NW == 0 && BM % 16 == 0 && BN % 16 == 0, "DMA split");
+  static_assert(A_INST % NW == 0 && B_INST % NW == 0 && BM % RPI == 0 && BN % RPI == 0, "DMA split");
   static_assert(SA >= 2 && SB >= SA && UNROLL <= 8, "ring shape");
   __shared__ __attribute__((aligned(1024))) char smem[RING];
   char* const ringA = smem;
@@ -155,14 +194,18 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
     rows_valid = min(BM, args.M - m0);
   }
 
-  // ---- DMA plan.  For each operand, wave `wave` moves 16-row blocks
-  // wave*X_W + ii of the tile.  Lane l carries tile row block*16 + l/4 and
-  // lands at LDS slot l%4 of that row; it fetches global 16-byte chunk
-  // (l%4) ^ ((l>>4)&3), i.e. rows are XOR-swizzled so that the fragment
-  // reads of 16 consecutive rows hit 16 distinct bank groups.  Rows past the
-  // valid range are clamped to the last valid row: every DMA instruction is
-  // always issued, which keeps the vmcnt accounting exact.
-  const uint32_t lane_chunk = (uint32_t)(((lane & 3) ^ ((lane >> 4) & 3)) * 16);
+  // ---- DMA plan.  For each operand, wave `wave` moves RPI-row blocks
+  // wave*X_W + ii of the tile.  Lane l carries tile row r = block*RPI + l/NCH
+  // and lands at LDS slot l%NCH of that row; it fetches global 16-byte chunk
+  // (l%NCH) ^ sw(r), sw(r) = (r / RSH) % NCH: rows are XOR-swizzled so that
+  // the fragment reads of 16 consecutive rows hit 16 distinct 16-byte bank
+  // groups.  Rows past the valid range are clamped to the last valid row:
+  // every DMA instruction is always issued, which keeps the vmcnt accounting
+  // exact.
+  auto lane_chunk = [&](int block) -> uint32_t {
+    const int r = block * RPI + lane / NCH;
+    return (uint32_t)(((lane % NCH) ^ ((r / RSH) % NCH)) * 16);
+  };
   constexpr int H = BMODE == B_DUAL ? BN / 2 : BN;  // rows of one B matrix per tile
   const int b_rows_here = min(H, args.nb_rows - nt * H);
   const char* a_base;
@@ -173,49 +216,54 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
   else a_base = args.a + (int64_t)m0 * args.lda;
 #pragma unroll
   for (int ii = 0; ii < A_W; ++ii) {
-    const int rr = min((wave * A_W + ii) * 16 + (lane >> 2), rows_valid - 1);
+    const int rr = min((wave * A_W + ii) * RPI + lane / NCH, rows_valid - 1);
     int64_t row = rr;
     if constexpr (AMODE == A_GATHER) row = args.order[off + m0 + rr] / args.top_k;
-    a_off[ii] = (uint32_t)(row * args.lda) + lane_chunk;
+    a_off[ii] = (uint32_t)(row * args.lda) + lane_chunk(wave * A_W + ii);
   }
   const char* b_base[B_W];  // workgroup-uniform
   uint32_t b_off[B_W];      // per lane, K step 0
+  uint32_t b_chunk[B_W];    // per lane swizzled chunk offset
   int b_brow[B_W];          // clamped row inside the tile's slice of its matrix
 #pragma unroll
   for (int ii = 0; ii < B_W; ++ii) {
-    const int r = (wave * B_W + ii) * 16 + (lane >> 2);
+    const int r = (wave * B_W + ii) * RPI + lane / NCH;
     const bool up = BMODE == B_DUAL && r >= H;
     const int br = min(up ? r - H : r, b_rows_here - 1);
     b_brow[ii] = br;
     b_base[ii] = (up ? args.b1 : args.b0) + (int64_t)e * args.b_expert_stride + (int64_t)nt * H * args.ldb;
-    b_off[ii] = (uint32_t)(br * args.ldb) + lane_chunk;
+    b_chunk[ii] = lane_chunk(wave * B_W + ii);
+    b_off[ii] = (uint32_t)(br * args.ldb) + b_chunk[ii];
   }
 
-  auto issue_a = [&](int kt, char* stage) {
-#pragma unroll
-    for (int ii = 0; ii < A_W; ++ii) {
-      const char* g = a_base + (a_off[ii] + (uint32_t)kt * ROWB);
-      __builtin_amdgcn_global_load_lds((const void*)g, (lds_void_t*)(stage + (wave * A_W + ii) * 16 * ROWB), 16, 0, 0);
+  // DMA of one K step.  dma_a / dma_b issue instruction ii of this wave for
+  // A / B tile kt into `stage`.
+  struct BStep {  // per-step B source of B_KSEG (segment lookup)
+    const char* base;
+    int64_t ld;
+  };
+  auto b_step = [&](int kt) -> BStep {
+    if constexpr (BMODE == B_KSEG) {
+      constexpr int U = KB / kSegUnit;  // segment units per K step
+      int s = 0;
+      while (s + 1 < args.nseg && kt * U >= args.seg_kt0[s + 1]) ++s;
+      const int64_t ld = args.seg_ld[s];
+      return {args.seg_base[s] + (int64_t)nt * BN * ld +
+                  ((int64_t)kt * ROWB - (int64_t)args.seg_kt0[s] * kSegUnit),
+              ld};
+    } else {
+      return {nullptr, 0};
     }
   };
-  auto issue_b = [&](int kt, char* stage) {
-    if constexpr (BMODE == B_KSEG) {
-      int s = 0;
-      while (s + 1 < args.nseg && kt >= args.seg_kt0[s + 1]) ++s;
-      const int64_t ld = args.seg_ld[s];
-      const char* bbase = args.seg_base[s] + (int64_t)nt * BN * ld + (int64_t)(kt - args.seg_kt0[s]) * ROWB;
-#pragma unroll
-      for (int ii = 0; ii < B_W; ++ii) {
-        const char* g = bbase + ((uint32_t)(b_brow[ii] * ld) + lane_chunk);
-        __builtin_amdgcn_global_load_lds((const void*)g, (lds_void_t*)(stage + (wave * B_W + ii) * 16 * ROWB), 16, 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int ii = 0; ii < B_W; ++ii) {
-        const char* g = b_base[ii] + (b_off[ii] + (uint32_t)kt * ROWB);
-        __builtin_amdgcn_global_load_lds((const void*)g, (lds_void_t*)(stage + (wave * B_W + ii) * 16 * ROWB), 16, 0, 0);
-      }
-    }
+  auto dma_a = [&](int kt, char* stage, int ii) {
+    const char* g = a_base + (a_off[ii] + (uint32_t)kt * ROWB);
+    __builtin_amdgcn_global_load_lds((const void*)g, (lds_void_t*)(stage + (wave * A_W + ii) * RPI * ROWB), 16, 0, 0);
+  };
+  auto dma_b = [&](int kt, const BStep& bs, char* stage, int ii) {
+    const char* g;
+    if constexpr (BMODE == B_KSEG) g = bs.base + ((uint32_t)(b_brow[ii] * bs.ld) + b_chunk[ii]);
+    else g = b_base[ii] + (b_off[ii] + (uint32_t)kt * ROWB);
+    __builtin_amdgcn_global_load_lds((const void*)g, (lds_void_t*)(stage + (wave * B_W + ii) * RPI * ROWB), 16, 0, 0);
   };
 
   f32x16 acc[TM][TN];
@@ -235,27 +283,92 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
     }
   };
   // physical byte offset of logical 16-byte chunk c of tile row `row`
-  auto swz = [](int row, int c) -> int { return row * ROWB + ((c ^ ((row >> 2) & 3)) << 4); };
+  auto swz = [](int row, int c) -> int { return row * ROWB + ((c ^ ((row / RSH) % NCH)) << 4); };
 
-  // Multiply one K step held in LDS.  NA = number of this wave's 32-row
-  // sub-tiles that hold valid rows (a wave-uniform constant of the
-  // instantiation, so the step is straight-line code).
-  auto compute = [&](const char* As, const char* Bs, auto na_c) {
-    constexpr int NA = decltype(na_c)::value;
-    // two fragment chunks per lane per K step:
-    //   16-bit: chunk lh holds k 8lh..8lh+7 of step 0, chunk 2+lh those of step 1
-    //   fp32:   chunks 2lh and 2lh+1 hold k 8lh..8lh+7, one k per MFMA
-    u32x4 fa[2][NA > 0 ? NA : 1], fb[2][TN];
+  // ---- main loop.  Tile t of A sits in A stage t % SA, of B in B stage
+  // t % SB.  A K step kt has two phases split by the workgroup barrier:
+  //   phase 1: MFMAs on fragment chunks 0..H-1 of tile kt (already in
+  //            registers) while chunks H..NC-1 of tile kt are read from LDS;
+  //   wait:    this wave's reads of tile kt are done (lgkmcnt 0) and its DMA
+  //            of tile kt+1 has landed (vmcnt), then the barrier: tile kt's
+  //            stages are free and tile kt+1 is visible to every wave;
+  //   phase 2: MFMAs on chunks H..NC-1 of tile kt while chunks 0..H-1 of tile
+  //            kt+1 are read and the DMA of A tile kt+SA / B tile kt+SB is
+  //            issued into the stages tile kt just released.
+  // Every MFMA after the barrier has its operands in registers already, so
+  // the barrier costs no LDS round trip.  Tiles past the end (t >= KT) reload
+  // tile KT-1 into their stage (no later step reads it): every step issues the
+  // same instructions, the steps are branch-free and the vmcnt accounting is
+  // exact.  B is issued after A when SB > SA (B runs further ahead) and before
+  // it when SB == SA; either way B(t) is issued before A(t), so waiting for
+  // A(kt+1) covers B(kt+1): the DMA instructions issued after A(kt+1) are
+  // those of the SA-2 later steps, plus B(kt+1-SA+SB) when SB > SA.
+  constexpr bool kAFirst = SB > SA;
+  constexpr int NI = A_W + B_W;                                 // DMA instructions per step
+  constexpr int kNewer = (kAFirst ? B_W : 0) + (SA - 2) * NI;  // vmcnt at the barrier of a step
+  constexpr int kNewer0 = kNewer + NI;                          // vmcnt before step 0
+  static_assert(kNewer0 < 64, "vmcnt range");
+  const int KT = args.K * (int)sizeof(TA) / ROWB;
+  auto clampt = [&](int t) { return t < KT ? t : KT - 1; };
+  // issue the DMA of A tile ta into A stage sa and B tile tb into B stage sb
+  auto dma_step = [&](int ta, char* sa, int tb, char* sb) {
+    const BStep bs = b_step(tb);
+    if constexpr (!kAFirst) {
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int ch = kHalf ? (2 * c + lh) : (2 * lh + c);
+      for (int ii = 0; ii < B_W; ++ii) dma_b(tb, bs, sb, ii);
+    }
+#pragma unroll
+    for (int ii = 0; ii < A_W; ++ii) dma_a(ta, sa, ii);
+    if constexpr (kAFirst) {
+#pragma unroll
+      for (int ii = 0; ii < B_W; ++ii) dma_b(tb, bs, sb, ii);
+    }
+  };
+  auto barrier = [&]() {
+    asm volatile("" ::: "memory");  // no LDS access may move across the barrier
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  // prologue: the DMA of virtual steps -SB..-1 (A tiles 0..SA-1, B tiles 0..SB-1)
+#pragma unroll
+  for (int s = -SB; s < 0; ++s) {
+    const int ta = s + SA, tb = s + SB;
+    const BStep bs = b_step(clampt(tb));
+    if constexpr (!kAFirst) {
+#pragma unroll
+      for (int ii = 0; ii < B_W; ++ii) dma_b(clampt(tb), bs, ringB + tb * kStageB, ii);
+    }
+    if (ta >= 0) {
+#pragma unroll
+      for (int ii = 0; ii < A_W; ++ii) dma_a(clampt(ta), ringA + ta * kStageA, ii);
+    }
+    if constexpr (kAFirst) {
+#pragma unroll
+      for (int ii = 0; ii < B_W; ++ii) dma_b(clampt(tb), bs, ringB + tb * kStageB, ii);
+    }
+  }
+
+  // NA = number of this wave's 32-row sub-tiles that hold valid rows (a
+  // wave-uniform constant of the instantiation, so every step is
+  // straight-line code).
+  auto main_loop = [&](auto na_c) {
+    constexpr int NA = decltype(na_c)::value;
+    // NC = NCH / 2 fragment chunks per lane per K step:
+    //   16-bit: chunk c holds k 8lh..8lh+7 of MFMA c (LDS chunk 2c + lh)
+    //   fp32:   chunk c is LDS chunk NC*lh + c (this lane's K half), one k per MFMA
+    constexpr int NC = NCH / 2, H = NC / 2;
+    constexpr int NAr = NA > 0 ? NA : 1;
+    u32x4 fa[NC][NAr], fb[NC][TN];
+    auto read_chunk = [&](const char* As, const char* Bs, auto c_c) {
+      constexpr int c = decltype(c_c)::value;
+      const int ch = kHalf ? (2 * c + lh) : (NC * lh + c);
 #pragma unroll
       for (int i = 0; i < NA; ++i) fa[c][i] = *(const u32x4*)(As + swz(wm * WTM + i * 32 + lr, ch));
 #pragma unroll
       for (int j = 0; j < TN; ++j) fb[c][j] = *(const u32x4*)(Bs + swz(b_tile_row(j) + lr, ch));
-    }
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
+    };
+    auto mfma_chunk = [&](auto c_c) {
+      constexpr int c = decltype(c_c)::value;
 #pragma unroll
       for (int j = 0; j < TN; ++j)
         if constexpr (kWiden) fb[c][j] = bf16x8_to_f16x8(fb[c][j]);
@@ -280,58 +393,52 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
           }
         }
       }
-    }
-  };
-
-  // ---- main loop.  Tile t of A sits in A stage t % SA, of B in B stage
-  // t % SB.  Step s issues, right after its barrier, the B DMA of tile
-  // s + SB - 1 and then the A DMA of tile s + SA - 1; each overwrites the
-  // stage that step s - 1 read, which that same barrier released.  With B
-  // issued first in every step (and SB >= SA), waiting for A of tile kt also
-  // covers B of tile kt, so one vmcnt per step suffices: the operations
-  // issued after A(kt) are B tiles kt+SB-SA+1 .. kt+SB-2 and A tiles
-  // kt+1 .. kt+SA-2 (SA-2 of each).
-  const int KT = args.K * (int)sizeof(TA) / ROWB;
-  constexpr int kNewer = (SA - 2) * (B_W + A_W);  // steady-state vmcnt
-#pragma unroll
-  for (int s = -(SB - 1); s < 0; ++s) {  // the steps before step 0, issue part only
-    const int tb = s + SB - 1, ta = s + SA - 1;
-    if (tb >= 0 && tb < KT) issue_b(tb, ringB + tb * kStageB);
-    if (ta >= 0 && ta < KT) issue_a(ta, ringA + ta * kStageA);
-  }
-  auto barrier = [&]() {
-    asm volatile("" ::: "memory");  // no LDS access may move across the barrier
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-  };
-  // steady steps: every tile counted in kNewer exists (kt + SB - 2 < KT)
-  const int n_steady = KT - SB + 2 > 0 ? KT - SB + 2 : 0;
-  auto main_loop = [&](auto na_c) {
-    auto steady = [&](int kt, auto u_c) {
-      constexpr int u = decltype(u_c)::value;  // kt % UNROLL, stages are static
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kNewer));
-      barrier();
-      if (kt + SB - 1 < KT) issue_b(kt + SB - 1, ringB + ((u + SB - 1) % SB) * kStageB);
-      if (kt + SA - 1 < KT) issue_a(kt + SA - 1, ringA + ((u + SA - 1) % SA) * kStageA);
-      compute(ringA + (u % SA) * kStageA, ringB + (u % SB) * kStageB, na_c);
     };
-    for (int kt = 0; kt < n_steady; kt += UNROLL) {
-      steady(kt, IntC<0>{});
-      if constexpr (UNROLL > 1) if (kt + 1 < n_steady) steady(kt + 1, IntC<1>{});
-      if constexpr (UNROLL > 2) if (kt + 2 < n_steady) steady(kt + 2, IntC<2>{});
-      if constexpr (UNROLL > 3) if (kt + 3 < n_steady) steady(kt + 3, IntC<3>{});
-      if constexpr (UNROLL > 4) if (kt + 4 < n_steady) steady(kt + 4, IntC<4>{});
-      if constexpr (UNROLL > 5) if (kt + 5 < n_steady) steady(kt + 5, IntC<5>{});
-      if constexpr (UNROLL > 6) if (kt + 6 < n_steady) steady(kt + 6, IntC<6>{});
-      if constexpr (UNROLL > 7) if (kt + 7 < n_steady) steady(kt + 7, IntC<7>{});
-    }
-    // last SB-2 steps: full waits (stage indices are no longer static here)
-    for (int kt = n_steady; kt < KT; ++kt) {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    constexpr int MPC = NA * TN * (kHalf ? 1 : 4);  // MFMAs per chunk
+    constexpr int RPC = NA + TN;                     // fragment reads per chunk
+    // tile 0 landed and visible; its first chunks into registers
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kNewer0));
+    barrier();
+    sfor<H>([&](auto c_c) { read_chunk(ringA, ringB, c_c); });
+
+    auto one = [&](int kt, auto u_c) {
+      constexpr int u = decltype(u_c)::value;  // kt % UNROLL: stages are static
+      const char* As = ringA + (u % SA) * kStageA;
+      const char* Bs = ringB + (u % SB) * kStageB;
+      // phase 1
+      sfor<NC - H>([&](auto c_c) { read_chunk(As, Bs, IntC<H + decltype(c_c)::value>{}); });
+      sfor<H>([&](auto c_c) { mfma_chunk(c_c); });
+      // one MFMA (its operands were read in the previous phase), then the
+      // reads, which must be complete at the barrier, then the other MFMAs;
+      // nothing crosses the barrier
+      if constexpr (H * MPC > 0) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, (NC - H) * RPC, 0);
+      if constexpr (H * MPC > 1) __builtin_amdgcn_sched_group_barrier(0x008, H * MPC - 1, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(kNewer));
       barrier();
-      if (kt + SA - 1 < KT) issue_a(kt + SA - 1, ringA + ((kt + SA - 1) % SA) * kStageA);
-      compute(ringA + (kt % SA) * kStageA, ringB + (kt % SB) * kStageB, na_c);
+      __builtin_amdgcn_sched_barrier(0);
+      // phase 2 (program order: reads of tile kt+1, then the DMA into tile kt's stages)
+      sfor<H>([&](auto c_c) {
+        read_chunk(ringA + ((u + 1) % SA) * kStageA, ringB + ((u + 1) % SB) * kStageB, c_c);
+      });
+      dma_step(clampt(kt + SA), ringA + (u % SA) * kStageA, clampt(kt + SB), ringB + (u % SB) * kStageB);
+      sfor<NC - H>([&](auto c_c) { mfma_chunk(IntC<H + decltype(c_c)::value>{}); });
+      sched_interleave<(NC - H) * MPC, H * RPC, NI>();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int kt = 0; kt < KT; kt += UNROLL) {
+      one(kt, IntC<0>{});
+      if constexpr (UNROLL > 1) if (kt + 1 < KT) one(kt + 1, IntC<1>{});
+      if constexpr (UNROLL > 2) if (kt + 2 < KT) one(kt + 2, IntC<2>{});
+      if constexpr (UNROLL > 3) if (kt + 3 < KT) one(kt + 3, IntC<3>{});
+      if constexpr (UNROLL > 4) if (kt + 4 < KT) one(kt + 4, IntC<4>{});
+      if constexpr (UNROLL > 5) if (kt + 5 < KT) one(kt + 5, IntC<5>{});
+      if constexpr (UNROLL > 6) if (kt + 6 < KT) one(kt + 6, IntC<6>{});
+      if constexpr (UNROLL > 7) if (kt + 7 < KT) one(kt + 7, IntC<7>{});
     }
+    // the reloads past the end land before the ring is reused by the epilogue
+    __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(0));
   };
   if constexpr (GROUPED) {
     // sub-tiles of this wave that hold valid rows (uniform across the wave)

@@ -194,12 +194,12 @@ lmoe_status side_stream(hipStream_t* out) {
 
 // ------------------------------------------------------------ GEMM launches
 template <typename TA, typename TB, typename OutT, int BM, int BN, int WGM, int WGN, int AM, int BMD,
-          int EM, int SA, int SB>
+          int EM, int SA, int SB, int KB>
 lmoe_status launch_gemm(GemmArgs a, hipStream_t st) {
   const int64_t grid = (int64_t)a.m_tiles * a.n_tiles;
   if (grid <= 0) return LMOE_OK;
   if (grid > INT32_MAX) return fail(LMOE_ERR_UNSUPPORTED, "GEMM grid too large");
-  gemm_kernel<TA, TB, OutT, BM, BN, WGM, WGN, AM, BMD, EM, SA, SB>
+  gemm_kernel<TA, TB, OutT, BM, BN, WGM, WGN, AM, BMD, EM, SA, SB, KB>
       <<<(unsigned)grid, 64 * WGM * WGN, 0, st>>>(a);
   LMOE_HIP(hipGetLastError());
   return LMOE_OK;
@@ -216,12 +216,16 @@ lmoe_status launch_gemm(GemmArgs a, hipStream_t st) {
 enum Tile { TILE_S = 0, TILE_M = 1, TILE_L = 2, TILE_W = 3, TILE_V = 4 };
 
 template <typename TA, typename TB, typename OutT, int AM, int BMD, int EM, int BM, int BN, int WGM,
-          int WGN, int SA, int SB>
+          int WGN, int SA, int SB, int KB = 64>
 lmoe_status gemm_cfg(GemmArgs a, hipStream_t st) {
   constexpr int cols = BMD == B_DUAL ? BN / 2 : BN;
   a.n_tiles = (a.N + cols - 1) / cols;
   if (AM == A_DENSE) a.m_tiles = (a.M + BM - 1) / BM;
-  return launch_gemm<TA, TB, OutT, BM, BN, WGM, WGN, AM, BMD, EM, SA, SB>(a, st);
+  if ((int64_t)a.K * (int64_t)sizeof(TA) % KB != 0) return fail(LMOE_ERR_UNSUPPORTED, "K not a multiple of the K step");
+  if (BMD == B_KSEG)
+    for (int s = 0; s <= a.nseg; ++s)
+      if (a.seg_kt0[s] % (KB / kSegUnit) != 0) return fail(LMOE_ERR_UNSUPPORTED, "K segment not a multiple of the K step");
+  return launch_gemm<TA, TB, OutT, BM, BN, WGM, WGN, AM, BMD, EM, SA, SB, KB>(a, st);
 }
 
 template <typename TA, typename TB, typename OutT, int AM, int BMD, int EM>
@@ -229,15 +233,15 @@ lmoe_status gemm(GemmArgs a, Tile t, hipStream_t st) {
   constexpr bool dual = BMD == B_DUAL;
   if constexpr (AM == A_DENSE) {
     switch (t) {
-      case TILE_S: return gemm_cfg<TA, TB, OutT, AM, BMD, EM, 64, dual ? 256 : 128, 1, 4, 4, 4>(a, st);
-      case TILE_M: return gemm_cfg<TA, TB, OutT, AM, BMD, EM, 128, 128, 2, 2, 4, 4>(a, st);
-      default: return gemm_cfg<TA, TB, OutT, AM, BMD, EM, 256, 256, 2, 4, 4, 4>(a, st);
+      case TILE_S: return gemm_cfg<TA, TB, OutT, AM, BMD, EM, 64, dual ? 256 : 128, 1, 4, 3, 3, 128>(a, st);
+      case TILE_M: return gemm_cfg<TA, TB, OutT, AM, BMD, EM, 128, 128, 2, 2, 3, 3, 128>(a, st);
+      default: return gemm_cfg<TA, TB, OutT, AM, BMD, EM, 256, 256, 2, 4, 2, 2, 128>(a, st);
     }
   } else {
     switch (t) {
-      case TILE_V: return gemm_cfg<TA, TB, OutT, AM, BMD, EM, 64, 256, 1, 4, 3, 6>(a, st);
-      case TILE_M: return gemm_cfg<TA, TB, OutT, AM, BMD, EM, 128, 128, 2, 2, 4, 4>(a, st);
-      default: return gemm_cfg<TA, TB, OutT, AM, BMD, EM, 192, 256, 2, 2, 3, 6>(a, st);
+      case TILE_V: return gemm_cfg<TA, TB, OutT, AM, BMD, EM, 64, 256, 1, 4, 2, 3, 128>(a, st);
+      case TILE_M: return gemm_cfg<TA, TB, OutT, AM, BMD, EM, 128, 128, 2, 2, 3, 3, 128>(a, st);
+      default: return gemm_cfg<TA, TB, OutT, AM, BMD, EM, 192, 256, 2, 2, 2, 3, 128>(a, st);
     }
   }
 }
@@ -464,7 +468,7 @@ lmoe_status run_forward(const Plan& p, const lmoe_dims* dm, const lmoe_weights* 
   f.a = w.hcat;
   f.lda = p.ldh * p.es;
   f.nb_rows = p.d;
-  const int kt_per_fs = p.fs * p.es / kKStepBytes;
+  const int kt_per_fs = p.fs * p.es / kSegUnit;
   f.nseg = p.ns + 1;
   for (int j = 0; j < p.ns; ++j) {
     f.seg_base[j] = (const char*)W->sh_o + (int64_t)j * p.d * p.fs * p.es;
@@ -474,7 +478,7 @@ lmoe_status run_forward(const Plan& p, const lmoe_dims* dm, const lmoe_weights* 
   f.seg_base[p.ns] = (const char*)W->w_up;
   f.seg_ld[p.ns] = (int64_t)p.l * p.es;
   f.seg_kt0[p.ns] = p.ns * kt_per_fs;
-  f.seg_kt0[p.ns + 1] = (int)(p.ldh * p.es / kKStepBytes);
+  f.seg_kt0[p.ns + 1] = (int)(p.ldh * p.es / kSegUnit);
   f.out = (char*)y;
   f.ldo = (int64_t)p.d * p.es;
   LMOE_TRY((gemm<TI, T, T, A_DENSE, B_KSEG, E_STORE>(f, dense_tile(p.N, p.d, false), st)));
