@@ -193,6 +193,18 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
     m0 = mt * BM;
     rows_valid = min(BM, args.M - m0);
   }
+  // E_SLOTS: slot row q and weight p_q of every tile row, fetched now (their
+  // latency hides behind the main loop) into LDS outside the operand ring;
+  // the main loop's barriers publish them to every wave.
+  __shared__ int slot_row[EMODE == E_SLOTS ? BM : 1];
+  __shared__ float slot_p[EMODE == E_SLOTS ? BM : 1];
+  if constexpr (EMODE == E_SLOTS) {
+    for (int r = tid; r < BM; r += 64 * NW) {
+      const int q = r < rows_valid ? args.order[off + m0 + r] : 0;
+      slot_row[r] = q;
+      slot_p[r] = r < rows_valid ? args.probs[q] : 0.f;
+    }
+  }
 
   // ---- DMA plan.  For each operand, wave `wave` moves RPI-row blocks
   // wave*X_W + ii of the tile.  Lane l carries tile row r = block*RPI + l/NCH
@@ -482,7 +494,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
       return acc[i][j][v];
   };
   auto out_row = [&](int r) -> int64_t {  // r: row inside the block tile
-    if constexpr (EMODE == E_SLOTS) return args.order[off + m0 + r];
+    if constexpr (EMODE == E_SLOTS) return slot_row[r];
     else return GROUPED ? off + m0 + r : (int64_t)(m0 + r);
   };
 
@@ -498,10 +510,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         ps[v] = 1.f;
-        if constexpr (EMODE == E_SLOTS) {
-          const int r = wm * WTM + i * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
-          ps[v] = r < rows_valid ? args.probs[args.order[off + m0 + r]] : 0.f;
-        }
+        if constexpr (EMODE == E_SLOTS) ps[v] = slot_p[wm * WTM + i * 32 + 8 * (v >> 2) + 4 * lh + (v & 3)];
       }
 #pragma unroll
       for (int j = 0; j < TJ; ++j) {
@@ -542,7 +551,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
           const int r = wm * WTM + i * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
           if (r >= rows_valid) continue;
           float val = value(i, j, v);
-          if constexpr (EMODE == E_SLOTS) val *= args.probs[args.order[off + m0 + r]];
+          if constexpr (EMODE == E_SLOTS) val *= slot_p[r];
           Elem<OutT>::store((OutT*)(args.out + out_row(r) * args.ldo) + col, val);
         }
       }

@@ -241,7 +241,7 @@ lmoe_status gemm(GemmArgs a, Tile t, hipStream_t st) {
     switch (t) {
       case TILE_V: return gemm_cfg<TA, TB, OutT, AM, BMD, EM, 64, 256, 1, 4, 2, 3, 128>(a, st);
       case TILE_M: return gemm_cfg<TA, TB, OutT, AM, BMD, EM, 128, 128, 2, 2, 3, 3, 128>(a, st);
-      default: return gemm_cfg<TA, TB, OutT, AM, BMD, EM, 192, 256, 2, 2, 2, 3, 128>(a, st);
+      default: return gemm_cfg<TA, TB, OutT, AM, BMD, EM, 192, 256, 2, 4, 2, 3, 128>(a, st);
     }
   }
 }
