@@ -35,6 +35,10 @@ Pins (tests marked ``not gpu`` in tests/test_oracle_*.py):
   dispatch brute-force sort on tiny inputs, counts/offsets/C invariants.
   routed   sparse == dense-then-mask (two independent code paths), identical
            experts, k = R mixture, W_g = 0.
+  backward central finite differences of <du, routed_sparse> in every input,
+           torch autograd of a dense-then-mask torch composition, exactly
+           zero weight gradients for experts without pairs, SiTU derivative
+           == torch autograd and its large-beta SwiGLU limit.
   SiTU     |gate * up| < beta1*beta2, near-origin SwiGLU series bound,
            large-beta limit == SwiGLU (torch.nn.functional.silu).
   layer    large-beta layer == a torch library composition (F.linear, F.silu,
@@ -239,6 +243,84 @@ def routed_dense(z: np.ndarray, ids: np.ndarray, p: np.ndarray, experts: ExpertF
     for j in range(np.asarray(ids).shape[1]):
         u += np.asarray(p)[:, j:j + 1] * all_out[rows, np.asarray(ids)[:, j]]
     return u
+
+
+# --------------------------------------------------- routed experts, backward
+
+
+def situ_hidden_grad(a_g: np.ndarray, a_u: np.ndarray, beta1: float,
+                     beta2: float) -> tuple[np.ndarray, np.ndarray]:
+    """Partial derivatives of the SiTU-GLU hidden h = G(a_g) * U(a_u) of the
+    [sec-07] SiTU-GLU equation, G(a) = beta1*tanh(a/beta1)*sigmoid(a) and
+    U(a) = beta2*tanh(a/beta2), by the product and chain rules:
+        dh/da_g = G'(a_g) U(a_u),  G'(a) = (1 - tanh(a/beta1)^2) sigmoid(a)
+                                           + beta1 tanh(a/beta1) sigmoid(a) (1 - sigmoid(a))
+        dh/da_u = G(a_g) U'(a_u),  U'(a) = 1 - tanh(a/beta2)^2."""
+    a_g = np.asarray(a_g, dtype=np.float64)
+    a_u = np.asarray(a_u, dtype=np.float64)
+    tg, sg, tu = np.tanh(a_g / beta1), sigmoid(a_g), np.tanh(a_u / beta2)
+    gate, up = beta1 * tg * sg, beta2 * tu
+    d_gate = (1.0 - tg * tg) * sg + beta1 * tg * sg * (1.0 - sg)
+    d_up = 1.0 - tu * tu
+    return d_gate * up, gate * d_up
+
+
+@dataclass
+class RoutedGrads:
+    dz: np.ndarray      # [N, ell]  dL/dz
+    dp: np.ndarray      # [N, k]    dL/dp in slot order
+    dw: dict            # e -> (dW_g [ff, ell], dW_u [ff, ell], dW_o [ell, ff])
+
+
+def routed_backward(z: np.ndarray, ids: np.ndarray, p: np.ndarray, experts: ExpertFn,
+                    n_routed: int, beta1: float, beta2: float, du: np.ndarray,
+                    want=None) -> RoutedGrads:
+    """Reverse-mode derivative of ``routed_sparse`` for an upstream gradient
+    du = dL/du [N, ell] (the routed block of the layer backward; the pages
+    train this layer and their tests compare its sparse gradients with the
+    dense helper's).  For each pair (n, j) with expert e = ids[n, j]:
+        forward   a_g = W_g^e z_n, a_u = W_u^e z_n, h = SiTU hidden, o = W_o^e h,
+                  u_n += p_nj o
+        backward  dp_nj = <du_n, o>,  g_o = p_nj du_n,  dW_o^e += g_o h^T,
+                  g_h = (W_o^e)^T g_o,  g_g = g_h * dh/da_g,  g_u = g_h * dh/da_u,
+                  dW_g^e += g_g z_n^T,  dW_u^e += g_u z_n^T,
+                  dz_n += (W_g^e)^T g_g + (W_u^e)^T g_u.
+    Executed per expert over its pairs, the grouping of ``routed_sparse``.
+    ``want``: expert ids whose weight gradients are returned (default all);
+    an expert with no pair gets exactly zero weight gradients."""
+    z = np.asarray(z, dtype=np.float64)
+    du = np.asarray(du, dtype=np.float64)
+    ids = np.asarray(ids, dtype=np.int64)
+    N, ell = z.shape
+    k = ids.shape[1]
+    pf = np.asarray(p, dtype=np.float64).reshape(-1)
+    dz = np.zeros((N, ell), dtype=np.float64)
+    dp = np.zeros(N * k, dtype=np.float64)
+    want = range(n_routed) if want is None else list(want)
+    dw = {}
+    disp = dispatch(ids, n_routed) if N * k else None
+    for e in range(n_routed):
+        cnt = 0 if disp is None else int(disp.counts[e])
+        w_g, w_u, w_o = experts(e) if (cnt or e in want) else (None, None, None)
+        if cnt == 0:
+            if e in want:
+                dw[e] = (np.zeros_like(w_g), np.zeros_like(w_u), np.zeros_like(w_o))
+            continue
+        q = disp.order[disp.offsets[e]:disp.offsets[e] + cnt]   # flat pair ids of expert e
+        tok = q // k
+        Z, DU, P = z[tok], du[tok], pf[q]
+        a_g, a_u = Z @ w_g.T, Z @ w_u.T
+        h = situ_hidden(a_g, a_u, beta1, beta2)
+        o = h @ w_o.T
+        dp[q] = np.sum(DU * o, axis=1)
+        g_o = P[:, None] * DU
+        g_h = g_o @ w_o
+        dg, dgu = situ_hidden_grad(a_g, a_u, beta1, beta2)
+        g_g, g_u = g_h * dg, g_h * dgu
+        np.add.at(dz, tok, g_g @ w_g + g_u @ w_u)
+        if e in want:
+            dw[e] = (g_g.T @ Z, g_u.T @ Z, g_o.T @ h)
+    return RoutedGrads(dz, dp.reshape(N, k), dw)
 
 
 # ------------------------------------------------------------ shared + merge
