@@ -77,10 +77,57 @@ def cpu_baseline(cfg, n_sample: int):
                       f"{len(need)} routed experts touched); {dt:.1f} s"}
 
 
+def backward_leg(cfg, ids, probs, steps: int, warmup: int):
+    """Times latentmoe_routed_backward on the routes of the forward just run,
+    with a seeded latent z and upstream gradient du (generated in HBM)."""
+    import torch
+
+    import mixture_experts_ffn_sigmoid_amd as M
+
+    N, l, R, f, k = cfg.n_tokens, cfg.d_latent, cfg.n_routed, cfg.ff_routed, cfg.top_k
+    td = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    dev = {n: S.gen.device_tensor(cfg, n) for n in ("w_g", "w_u", "w_o", "z", "du")}
+    dz = torch.empty((N, l), dtype=torch.float32, device="cuda")
+    dprobs = torch.empty((N, k), dtype=torch.float32, device="cuda")
+    dw = [torch.empty((R, f, l), dtype=td, device="cuda"), torch.empty((R, f, l), dtype=td, device="cuda"),
+          torch.empty((R, l, f), dtype=td, device="cuda")]
+    dims = M.dims_of(cfg)
+    ws = torch.empty(M.workspace_bytes(dims, M.ENTRY_ROUTED_BACKWARD), dtype=torch.uint8, device="cuda")
+
+    def call():
+        M.latentmoe_routed_backward(dims, dev["z"], ids, probs, dev["w_g"], dev["w_u"], dev["w_o"], dev["du"],
+                                    dz, dprobs, *dw, workspace=ws)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        call()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    P = N * k
+    es = 2 if cfg.dtype == "bf16" else 4
+    flops = 18.0 * P * l * f  # g, up: 4; o: 2; dh: 2; dz: 4; three weight gradients: 6 (x P l f)
+    # unavoidable HBM bytes: read the routed weights once, write their gradients once
+    wbytes = 3 * R * f * l * es
+    by = 2 * wbytes + es * N * l + 4 * N * l * 2
+    out = {"ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 1), "algorithmic_flops": flops,
+           "algorithmic_bytes": by, "hbm_gbs": round(by / ms / 1e6, 1),
+           "roofline_frac_hbm": round(by / ms / 1e6 / PEAK_HBM_GBS, 4),
+           "note": "includes per-call transposes of the routed weights (2 x their bytes) and one host sync"}
+    del dev, dw, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 KERNEL_SOURCES = ("mixture_experts_ffn_sigmoid_amd/csrc/gemm_kernel.h",
                   "mixture_experts_ffn_sigmoid_amd/csrc/lmoe_common.h",
                   "mixture_experts_ffn_sigmoid_amd/csrc/route_kernels.h",
                   "mixture_experts_ffn_sigmoid_amd/csrc/merge_kernels.h",
+                  "mixture_experts_ffn_sigmoid_amd/csrc/backward_kernels.h",
                   "mixture_experts_ffn_sigmoid_amd/csrc/latentmoe.hip")
 
 
@@ -134,6 +181,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="k3full_n8192", choices=sorted(S.CONFIGS))
     ap.add_argument("--cpu-sample", type=int, default=24, help="tokens for the CPU oracle baseline (0: skip)")
+    ap.add_argument("--no-backward", action="store_true", help="skip the routed-block backward leg")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (FETCH_SIZE / WRITE_SIZE calibration)")
     args = ap.parse_args()
@@ -246,6 +294,8 @@ def main():
         "steps_breakdown": steps_out,
         "roofline": roof,
     }
+    if not args.no_backward:
+        out["routed_backward"] = backward_leg(cfg, bufs["ids"], bufs["probs"], max(2, args.steps // 4), 1)
     if args.cpu_sample > 0:
         out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_sample)
     print(json.dumps(out), flush=True)

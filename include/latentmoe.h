@@ -65,7 +65,8 @@ typedef enum {
   LMOE_ENTRY_ROUTE = 0,
   LMOE_ENTRY_DISPATCH = 1,
   LMOE_ENTRY_EXPERTS = 2,
-  LMOE_ENTRY_FORWARD = 3
+  LMOE_ENTRY_FORWARD = 3,
+  LMOE_ENTRY_ROUTED_BACKWARD = 4
 } lmoe_entry;
 
 /* Layer sizes (names after the chapter's component table). */
@@ -164,6 +165,33 @@ lmoe_status latentmoe_forward(const lmoe_dims* dims, const lmoe_weights* weights
                               void* y, int32_t* ids, float* probs, int32_t* counts,
                               int64_t* C_host, void* workspace, size_t workspace_bytes,
                               void* stream);
+
+/* Backward of the routed-expert block u = sum_j p_j E_{ids_j}(z) (chapter
+ * step 3 and the sparse-execution section, differentiated; the pages train
+ * this layer and their tests compare its sparse gradients with the dense
+ * helper's) for an upstream gradient du = dL/du.  Per pair (n, j), e = ids[n, j]:
+ *   a_g = W_g^e z_n, a_u = W_u^e z_n, h = SiTU hidden, o = W_o^e h
+ *   dprobs[n, j] = <du_n, o>          dW_o^e += p du_n h^T
+ *   g_h = (W_o^e)^T (p du_n), g_g = g_h * dh/da_g, g_u = g_h * dh/da_u
+ *   dW_g^e += g_g z_n^T, dW_u^e += g_u z_n^T, dz_n += (W_g^e)^T g_g + (W_u^e)^T g_u
+ * Inputs: z [N, l] and the weights w_g, w_u [R, f_r, l], w_o [R, l, f_r] in the
+ * storage dtype; ids [N, k] int32 and probs [N, k] fp32 as from
+ * latentmoe_route; du [N, l] fp32.  Outputs (device memory, caller-owned):
+ * dz [N, l] fp32, dprobs [N, k] fp32, dw_g, dw_u [R, f_r, l] and dw_o
+ * [R, l, f_r] in the storage dtype (fp32 accumulation, one rounding); every
+ * expert without pairs gets exact zeros.  With bf16 storage the pair
+ * intermediates are fp16 (as in the forward).  The pre-activations are
+ * recomputed from z.  Reads C back (waits on `stream` once); the rest is
+ * asynchronous.  Workspace: latentmoe_workspace_bytes(dims,
+ * LMOE_ENTRY_ROUTED_BACKWARD) bytes of device memory (it holds transposed
+ * copies of the routed weights).  Errors: INVALID_ARGUMENT for bad dims, NULL
+ * pointers or ids outside [0, R); WORKSPACE; UNSUPPORTED when l or f_r times
+ * (N k + 63 R) times the element size reaches 4 GiB. */
+lmoe_status latentmoe_routed_backward(const lmoe_dims* dims, const void* z, const int32_t* ids,
+                                      const float* probs, const void* w_g, const void* w_u,
+                                      const void* w_o, const float* du, float* dz, float* dprobs,
+                                      void* dw_g, void* dw_u, void* dw_o, void* workspace,
+                                      size_t workspace_bytes, void* stream);
 
 /* Legacy router that the K3 sigmoid router replaced (compare page, forward
  * hunk of latent_moe.py): ids = the k largest raw logits = W_r x (equal values:

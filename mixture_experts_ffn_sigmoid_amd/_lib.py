@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "liblatentmoe.so")
 
 LMOE_F32, LMOE_BF16 = 0, 1
-ENTRY_ROUTE, ENTRY_DISPATCH, ENTRY_EXPERTS, ENTRY_FORWARD = 0, 1, 2, 3
+ENTRY_ROUTE, ENTRY_DISPATCH, ENTRY_EXPERTS, ENTRY_FORWARD, ENTRY_ROUTED_BACKWARD = 0, 1, 2, 3, 4
 STATUS = {0: "OK", 1: "INVALID_ARGUMENT", 2: "UNSUPPORTED", 3: "CAPACITY", 4: "WORKSPACE", 5: "HIP"}
 
 # every symbol include/latentmoe.h declares
@@ -21,7 +21,7 @@ EXPORTS = (
     "latentmoe_workspace_bytes", "latentmoe_status_string", "latentmoe_last_error",
     "latentmoe_route", "latentmoe_dispatch", "latentmoe_experts", "latentmoe_forward",
     "latentmoe_forward_timed", "latentmoe_route_softmax", "latentmoe_router_losses_workspace_bytes",
-    "latentmoe_router_losses",
+    "latentmoe_router_losses", "latentmoe_routed_backward",
 )
 TIMING_EVENTS = 9
 STEP_NAMES = ("latent_gemm", "router", "dispatch", "shared_gateup", "routed_gateup", "routed_down",
@@ -77,8 +77,10 @@ def load() -> ctypes.CDLL:
     lib.latentmoe_router_losses_workspace_bytes.argtypes = [D]
     lib.latentmoe_router_losses_workspace_bytes.restype = st
     lib.latentmoe_router_losses.argtypes = [D, vp, vp, vp, vp, st, vp]
+    lib.latentmoe_routed_backward.argtypes = [D] + [vp] * 13 + [st, vp]
     for fn in ("latentmoe_route", "latentmoe_dispatch", "latentmoe_experts", "latentmoe_forward",
-               "latentmoe_forward_timed", "latentmoe_route_softmax", "latentmoe_router_losses"):
+               "latentmoe_forward_timed", "latentmoe_route_softmax", "latentmoe_router_losses",
+               "latentmoe_routed_backward"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -148,6 +150,15 @@ def latentmoe_router_losses(dims, logits, counts, out, workspace=None, stream=No
     check(load().latentmoe_router_losses(ctypes.byref(dims), ptr(logits), ptr(counts), ptr(out), ptr(ws),
                                          0 if ws is None else ws.numel() * ws.element_size(),
                                          stream_handle(stream)))
+
+
+def latentmoe_routed_backward(dims, z, ids, probs, w_g, w_u, w_o, du, dz, dprobs, dw_g, dw_u, dw_o,
+                              workspace=None, stream=None):
+    ws = workspace
+    check(load().latentmoe_routed_backward(ctypes.byref(dims), ptr(z), ptr(ids), ptr(probs), ptr(w_g), ptr(w_u),
+                                           ptr(w_o), ptr(du), ptr(dz), ptr(dprobs), ptr(dw_g), ptr(dw_u),
+                                           ptr(dw_o), ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                                           stream_handle(stream)))
 
 
 def latentmoe_dispatch(dims, ids, z, counts, offsets, order, padded=None, capacity=0,

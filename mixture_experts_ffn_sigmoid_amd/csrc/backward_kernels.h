@@ -1,0 +1,185 @@
+// Element-wise, reduction and layout kernels of the routed-block backward.
+// The matrix products run on the GEMM family (gemm_kernel.h).
+#pragma once
+
+#include "lmoe_common.h"
+
+namespace lmoe {
+
+// Zero n 4-byte words.
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0u;
+}
+
+// Batched transpose through a 64 x 64 LDS tile: out[b][c][col0 + r] = in[b][r][c]
+// for r < rows, c < cols (leading dimensions in elements).  Batches with
+// counts[b] == 0 are skipped when counts is given.  Grid: (ceil(cols/64),
+// ceil(rows/64), batches), 256 threads.
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_batched_kernel(const T* __restrict__ in, int64_t in_bstride,
+                                                                int ld_in, int rows, int cols,
+                                                                T* __restrict__ out, int64_t out_bstride,
+                                                                int ld_out, int col0,
+                                                                const int32_t* __restrict__ counts) {
+  const int b = blockIdx.z;
+  if (counts && counts[b] == 0) return;
+  __shared__ T tile[64][65];
+  const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const T* src = in + (int64_t)b * in_bstride;
+  T* dst = out + (int64_t)b * out_bstride;
+  for (int i = ty; i < 64; i += 4) {
+    const int r = r0 + i, c = c0 + tx;
+    if (r < rows && c < cols) tile[i][tx] = src[(int64_t)r * ld_in + c];
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int c = c0 + i, r = r0 + tx;
+    if (r < rows && c < cols) dst[(int64_t)c * ld_out + col0 + r] = tile[tx][i];
+  }
+}
+
+// Per-expert padded K ranges of the weight-gradient products:
+// kr_len[e] = counts[e] rounded up to 64, kr_off[e] = sum of kr_len[e'] for e' < e.
+// One workgroup of 1024 threads; R <= 4096.
+__global__ __launch_bounds__(1024) void padded_ranges_kernel(const int32_t* __restrict__ counts, int R,
+                                                             int32_t* __restrict__ kr_off,
+                                                             int32_t* __restrict__ kr_len) {
+  __shared__ int32_t part[1024];
+  const int t = threadIdx.x;
+  const int per = (R + 1023) / 1024;
+  const int e0 = t * per, e1 = min(R, e0 + per);
+  int32_t s = 0;
+  for (int e = e0; e < e1; ++e) s += (counts[e] + 63) & ~63;
+  part[t] = s;
+  __syncthreads();
+  for (int d = 1; d < 1024; d <<= 1) {  // inclusive scan of the partial sums
+    const int32_t v = t >= d ? part[t - d] : 0;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  int32_t run = part[t] - s;
+  for (int e = e0; e < e1; ++e) {
+    const int32_t len = (counts[e] + 63) & ~63;
+    kr_off[e] = run;
+    kr_len[e] = len;
+    run += len;
+  }
+}
+
+// Expert-segment transpose with zero padding: for expert e (blockIdx.z) and
+// segment row r < kr_len[e] (pairs of e in sorted order, r >= counts[e] pad):
+//   out[c * ld_out + kr_off[e] + r] = r < counts[e] ? src_row(e, r)[col_off + c] : 0
+// src_row(e, r) = src + row * ld_src with row = offsets[e] + r (sorted rows)
+// or, when order is given, row = order[offsets[e] + r] / top_k (token rows).
+// Grid: (ceil(ncols/64), ceil(max_len/64), R), 256 threads.
+template <typename TS, typename TD>
+__global__ __launch_bounds__(256) void segment_transpose_kernel(
+    const TS* __restrict__ src, int64_t ld_src, int col_off, int ncols, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ order, int top_k,
+    const int32_t* __restrict__ kr_off, const int32_t* __restrict__ kr_len, TD* __restrict__ out,
+    int64_t ld_out) {
+  const int e = blockIdx.z;
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  if (r0 >= kr_len[e]) return;
+  __shared__ float tile[64][65];
+  const int cnt = counts[e];
+  const int64_t base = offsets[e];
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int i = ty; i < 64; i += 4) {
+    const int r = r0 + i, c = c0 + tx;
+    float v = 0.f;
+    if (r < cnt && c < ncols) {
+      const int64_t row = order ? (int64_t)(order[base + r] / top_k) : base + r;
+      v = Elem<TS>::load(src + row * ld_src + col_off + c);
+    }
+    tile[i][tx] = v;
+  }
+  __syncthreads();
+  const int64_t dst0 = kr_off[e];
+  for (int i = ty; i < 64; i += 4) {
+    const int c = c0 + i, r = r0 + tx;
+    if (c < ncols) Elem<TD>::store(out + (int64_t)c * ld_out + dst0 + r, tile[tx][i]);
+  }
+}
+
+// h = SiTU hidden of the (gate, up) pre-activations, n elements.
+template <typename TD>
+__global__ __launch_bounds__(256) void situ_hidden_kernel(const float* __restrict__ g, const float* __restrict__ u,
+                                                          int64_t n, float beta1, float beta2,
+                                                          TD* __restrict__ h) {
+  const float ib1 = 1.0f / beta1, ib2 = 1.0f / beta2;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    Elem<TD>::store(h + i, situ_hidden(g[i], u[i], beta1, beta2, ib1, ib2));
+}
+
+// Pair gradients, one workgroup per sorted pair q' (pair q = order[q'],
+// token n = q / k):  dprobs[q] = <du[n], o[q']>,  dout[q'] = probs[q] * du[n].
+template <typename TD>
+__global__ __launch_bounds__(256) void pair_grad_kernel(const float* __restrict__ du, const float* __restrict__ o,
+                                                        const float* __restrict__ probs,
+                                                        const int32_t* __restrict__ order, int top_k, int ell,
+                                                        float* __restrict__ dprobs, TD* __restrict__ dout) {
+  const int64_t qs = blockIdx.x;
+  const int32_t q = order[qs];
+  const float* dur = du + (int64_t)(q / top_k) * ell;
+  const float* orow = o + qs * ell;
+  TD* drow = dout + qs * ell;
+  const float pq = probs[q];
+  float acc = 0.f;
+  for (int c = threadIdx.x; c < ell; c += 256) {
+    const float v = dur[c];
+    acc += v * orow[c];
+    Elem<TD>::store(drow + c, pq * v);
+  }
+  __shared__ float red[4];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) dprobs[q] = (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// SiTU-GLU backward through the hidden: with G(a) = b1 tanh(a/b1) sigmoid(a)
+// and U(a) = b2 tanh(a/b2),
+//   dg = dh * G'(g) U(u),  du = dh * G(g) U'(u)
+//   G'(a) = (1 - tanh(a/b1)^2) sigmoid(a) + b1 tanh(a/b1) sigmoid(a) (1 - sigmoid(a)),
+//   U'(a) = 1 - tanh(a/b2)^2.
+// Row q of dgu holds [dg | du] (f columns each); n = pairs * f elements.
+template <typename TD>
+__global__ __launch_bounds__(256) void situ_backward_kernel(const float* __restrict__ dh, const float* __restrict__ g,
+                                                            const float* __restrict__ u, int64_t n, int f,
+                                                            float beta1, float beta2, TD* __restrict__ dgu) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const float a = g[i], b = u[i], d = dh[i];
+    const float tg = tanhf(a / beta1), tu = tanhf(b / beta2);
+    const float sg = 1.0f / (1.0f + expf(-a));
+    const float gate = beta1 * tg * sg, up = beta2 * tu;
+    const float dgate = (1.0f - tg * tg) * sg + beta1 * tg * sg * (1.0f - sg);
+    const float dup = 1.0f - tu * tu;
+    const int64_t q = i / f, j = i - q * f;
+    Elem<TD>::store(dgu + q * 2 * f + j, d * dgate * up);
+    Elem<TD>::store(dgu + q * 2 * f + f + j, d * gate * dup);
+  }
+}
+
+// inv[order[q']] = q'
+__global__ __launch_bounds__(256) void inverse_order_kernel(const int32_t* __restrict__ order, int64_t pairs,
+                                                            int32_t* __restrict__ inv) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < pairs) inv[order[i]] = (int32_t)i;
+}
+
+// dz[n] = sum over slots j (in slot order) of rows[inv[n k + j]], one workgroup per token.
+__global__ __launch_bounds__(256) void pair_sum_kernel(const float* __restrict__ rows, const int32_t* __restrict__ inv,
+                                                       int top_k, int ell, float* __restrict__ dz) {
+  const int64_t n = blockIdx.x;
+  for (int c = threadIdx.x; c < ell; c += 256) {
+    float acc = 0.f;
+    for (int j = 0; j < top_k; ++j) acc += rows[(int64_t)inv[n * top_k + j] * ell + c];
+    dz[n * ell + c] = acc;
+  }
+}
+
+}  // namespace lmoe

@@ -22,6 +22,8 @@
 //   A_GATHER  grouped by expert: A row = z[order[offsets[e] + r] / k]   (routed, no padded copy)
 //   A_PADDED  grouped by expert: A row = padded[e * C + r]              (pages' [R, C, l] layout)
 //   A_SORTED  grouped by expert: A row = h[offsets[e] + r]              (rows in sorted pair order)
+//   A_KBATCH  dense A and B, batched: batch e multiplies the K range
+//             [kr_off[e], kr_off[e] + kr_len[e]) into out + e * o_batch_stride
 //   B_SINGLE  one weight matrix (per expert in grouped mode)
 //   B_DUAL    gate and up matrices interleaved per tile (BN/2 rows of each)
 //   B_KSEG    B concatenated along K from up to kMaxSeg separate matrices
@@ -34,7 +36,7 @@
 
 namespace lmoe {
 
-enum { A_DENSE = 0, A_GATHER = 1, A_PADDED = 2, A_SORTED = 3 };
+enum { A_DENSE = 0, A_GATHER = 1, A_PADDED = 2, A_SORTED = 3, A_KBATCH = 4 };
 enum { B_SINGLE = 0, B_DUAL = 1, B_KSEG = 2 };
 enum { E_STORE = 0, E_SITU = 1, E_SLOTS = 2 };
 
@@ -73,6 +75,11 @@ struct GemmArgs {
   const char* seg_base[kMaxSeg];
   int64_t seg_ld[kMaxSeg];
   int seg_kt0[kMaxSeg + 1];  // first K byte of each segment / kSegUnit (a multiple of KB / kSegUnit)
+  // A_KBATCH: per-batch K range (elements; multiples of KB / element size)
+  const int32_t* kr_off;
+  const int32_t* kr_len;
+  int nbatch;
+  int64_t o_batch_stride;  // bytes
   // out
   char* out;
   int64_t ldo;  // bytes (E_SLOTS: fp32 elements per slot row * 4)
@@ -132,7 +139,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
   constexpr int NW = WGM * WGN;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int TM = WTM / 32, TN = WTN / 32;
-  constexpr bool GROUPED = AMODE != A_DENSE;
+  constexpr bool GROUPED = AMODE == A_GATHER || AMODE == A_PADDED || AMODE == A_SORTED;
+  constexpr bool KBATCH = AMODE == A_KBATCH;
   // K step: KB bytes of every tile row = NCH 16-byte chunks.  One LDS-DMA
   // wave instruction moves 64 lanes x 16 bytes = RPI tile rows.
   static_assert(KB == 64 || KB == 128, "K step of 64 or 128 bytes");
@@ -159,7 +167,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
   const int wm = wave / WGN, wn = wave % WGN;
   const int lr = lane & 31, lh = lane >> 5;
 
-  int mt, nt;
+  int mt, nt, e_batch = 0;
   if constexpr (GROUPED) {
     // The grid is sized by a bound on the tile list; only the first
     // tile_count * n_tiles workgroup ids carry work.  Those ids reach the
@@ -171,8 +179,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
     mt = L / args.n_tiles;
     nt = L % args.n_tiles;
   } else {
-    const int total = args.m_tiles * args.n_tiles;
-    const int L = xcd_contiguous_id(blockIdx.x, total);
+    const int per = args.m_tiles * args.n_tiles;
+    const int total = per * (KBATCH ? args.nbatch : 1);
+    int L = xcd_contiguous_id(blockIdx.x, total);
+    if constexpr (KBATCH) {
+      e_batch = L / per;
+      L -= e_batch * per;
+    }
     constexpr int GM = 8;  // raster: groups of 8 M tiles sweep all N tiles
     const int group = L / (GM * args.n_tiles);
     const int first_m = group * GM;
@@ -193,6 +206,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
     m0 = mt * BM;
     rows_valid = min(BM, args.M - m0);
   }
+  // K range of this workgroup (A_KBATCH: its batch's range), in elements
+  const int kbeg = KBATCH ? args.kr_off[e_batch] : 0;
+  const int klen = KBATCH ? args.kr_len[e_batch] : args.K;
+  char* const outp = args.out + (KBATCH ? e_batch * args.o_batch_stride : 0);
   // E_SLOTS: slot row q and weight p_q of every tile row, fetched now (their
   // latency hides behind the main loop) into LDS outside the operand ring;
   // the main loop's barriers publish them to every wave.
@@ -225,7 +242,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
   if constexpr (AMODE == A_GATHER) a_base = args.a;
   else if constexpr (AMODE == A_PADDED) a_base = args.a + ((int64_t)e * args.cap + m0) * args.lda;
   else if constexpr (AMODE == A_SORTED) a_base = args.a + (off + m0) * args.lda;
-  else a_base = args.a + (int64_t)m0 * args.lda;
+  else a_base = args.a + (int64_t)m0 * args.lda + (int64_t)kbeg * (int64_t)sizeof(TA);
 #pragma unroll
   for (int ii = 0; ii < A_W; ++ii) {
     const int rr = min((wave * A_W + ii) * RPI + lane / NCH, rows_valid - 1);
@@ -243,7 +260,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
     const bool up = BMODE == B_DUAL && r >= H;
     const int br = min(up ? r - H : r, b_rows_here - 1);
     b_brow[ii] = br;
-    b_base[ii] = (up ? args.b1 : args.b0) + (int64_t)e * args.b_expert_stride + (int64_t)nt * H * args.ldb;
+    b_base[ii] = (up ? args.b1 : args.b0) + (int64_t)e * args.b_expert_stride + (int64_t)nt * H * args.ldb +
+                 (int64_t)kbeg * (int64_t)sizeof(TB);
     b_chunk[ii] = lane_chunk(wave * B_W + ii);
     b_off[ii] = (uint32_t)(br * args.ldb) + b_chunk[ii];
   }
@@ -320,7 +338,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
   constexpr int kNewer = (kAFirst ? B_W : 0) + (SA - 2) * NI;  // vmcnt at the barrier of a step
   constexpr int kNewer0 = kNewer + NI;                          // vmcnt before step 0
   static_assert(kNewer0 < 64, "vmcnt range");
-  const int KT = args.K * (int)sizeof(TA) / ROWB;
+  const int KT = klen * (int)sizeof(TA) / ROWB;  // 0 only for an empty A_KBATCH range
   auto clampt = [&](int t) { return t < KT ? t : KT - 1; };
   // issue the DMA of A tile ta into A stage sa and B tile tb into B stage sb
   auto dma_step = [&](int ta, char* sa, int tb, char* sb) {
@@ -341,9 +359,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
-  // prologue: the DMA of virtual steps -SB..-1 (A tiles 0..SA-1, B tiles 0..SB-1)
+  // prologue: the DMA of virtual steps -SB..-1 (A tiles 0..SA-1, B tiles 0..SB-1);
+  // an empty K range (KT == 0, uniform over the workgroup) has no DMA and no
+  // main loop: its tile is stored as zeros
 #pragma unroll
-  for (int s = -SB; s < 0; ++s) {
+  for (int s = -SB; s < 0 && KT > 0; ++s) {
     const int ta = s + SA, tb = s + SB;
     const BStep bs = b_step(clampt(tb));
     if constexpr (!kAFirst) {
@@ -452,7 +472,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
     // the reloads past the end land before the ring is reused by the epilogue
     __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(0));
   };
-  if constexpr (GROUPED) {
+  if (KT == 0) {
+  } else if constexpr (GROUPED) {
     // sub-tiles of this wave that hold valid rows (uniform across the wave)
     const int na = __builtin_amdgcn_readfirstlane(
         max(0, min(TM, (rows_valid - wm * WTM + 31) / 32)));
@@ -524,7 +545,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
         }
       }
     }
-    const bool aligned = (((uintptr_t)args.out | (uintptr_t)args.ldo) & 15) == 0;
+    const bool aligned = (((uintptr_t)outp | (uintptr_t)args.ldo) & 15) == 0;
     constexpr int EPC = 16 / OES;  // elements per chunk
     for (int id = lane; id < WTM * CPR; id += 64) {
       const int rl = id / CPR, c = id % CPR;
@@ -532,7 +553,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
       const int col = col0 + c * EPC;
       if (r >= rows_valid || col >= args.N) continue;
       const char* src = E + pos(rl, c);
-      OutT* dst = (OutT*)(args.out + out_row(r) * args.ldo) + col;
+      OutT* dst = (OutT*)(outp + out_row(r) * args.ldo) + col;
       if (aligned && col + EPC <= args.N) {
         *(u32x4*)dst = *(const u32x4*)src;
       } else {
@@ -552,7 +573,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
           if (r >= rows_valid) continue;
           float val = value(i, j, v);
           if constexpr (EMODE == E_SLOTS) val *= slot_p[r];
-          Elem<OutT>::store((OutT*)(args.out + out_row(r) * args.ldo) + col, val);
+          Elem<OutT>::store((OutT*)(outp + out_row(r) * args.ldo) + col, val);
         }
       }
     }

@@ -2,12 +2,14 @@
 // carving and the launch sequence of each entry point (see latentmoe.h).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
 #include <mutex>
 
 #include "latentmoe.h"
+#include "backward_kernels.h"
 #include "gemm_kernel.h"
 #include "merge_kernels.h"
 #include "route_kernels.h"
@@ -33,6 +35,15 @@ lmoe_status fail(lmoe_status s, const char* fmt, ...) {
       return fail(LMOE_ERR_HIP, "%s failed: %s (%s:%d)", #call, hipGetErrorString(e_), __FILE__, \
                   __LINE__);                                                                \
   } while (0)
+
+// Stream of an entry point's launches.  Also clears the calling thread's last
+// HIP error, which earlier calls of the caller (a failed pointer query, say)
+// may have left behind, so that the launch checks report this library's own
+// launches only.
+hipStream_t launch_stream(void* stream) {
+  (void)hipGetLastError();
+  return (hipStream_t)stream;
+}
 
 // ----------------------------------------------------------------- sizes
 struct Plan {
@@ -175,6 +186,48 @@ size_t carve_forward(const Plan& p, char* b, ForwardWs* w) {
   return c.off;
 }
 
+// Routed-block backward.  Rows of the [pairs, *] buffers are in sorted pair
+// order; the transposed [cols, kpad] buffers hold each expert's pairs as a
+// zero-padded column range of a multiple of 64 (kpad bounds their total).
+struct RoutedBwdWs {
+  int32_t *counts, *offsets, *order, *chunk_hist, *chunk_bad, *meta, *tile_list, *inv, *kr_off, *kr_len;
+  float *g, *up, *o, *dh;  // o also holds the dz rows once it is consumed
+  char *hs, *dout, *dgu;   // intermediate type
+  char *w_oT, *w_guT;      // storage type
+  char *doutT, *hT, *dgT, *duT, *zT;
+  int64_t kpad;
+};
+size_t carve_routed_backward(const Plan& p, char* b, RoutedBwdWs* w) {
+  Carver c{b};
+  const int64_t P = p.pairs, ei = p.es;  // intermediates: fp16 with bf16 storage, fp32 with fp32
+  w->kpad = P + 63 * (int64_t)p.R;
+  w->counts = c.take<int32_t>((size_t)p.R * 4);
+  w->offsets = c.take<int32_t>((size_t)p.R * 4);
+  w->order = c.take<int32_t>((size_t)P * 4);
+  w->chunk_hist = c.take<int32_t>((size_t)p.nchunks * p.R * 4);
+  w->chunk_bad = c.take<int32_t>((size_t)p.nchunks * 4);
+  w->meta = c.take<int32_t>(64);
+  w->tile_list = c.take<int32_t>((size_t)p.tile_bound * 8);
+  w->inv = c.take<int32_t>((size_t)P * 4);
+  w->kr_off = c.take<int32_t>((size_t)p.R * 4);
+  w->kr_len = c.take<int32_t>((size_t)p.R * 4);
+  w->g = c.take<float>((size_t)P * p.fr * 4);
+  w->up = c.take<float>((size_t)P * p.fr * 4);
+  w->o = c.take<float>((size_t)P * p.l * 4);
+  w->dh = c.take<float>((size_t)P * p.fr * 4);
+  w->hs = c.take<char>((size_t)P * p.fr * ei);
+  w->dout = c.take<char>((size_t)P * p.l * ei);
+  w->dgu = c.take<char>((size_t)P * 2 * p.fr * ei);
+  w->w_oT = c.take<char>((size_t)p.R * p.fr * p.l * p.es);
+  w->w_guT = c.take<char>((size_t)p.R * p.l * 2 * p.fr * p.es);
+  w->doutT = c.take<char>((size_t)p.l * w->kpad * ei);
+  w->hT = c.take<char>((size_t)p.fr * w->kpad * ei);
+  w->dgT = c.take<char>((size_t)p.fr * w->kpad * ei);
+  w->duT = c.take<char>((size_t)p.fr * w->kpad * ei);
+  w->zT = c.take<char>((size_t)p.l * w->kpad * ei);
+  return c.off;
+}
+
 // Largest batch whose shared-expert GEMM runs on the second stream.
 constexpr int64_t kOverlapMaxTokens = 2048;
 
@@ -196,7 +249,7 @@ lmoe_status side_stream(hipStream_t* out) {
 template <typename TA, typename TB, typename OutT, int BM, int BN, int WGM, int WGN, int AM, int BMD,
           int EM, int SA, int SB, int KB>
 lmoe_status launch_gemm(GemmArgs a, hipStream_t st) {
-  const int64_t grid = (int64_t)a.m_tiles * a.n_tiles;
+  const int64_t grid = (int64_t)a.m_tiles * a.n_tiles * (AM == A_KBATCH ? a.nbatch : 1);
   if (grid <= 0) return LMOE_OK;
   if (grid > INT32_MAX) return fail(LMOE_ERR_UNSUPPORTED, "GEMM grid too large");
   gemm_kernel<TA, TB, OutT, BM, BN, WGM, WGN, AM, BMD, EM, SA, SB, KB>
@@ -220,7 +273,7 @@ template <typename TA, typename TB, typename OutT, int AM, int BMD, int EM, int 
 lmoe_status gemm_cfg(GemmArgs a, hipStream_t st) {
   constexpr int cols = BMD == B_DUAL ? BN / 2 : BN;
   a.n_tiles = (a.N + cols - 1) / cols;
-  if (AM == A_DENSE) a.m_tiles = (a.M + BM - 1) / BM;
+  if (AM == A_DENSE || AM == A_KBATCH) a.m_tiles = (a.M + BM - 1) / BM;
   if ((int64_t)a.K * (int64_t)sizeof(TA) % KB != 0) return fail(LMOE_ERR_UNSUPPORTED, "K not a multiple of the K step");
   if (BMD == B_KSEG)
     for (int s = 0; s <= a.nseg; ++s)
@@ -231,7 +284,7 @@ lmoe_status gemm_cfg(GemmArgs a, hipStream_t st) {
 template <typename TA, typename TB, typename OutT, int AM, int BMD, int EM>
 lmoe_status gemm(GemmArgs a, Tile t, hipStream_t st) {
   constexpr bool dual = BMD == B_DUAL;
-  if constexpr (AM == A_DENSE) {
+  if constexpr (AM == A_DENSE || AM == A_KBATCH) {
     switch (t) {
       case TILE_S: return gemm_cfg<TA, TB, OutT, AM, BMD, EM, 64, dual ? 256 : 128, 1, 4, 3, 3, 128>(a, st);
       case TILE_M: return gemm_cfg<TA, TB, OutT, AM, BMD, EM, 128, 128, 2, 2, 3, 3, 128>(a, st);
@@ -368,6 +421,131 @@ lmoe_status run_experts(const Plan& p, const lmoe_dims* dm, const void* a_src, i
   b.ldo = (int64_t)p.l * sizeof(TH);
   b.probs = probs;
   return gemm<TH, TW, TH, A_SORTED, B_SINGLE, E_SLOTS>(b, tile, st);
+}
+
+// Routed-block backward (see latentmoe_routed_backward).  T: storage type of
+// z, the weights and the weight gradients; TI: intermediate type.
+template <typename T, typename TI>
+lmoe_status run_routed_backward(const Plan& p, const lmoe_dims* dm, const void* z, const int32_t* ids,
+                                const float* probs, const void* w_g, const void* w_u, const void* w_o,
+                                const float* du, float* dz, float* dprobs, void* dw_g, void* dw_u,
+                                void* dw_o, const RoutedBwdWs& w, hipStream_t st) {
+  const int64_t P = p.pairs;
+  const int f = p.fr, l = p.l, R = p.R;
+  const int64_t es = sizeof(T), ei = sizeof(TI);
+  auto blocks = [](int64_t n) { return (unsigned)std::min<int64_t>((n + 255) / 256, 65536); };
+  // 1. bookkeeping: counts, offsets, stable order, C, tile list, inverse order, padded K ranges
+  LMOE_TRY(run_dispatch(p, ids, w.chunk_hist, w.chunk_bad, w.counts, w.offsets, w.order, w.meta, st));
+  tile_list_kernel<<<1, 1024, 0, st>>>(w.counts, R, p.tile_m, w.tile_list, w.meta);
+  LMOE_HIP(hipGetLastError());
+  int32_t meta[4] = {0, 0, 0, 0};
+  LMOE_HIP(hipMemcpyAsync(meta, w.meta, sizeof(meta), hipMemcpyDeviceToHost, st));
+  LMOE_HIP(hipStreamSynchronize(st));
+  if (meta[2] != 0) return fail(LMOE_ERR_INVALID_ARGUMENT, "%d expert ids outside [0, R)", meta[2]);
+  const int C = meta[0];
+  inverse_order_kernel<<<(unsigned)((P + 255) / 256), 256, 0, st>>>(w.order, P, w.inv);
+  LMOE_HIP(hipGetLastError());
+  padded_ranges_kernel<<<1, 1024, 0, st>>>(w.counts, R, w.kr_off, w.kr_len);
+  LMOE_HIP(hipGetLastError());
+  const Tile tile = p.tile_m == 64 ? TILE_V : p.tile_m == 128 ? TILE_M : TILE_W;
+  auto grouped = [&](const void* a, int64_t lda, const void* bw, int64_t ldb, int64_t bstride, int nrows,
+                     int K, void* out, int64_t ldo) {
+    GemmArgs g = base_args(dm);
+    g.N = nrows;
+    g.K = K;
+    g.m_tiles = (int)p.tile_bound;
+    g.a = (const char*)a;
+    g.lda = lda;
+    g.order = w.order;
+    g.top_k = p.k;
+    g.tile_list = w.tile_list;
+    g.tile_count = w.meta + 1;
+    g.counts = w.counts;
+    g.offsets = w.offsets;
+    g.b0 = (const char*)bw;
+    g.ldb = ldb;
+    g.b_expert_stride = bstride;
+    g.nb_rows = nrows;
+    g.out = (char*)out;
+    g.ldo = ldo;
+    return g;
+  };
+  // 2. pre-activations of every pair: g = z W_g^T, up = z W_u^T (fp32, sorted rows)
+  LMOE_TRY((gemm<T, T, float, A_GATHER, B_SINGLE, E_STORE>(
+      grouped(z, l * es, w_g, l * es, (int64_t)f * l * es, f, l, w.g, (int64_t)f * 4), tile, st)));
+  LMOE_TRY((gemm<T, T, float, A_GATHER, B_SINGLE, E_STORE>(
+      grouped(z, l * es, w_u, l * es, (int64_t)f * l * es, f, l, w.up, (int64_t)f * 4), tile, st)));
+  situ_hidden_kernel<TI><<<blocks(P * f), 256, 0, st>>>(w.g, w.up, P * f, dm->beta1, dm->beta2, (TI*)w.hs);
+  LMOE_HIP(hipGetLastError());
+  // 3. expert outputs o = h W_o^T (fp32), then dprobs and dout = p * du (sorted rows)
+  LMOE_TRY((gemm<TI, T, float, A_SORTED, B_SINGLE, E_STORE>(
+      grouped(w.hs, f * ei, w_o, f * es, (int64_t)l * f * es, l, f, w.o, (int64_t)l * 4), tile, st)));
+  pair_grad_kernel<TI><<<(unsigned)P, 256, 0, st>>>(du, w.o, probs, w.order, p.k, l, dprobs, (TI*)w.dout);
+  LMOE_HIP(hipGetLastError());
+  // 4. dh = dout W_o (through W_o^T [R, f, l]), then the SiTU backward -> [dg | du]
+  transpose_batched_kernel<T><<<dim3(f / 64, l / 64, R), 256, 0, st>>>(
+      (const T*)w_o, (int64_t)l * f, f, l, f, (T*)w.w_oT, (int64_t)f * l, l, 0, w.counts);
+  LMOE_HIP(hipGetLastError());
+  LMOE_TRY((gemm<TI, T, float, A_SORTED, B_SINGLE, E_STORE>(
+      grouped(w.dout, l * ei, w.w_oT, l * es, (int64_t)f * l * es, f, l, w.dh, (int64_t)f * 4), tile, st)));
+  situ_backward_kernel<TI><<<blocks(P * f), 256, 0, st>>>(w.dh, w.g, w.up, P * f, f, dm->beta1, dm->beta2,
+                                                          (TI*)w.dgu);
+  LMOE_HIP(hipGetLastError());
+  // 5. dz rows = [dg | du] [W_g | W_u] (through [W_g^T | W_u^T] [R, l, 2f]), summed per token
+  transpose_batched_kernel<T><<<dim3(l / 64, f / 64, R), 256, 0, st>>>(
+      (const T*)w_g, (int64_t)f * l, l, f, l, (T*)w.w_guT, (int64_t)l * 2 * f, 2 * f, 0, w.counts);
+  LMOE_HIP(hipGetLastError());
+  transpose_batched_kernel<T><<<dim3(l / 64, f / 64, R), 256, 0, st>>>(
+      (const T*)w_u, (int64_t)f * l, l, f, l, (T*)w.w_guT, (int64_t)l * 2 * f, 2 * f, f, w.counts);
+  LMOE_HIP(hipGetLastError());
+  float* dzrows = w.o;  // o is consumed
+  LMOE_TRY((gemm<TI, T, float, A_SORTED, B_SINGLE, E_STORE>(
+      grouped(w.dgu, 2 * f * ei, w.w_guT, 2 * f * es, (int64_t)l * 2 * f * es, l, 2 * f, dzrows,
+              (int64_t)l * 4),
+      tile, st)));
+  pair_sum_kernel<<<(unsigned)p.N, 256, 0, st>>>(dzrows, w.inv, p.k, l, dz);
+  LMOE_HIP(hipGetLastError());
+  // 6. weight gradients: per expert, products over its pairs (K = padded pair range)
+  const unsigned ysegs = (unsigned)((C + 63) / 64);
+  if (ysegs > 0) {
+    segment_transpose_kernel<TI, TI><<<dim3(l / 64, ysegs, R), 256, 0, st>>>(
+        (const TI*)w.dout, l, 0, l, w.counts, w.offsets, nullptr, p.k, w.kr_off, w.kr_len, (TI*)w.doutT, w.kpad);
+    LMOE_HIP(hipGetLastError());
+    segment_transpose_kernel<TI, TI><<<dim3(f / 64, ysegs, R), 256, 0, st>>>(
+        (const TI*)w.hs, f, 0, f, w.counts, w.offsets, nullptr, p.k, w.kr_off, w.kr_len, (TI*)w.hT, w.kpad);
+    LMOE_HIP(hipGetLastError());
+    segment_transpose_kernel<TI, TI><<<dim3(f / 64, ysegs, R), 256, 0, st>>>(
+        (const TI*)w.dgu, 2 * f, 0, f, w.counts, w.offsets, nullptr, p.k, w.kr_off, w.kr_len, (TI*)w.dgT, w.kpad);
+    LMOE_HIP(hipGetLastError());
+    segment_transpose_kernel<TI, TI><<<dim3(f / 64, ysegs, R), 256, 0, st>>>(
+        (const TI*)w.dgu, 2 * f, f, f, w.counts, w.offsets, nullptr, p.k, w.kr_off, w.kr_len, (TI*)w.duT, w.kpad);
+    LMOE_HIP(hipGetLastError());
+    segment_transpose_kernel<T, TI><<<dim3(l / 64, ysegs, R), 256, 0, st>>>(
+        (const T*)z, l, 0, l, w.counts, w.offsets, w.order, p.k, w.kr_off, w.kr_len, (TI*)w.zT, w.kpad);
+    LMOE_HIP(hipGetLastError());
+  }
+  auto batched = [&](const char* a, int M, const char* b, int N, void* out) {
+    GemmArgs g = base_args(dm);
+    g.M = M;
+    g.N = N;
+    g.K = 64;  // per-batch K comes from kr_len
+    g.a = a;
+    g.lda = w.kpad * ei;
+    g.b0 = b;
+    g.ldb = w.kpad * ei;
+    g.nb_rows = N;
+    g.kr_off = w.kr_off;
+    g.kr_len = w.kr_len;
+    g.nbatch = R;
+    g.out = (char*)out;
+    g.ldo = (int64_t)N * es;
+    g.o_batch_stride = (int64_t)M * N * es;
+    return g;
+  };
+  LMOE_TRY((gemm<TI, TI, T, A_KBATCH, B_SINGLE, E_STORE>(batched(w.doutT, l, w.hT, f, dw_o), dense_tile(l, f, false), st)));
+  LMOE_TRY((gemm<TI, TI, T, A_KBATCH, B_SINGLE, E_STORE>(batched(w.dgT, f, w.zT, l, dw_g), dense_tile(f, l, false), st)));
+  LMOE_TRY((gemm<TI, TI, T, A_KBATCH, B_SINGLE, E_STORE>(batched(w.duT, f, w.zT, l, dw_u), dense_tile(f, l, false), st)));
+  return LMOE_OK;
 }
 
 // Shared experts' gate/up GEMM with the SiTU epilogue -> hcat[:, :n_s f_s].
@@ -524,6 +702,10 @@ size_t latentmoe_workspace_bytes(const lmoe_dims* dims, int32_t entry) {
       ForwardWs w;
       return carve_forward(p, nullptr, &w);
     }
+    case LMOE_ENTRY_ROUTED_BACKWARD: {
+      RoutedBwdWs w;
+      return carve_routed_backward(p, nullptr, &w);
+    }
   }
   return 0;
 }
@@ -543,7 +725,7 @@ lmoe_status latentmoe_route(const lmoe_dims* dims, const void* x, const void* w_
     carve_route(p, (char*)workspace, &w);
     logits = w.logits;
   }
-  hipStream_t st = (hipStream_t)stream;
+  hipStream_t st = launch_stream(stream);
   if (p.bf16) return run_route<bf16_t>(p, dims, x, w_router, bias, ids, probs, logits, st);
   return run_route<float>(p, dims, x, w_router, bias, ids, probs, logits, st);
 }
@@ -563,7 +745,7 @@ lmoe_status latentmoe_route_softmax(const lmoe_dims* dims, const void* x, const 
     carve_route(p, (char*)workspace, &w);
     logits = w.logits;
   }
-  hipStream_t st = (hipStream_t)stream;
+  hipStream_t st = launch_stream(stream);
   if (p.bf16) return run_route<bf16_t>(p, dims, x, w_router, nullptr, ids, probs, logits, st, true);
   return run_route<float>(p, dims, x, w_router, nullptr, ids, probs, logits, st, true);
 }
@@ -581,7 +763,7 @@ lmoe_status latentmoe_router_losses(const lmoe_dims* dims, const float* logits, 
   Plan p;
   LMOE_TRY(check_dims(dims, &p));
   if (!out || !counts || (p.N > 0 && !logits)) return fail(LMOE_ERR_INVALID_ARGUMENT, "NULL tensor");
-  hipStream_t st = (hipStream_t)stream;
+  hipStream_t st = launch_stream(stream);
   const int64_t nblk = (p.N + kLossTokens - 1) / kLossTokens;
   const size_t need = latentmoe_router_losses_workspace_bytes(dims);
   if (!workspace || workspace_bytes < need)
@@ -608,7 +790,7 @@ lmoe_status latentmoe_dispatch(const lmoe_dims* dims, const int32_t* ids, const 
     return fail(LMOE_ERR_INVALID_ARGUMENT, "NULL argument");
   if (padded && !z) return fail(LMOE_ERR_INVALID_ARGUMENT, "padded output needs z");
   if (capacity < 0) return fail(LMOE_ERR_INVALID_ARGUMENT, "capacity < 0");
-  hipStream_t st = (hipStream_t)stream;
+  hipStream_t st = launch_stream(stream);
   *C_out = 0;
   if (p.N == 0) {
     LMOE_HIP(hipMemsetAsync(counts, 0, (size_t)p.R * 4, st));
@@ -659,7 +841,7 @@ lmoe_status latentmoe_experts(const lmoe_dims* dims, const void* padded, int64_t
   if (!workspace || workspace_bytes < need)
     return fail(LMOE_ERR_WORKSPACE, "experts needs %zu workspace bytes", need);
   carve_experts(p, (char*)workspace, &w);
-  hipStream_t st = (hipStream_t)stream;
+  hipStream_t st = launch_stream(stream);
   if (p.bf16)
     LMOE_TRY((run_experts<bf16_t, bf16_t, f16_t, A_PADDED>(p, dims, padded, C, counts, offsets, order, probs, w_g,
                                             w_u, w_o, w.tile_list, w.meta, w.h, w.slots, st)));
@@ -698,7 +880,7 @@ lmoe_status forward_impl(const lmoe_dims* dims, const lmoe_weights* weights, con
   if (!workspace || workspace_bytes < need)
     return fail(LMOE_ERR_WORKSPACE, "forward needs %zu workspace bytes", need);
   carve_forward(p, (char*)workspace, &w);
-  hipStream_t st = (hipStream_t)stream;
+  hipStream_t st = launch_stream(stream);
   if (p.bf16) LMOE_TRY((run_forward<bf16_t, f16_t>(p, dims, W, x, y, ids, probs, counts, w, st, ev)));
   else LMOE_TRY((run_forward<float, float>(p, dims, W, x, y, ids, probs, counts, w, st, ev)));
   if (C_host) {
@@ -732,6 +914,40 @@ lmoe_status latentmoe_forward_timed(const lmoe_dims* dims, const lmoe_weights* w
     if (!events[i]) return fail(LMOE_ERR_INVALID_ARGUMENT, "NULL event");
   return forward_impl(dims, weights, x, y, ids, probs, counts, nullptr, workspace, workspace_bytes,
                       stream, (hipEvent_t*)events);
+}
+
+lmoe_status latentmoe_routed_backward(const lmoe_dims* dims, const void* z, const int32_t* ids,
+                                      const float* probs, const void* w_g, const void* w_u,
+                                      const void* w_o, const float* du, float* dz, float* dprobs,
+                                      void* dw_g, void* dw_u, void* dw_o, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  Plan p;
+  LMOE_TRY(check_dims(dims, &p));
+  if (!w_g || !w_u || !w_o || !dw_g || !dw_u || !dw_o) return fail(LMOE_ERR_INVALID_ARGUMENT, "NULL weight");
+  if (p.N > 0 && (!z || !ids || !probs || !du || !dz || !dprobs))
+    return fail(LMOE_ERR_INVALID_ARGUMENT, "NULL tensor");
+  RoutedBwdWs w{};
+  const size_t need = carve_routed_backward(p, nullptr, &w);
+  if (!workspace || workspace_bytes < need)
+    return fail(LMOE_ERR_WORKSPACE, "routed backward needs %zu workspace bytes", need);
+  // transposed segments are addressed with 32-bit row offsets
+  if ((int64_t)std::max(p.l, p.fr) * w.kpad * p.es >= ((int64_t)1 << 32))
+    return fail(LMOE_ERR_UNSUPPORTED, "too many pairs for the weight-gradient layout");
+  carve_routed_backward(p, (char*)workspace, &w);
+  hipStream_t st = launch_stream(stream);
+  if (p.N == 0) {  // no pairs: every weight gradient is zero
+    const int64_t words = (int64_t)p.R * p.fr * p.l * p.es / 4;
+    for (void* d : {dw_g, dw_u, dw_o}) {
+      zero_words_kernel<<<1024, 256, 0, st>>>((uint32_t*)d, words);
+      LMOE_HIP(hipGetLastError());
+    }
+    return LMOE_OK;
+  }
+  if (p.bf16)
+    return run_routed_backward<bf16_t, f16_t>(p, dims, z, ids, probs, w_g, w_u, w_o, du, dz, dprobs, dw_g,
+                                              dw_u, dw_o, w, st);
+  return run_routed_backward<float, float>(p, dims, z, ids, probs, w_g, w_u, w_o, du, dz, dprobs, dw_g, dw_u,
+                                           dw_o, w, st);
 }
 
 }  // extern "C"

@@ -274,7 +274,7 @@ class RoutedGrads:
 
 def routed_backward(z: np.ndarray, ids: np.ndarray, p: np.ndarray, experts: ExpertFn,
                     n_routed: int, beta1: float, beta2: float, du: np.ndarray,
-                    want=None) -> RoutedGrads:
+                    want=None, only_want: bool = False) -> RoutedGrads:
     """Reverse-mode derivative of ``routed_sparse`` for an upstream gradient
     du = dL/du [N, ell] (the routed block of the layer backward; the pages
     train this layer and their tests compare its sparse gradients with the
@@ -287,7 +287,9 @@ def routed_backward(z: np.ndarray, ids: np.ndarray, p: np.ndarray, experts: Expe
                   dz_n += (W_g^e)^T g_g + (W_u^e)^T g_u.
     Executed per expert over its pairs, the grouping of ``routed_sparse``.
     ``want``: expert ids whose weight gradients are returned (default all);
-    an expert with no pair gets exactly zero weight gradients."""
+    an expert with no pair gets exactly zero weight gradients.  With
+    ``only_want`` the other experts are skipped altogether (dz and dp then
+    hold only the contributions of the wanted experts)."""
     z = np.asarray(z, dtype=np.float64)
     du = np.asarray(du, dtype=np.float64)
     ids = np.asarray(ids, dtype=np.int64)
@@ -300,6 +302,8 @@ def routed_backward(z: np.ndarray, ids: np.ndarray, p: np.ndarray, experts: Expe
     dw = {}
     disp = dispatch(ids, n_routed) if N * k else None
     for e in range(n_routed):
+        if only_want and e not in want:
+            continue
         cnt = 0 if disp is None else int(disp.counts[e])
         w_g, w_u, w_o = experts(e) if (cnt or e in want) else (None, None, None)
         if cnt == 0:

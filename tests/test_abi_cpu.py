@@ -29,7 +29,7 @@ def test_workspace_sizes_grow_with_tokens():
     for cfg in S.CONFIGS.values():
         d1 = M.dims_of(cfg)
         d2 = M.dims_of(cfg, n_tokens=2 * cfg.n_tokens)
-        for e in range(4):
+        for e in range(5):
             assert M.workspace_bytes(d1, e) > 0
             assert M.workspace_bytes(d2, e) >= M.workspace_bytes(d1, e)
     # forward needs at least z, the slots and the expert hidden of every pair (16-bit)
@@ -96,3 +96,25 @@ def test_router_entry_errors():
     assert lib.latentmoe_router_losses(ctypes.byref(dims), 16, 16, 16, 16, 8, None) == 4
     assert lib.latentmoe_route_softmax(ctypes.byref(dims), 16, 16, None, 16, 16, 16, 1 << 30, None) == 1
     assert lib.latentmoe_route_softmax(ctypes.byref(dims), 16, 16, 16, 16, None, 16, 8, None) == 4
+
+
+def test_routed_backward_argument_errors():
+    lib = M.load()
+    dims = M.dims_of(S.CONFIGS["toy_n128"])
+    fake = 4096  # never dereferenced: validation fails first
+    args = [fake] * 12
+    # NULL weight gradient
+    bad = list(args)
+    bad[11] = None
+    assert lib.latentmoe_routed_backward(ctypes.byref(dims), *bad, fake, 1 << 40, None) == 1
+    # NULL upstream gradient
+    bad = list(args)
+    bad[6] = None
+    assert lib.latentmoe_routed_backward(ctypes.byref(dims), *bad, fake, 1 << 40, None) == 1
+    # workspace too small
+    assert lib.latentmoe_routed_backward(ctypes.byref(dims), *args, fake, 16, None) == 4
+    assert b"workspace" in lib.latentmoe_last_error()
+    # the workspace holds at least the transposed routed weights
+    c = S.CONFIGS["b05_n4096"]
+    need = 3 * c.n_routed * c.ff_routed * c.d_latent * 2
+    assert M.workspace_bytes(M.dims_of(c), M.ENTRY_ROUTED_BACKWARD) >= need

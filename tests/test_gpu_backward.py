@@ -1,0 +1,187 @@
+"""Parity of the routed-block backward (latentmoe_routed_backward, through
+the C ABI) with the oracle's ``routed_backward`` on seeded inputs: z and du
+from the generator, routes from the oracle router on the configured x."""
+import numpy as np
+import pytest
+import torch
+
+import lmoe_synth as S
+import mixture_experts_ffn_sigmoid_amd as M
+import oracle as O
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+
+def setup_module(module):
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    M.load()  # fails loudly when the library is missing
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _routes(cfg, W):
+    """ids and fp32 probs from the oracle router on the configured x."""
+    r = O.route(O.config_x(cfg), W.w_router, W.bias, cfg.top_k)
+    return r.ids.astype(np.int32), r.p.astype(np.float32)
+
+
+def _run_gpu(cfg, ids, probs, dev=None):
+    N, l, R, f, k = cfg.n_tokens, cfg.d_latent, cfg.n_routed, cfg.ff_routed, cfg.top_k
+    sdt = cfg.dtype
+    if dev is None:  # small configs: host arrays uploaded
+        dev = {n: G.upload(S.host_tensor(cfg, n), S.tensor_spec(cfg, n)[1]).reshape(S.tensor_spec(cfg, n)[0])
+               for n in ("w_g", "w_u", "w_o", "z", "du")}
+    dims = M.dims_of(cfg)
+    td = G.torch_dtype(sdt)
+    out = dict(
+        dz=torch.full((N, l), float("nan"), dtype=torch.float32, device="cuda"),
+        dprobs=torch.full((N, k), float("nan"), dtype=torch.float32, device="cuda"),
+        dw_g=torch.full((R, f, l), float("nan"), dtype=td, device="cuda"),
+        dw_u=torch.full((R, f, l), float("nan"), dtype=td, device="cuda"),
+        dw_o=torch.full((R, l, f), float("nan"), dtype=td, device="cuda"),
+    )
+    ws = torch.empty(max(M.workspace_bytes(dims, M.ENTRY_ROUTED_BACKWARD), 1), dtype=torch.uint8, device="cuda")
+    M.latentmoe_routed_backward(dims, dev["z"], torch.from_numpy(ids).cuda(), torch.from_numpy(probs).cuda(),
+                                dev["w_g"], dev["w_u"], dev["w_o"], dev["du"], out["dz"], out["dprobs"],
+                                out["dw_g"], out["dw_u"], out["dw_o"], workspace=ws)
+    torch.cuda.synchronize()
+    return out
+
+
+def _z_du(cfg, rows=None):
+    l = cfg.d_latent
+    if rows is None:
+        z = S.to_f64(S.host_tensor(cfg, "z"), cfg.dtype).reshape(cfg.n_tokens, l)
+        du = S.host_tensor(cfg, "du").astype(np.float64).reshape(cfg.n_tokens, l)
+        return z, du
+    z = np.stack([S.to_f64(S.host_tensor(cfg, "z", int(r) * l, l), cfg.dtype) for r in rows])
+    du = np.stack([S.host_tensor(cfg, "du", int(r) * l, l).astype(np.float64) for r in rows])
+    return z, du
+
+
+def _check(name, got, ref, tol):
+    err = G.rel_err(got, ref)
+    _say(f"   {name}: err {err:.3e}")
+    assert np.isfinite(got).all(), name
+    assert err <= tol, (name, err)
+
+
+def _check_wgrad(name, got, ref, dtype):
+    """Weight gradients are stored in the storage dtype.  bf16: every element
+    within 2 units in the last place of bf16 (2^-7 relative) plus 1e-2 of the
+    matrix rms (the fp16 pair intermediates summed over the expert's pairs);
+    fp32: the fp32 bar max|diff| <= 1e-4 rms."""
+    assert np.isfinite(got).all(), name
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    d = np.abs(got - ref)
+    if dtype == "bf16":
+        bound = 2.0 ** -7 * np.abs(ref) + 1e-2 * rms
+        worst = float(np.max(d / bound))
+        assert worst <= 1.0, (name, worst, G.rel_err(got, ref))
+    else:
+        assert G.rel_err(got, ref) <= G.TOL["f32"], (name, G.rel_err(got, ref))
+    return G.rel_err(got, ref)
+
+
+def _cfgs():
+    base = S.CONFIGS
+    return [
+        base["toy_n128"],
+        base["b05_n4096"],
+        base["b05skew_n4096"],
+        base["toy_n128"].with_(name="toy_n77_ragged", n_tokens=77),
+        base["toy_n128"].with_(name="toy_n3_sparse", n_tokens=3),
+        S.LayerConfig("kR_bf16", 70, 128, 64, 6, 6, 3, 128, 64, "bf16", seed=8, bias="uniform"),
+        S.LayerConfig("wide_k_bf16", 333, 256, 128, 40, 9, 1, 192, 256, "bf16", seed=9, bias="uniform"),
+    ]
+
+
+@pytest.mark.parametrize("cfg", _cfgs(), ids=lambda c: c.name)
+def test_routed_backward_parity(cfg):
+    _say(f"[routed_backward] {cfg.name}")
+    W = O.config_weights(cfg, cache_experts=cfg.n_routed)
+    ids, probs = _routes(cfg, W)
+    out = _run_gpu(cfg, ids, probs)
+    z, du = _z_du(cfg)
+    ref = O.routed_backward(z, ids, probs.astype(np.float64), W.experts, cfg.n_routed, cfg.beta1, cfg.beta2, du)
+    tol = G.TOL[cfg.dtype]
+    _check("dz", G.download_f64(out["dz"]), ref.dz, tol)
+    _check("dprobs", G.download_f64(out["dprobs"]), ref.dp, tol)
+    used = set(ids.reshape(-1).tolist())
+    for e in range(cfg.n_routed):
+        for j, nm in enumerate(("dw_g", "dw_u", "dw_o")):
+            got = G.download_f64(out[nm][e])
+            if e not in used:  # experts without pairs: exact zeros
+                assert np.all(got == 0.0), (nm, e)
+            else:
+                _check_wgrad(f"{nm}[{e}]", got, ref.dw[e][j], cfg.dtype)
+    _say(f"   experts used {len(used)}/{cfg.n_routed}")
+
+
+def test_routed_backward_is_deterministic():
+    cfg = S.CONFIGS["b05skew_n4096"]
+    W = O.config_weights(cfg)
+    ids, probs = _routes(cfg, W)
+    a = _run_gpu(cfg, ids, probs)
+    b = _run_gpu(cfg, ids, probs)
+    for k in a:
+        assert torch.equal(a[k].view(torch.int16) if a[k].dtype == torch.bfloat16 else a[k],
+                           b[k].view(torch.int16) if b[k].dtype == torch.bfloat16 else b[k]), k
+
+
+def test_routed_backward_empty_batch_zeroes_weight_grads():
+    cfg = S.CONFIGS["toy_n128"].with_(name="toy_n0", n_tokens=0)
+    out = _run_gpu(cfg, np.zeros((0, cfg.top_k), np.int32), np.zeros((0, cfg.top_k), np.float32),
+                   dev={n: G.upload(S.host_tensor(S.CONFIGS["toy_n128"], n), "f32").reshape(
+                       S.tensor_spec(S.CONFIGS["toy_n128"], n)[0]) for n in ("w_g", "w_u", "w_o")} |
+                   {"z": torch.empty(0, device="cuda"), "du": torch.empty(0, device="cuda")})
+    for nm in ("dw_g", "dw_u", "dw_o"):
+        assert torch.all(out[nm] == 0)
+
+
+def _full_size(name, tok_sample, n_experts_sample):
+    cfg = S.CONFIGS[name]
+    _say(f"[routed_backward full] {cfg.name}")
+    W = O.config_weights(cfg, cache_experts=2)
+    ids, probs = _routes(cfg, W)
+    dev = {n: S.gen.device_tensor(cfg, n) for n in ("w_g", "w_u", "w_o", "z", "du")}
+    out = _run_gpu(cfg, ids, probs, dev=dev)
+    del dev
+    tol = G.TOL[cfg.dtype]
+    # dz / dprobs of sampled tokens: their own pairs only
+    rows = np.asarray(tok_sample)
+    z, du = _z_du(cfg, rows)
+    ref = O.routed_backward(z, ids[rows], probs[rows].astype(np.float64), W.experts, cfg.n_routed,
+                            cfg.beta1, cfg.beta2, du, want=[])
+    _check("dz (sampled tokens)", G.download_f64(out["dz"][torch.as_tensor(rows)]), ref.dz, tol)
+    _check("dprobs (sampled tokens)", G.download_f64(out["dprobs"][torch.as_tensor(rows)]), ref.dp, tol)
+    # weight gradients of sampled experts: all their pairs
+    counts = np.bincount(ids.reshape(-1), minlength=cfg.n_routed)
+    used = np.nonzero(counts)[0]
+    picks = [int(used[0]), int(used[len(used) // 2]), int(used[-1])][:n_experts_sample]
+    for e in picks:
+        toks = np.nonzero((ids == e).any(axis=1))[0]
+        z, du = _z_du(cfg, toks)
+        r = O.routed_backward(z, ids[toks], probs[toks].astype(np.float64), W.experts, cfg.n_routed,
+                              cfg.beta1, cfg.beta2, du, want=[e], only_want=True)
+        for j, nm in enumerate(("dw_g", "dw_u", "dw_o")):
+            err = _check_wgrad(f"{nm}[{e}]", G.download_f64(out[nm][e]), r.dw[e][j], cfg.dtype)
+            _say(f"   {nm}[{e}] ({counts[e]} pairs): err {err:.3e}")
+    empty = np.nonzero(counts == 0)[0]
+    if empty.size:
+        for nm in ("dw_g", "dw_u", "dw_o"):
+            assert torch.all(out[nm][int(empty[0])].float() == 0), nm
+
+
+@pytest.mark.slow
+def test_routed_backward_k3_decode_sample():
+    _full_size("k3full_n64", [0, 21, 42, 63], 3)
+
+
+@pytest.mark.slow
+def test_routed_backward_k3_prefill_sample():
+    _full_size("k3full_n8192", [0, 4097, 8191], 2)

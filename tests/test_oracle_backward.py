@@ -141,3 +141,16 @@ def test_routed_backward_subset_and_empty():
     empty = O.routed_backward(np.zeros((0, 6)), np.zeros((0, 2), dtype=np.int64), np.zeros((0, 2)),
                               lambda e: (wg[e], wu[e], wo[e]), R, B1, B2, np.zeros((0, 6)))
     assert empty.dz.shape == (0, 6) and all(np.all(a == 0) for v in empty.dw.values() for a in v)
+
+
+def test_only_want_restricts_to_wanted_experts():
+    R = 4
+    z, wg, wu, wo, ids, p, du = _case(13, R=R)
+    full = O.routed_backward(z, ids, p, lambda e: (wg[e], wu[e], wo[e]), R, B1, B2, du)
+    e = int(ids[0, 0])
+    only = O.routed_backward(z, ids, p, lambda x: (wg[x], wu[x], wo[x]), R, B1, B2, du, want=[e], only_want=True)
+    for a, b in zip(full.dw[e], only.dw[e]):
+        assert np.array_equal(a, b)
+    # dp of the wanted expert's pairs is complete, the others are left at zero
+    mask = ids == e
+    assert np.array_equal(only.dp[mask], full.dp[mask]) and np.all(only.dp[~mask] == 0)
