@@ -185,8 +185,7 @@ lmoe_status latentmoe_forward(const lmoe_dims* dims, const lmoe_weights* weights
  * asynchronous.  Workspace: latentmoe_workspace_bytes(dims,
  * LMOE_ENTRY_ROUTED_BACKWARD) bytes of device memory (it holds transposed
  * copies of the routed weights).  Errors: INVALID_ARGUMENT for bad dims, NULL
- * pointers or ids outside [0, R); WORKSPACE; UNSUPPORTED when l or f_r times
- * (N k + 63 R) times the element size reaches 4 GiB. */
+ * pointers or ids outside [0, R); WORKSPACE. */
 lmoe_status latentmoe_routed_backward(const lmoe_dims* dims, const void* z, const int32_t* ids,
                                       const float* probs, const void* w_g, const void* w_u,
                                       const void* w_o, const float* du, float* dz, float* dprobs,

@@ -39,6 +39,43 @@ __global__ __launch_bounds__(256) void transpose_batched_kernel(const T* __restr
   }
 }
 
+// The same transpose for 16-bit elements with 16-byte global accesses: a
+// 64 x 64 tile is read as 8-element row chunks and written as 8-element
+// column chunks.  rows, cols, ld_in, ld_out and col0 are multiples of 8 and
+// the buffers 16-byte aligned.
+__global__ __launch_bounds__(256) void transpose16_batched_kernel(const uint16_t* __restrict__ in,
+                                                                  int64_t in_bstride, int ld_in, int rows,
+                                                                  int cols, uint16_t* __restrict__ out,
+                                                                  int64_t out_bstride, int ld_out, int col0,
+                                                                  const int32_t* __restrict__ counts) {
+  const int b = blockIdx.z;
+  if (counts && counts[b] == 0) return;
+  constexpr int LD = 72;  // padded row of the LDS tile (elements)
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64 * LD];
+  const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
+  const uint16_t* src = in + (int64_t)b * in_bstride;
+  uint16_t* dst = out + (int64_t)b * out_bstride;
+  const int t = threadIdx.x, q = t & 7;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {  // 64 rows x 8 chunks
+    const int r = (t >> 3) + 32 * i;
+    if (r0 + r < rows && c0 + q * 8 < cols)
+      *(u32x4*)(tile + r * LD + q * 8) = *(const u32x4*)(src + (int64_t)(r0 + r) * ld_in + c0 + q * 8);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {  // 64 output rows (columns c) x 8 chunks of 8 r
+    const int c = (t >> 3) + 32 * i;
+    if (c0 + c >= cols || r0 + q * 8 >= rows) continue;
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      w[j] = (uint32_t)tile[(q * 8 + 2 * j) * LD + c] | ((uint32_t)tile[(q * 8 + 2 * j + 1) * LD + c] << 16);
+    const u32x4 v = {w[0], w[1], w[2], w[3]};
+    *(u32x4*)(dst + (int64_t)(c0 + c) * ld_out + col0 + r0 + q * 8) = v;
+  }
+}
+
 // Per-expert padded K ranges of the weight-gradient products:
 // kr_len[e] = counts[e] rounded up to 64, kr_off[e] = sum of kr_len[e'] for e' < e.
 // One workgroup of 1024 threads; R <= 4096.
@@ -69,8 +106,10 @@ __global__ __launch_bounds__(1024) void padded_ranges_kernel(const int32_t* __re
 }
 
 // Expert-segment transpose with zero padding: for expert e (blockIdx.z) and
-// segment row r < kr_len[e] (pairs of e in sorted order, r >= counts[e] pad):
-//   out[c * ld_out + kr_off[e] + r] = r < counts[e] ? src_row(e, r)[col_off + c] : 0
+// segment row r < kr_len[e] (pairs of e in sorted order, r >= counts[e] pad),
+// expert e's block of out is row-major [ncols, kr_len[e]] at element
+// kr_off[e] * ncols:
+//   block[c * kr_len[e] + r] = r < counts[e] ? src_row(e, r)[col_off + c] : 0
 // src_row(e, r) = src + row * ld_src with row = offsets[e] + r (sorted rows)
 // or, when order is given, row = order[offsets[e] + r] / top_k (token rows).
 // Grid: (ceil(ncols/64), ceil(max_len/64), R), 256 threads.
@@ -78,8 +117,7 @@ template <typename TS, typename TD>
 __global__ __launch_bounds__(256) void segment_transpose_kernel(
     const TS* __restrict__ src, int64_t ld_src, int col_off, int ncols, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ order, int top_k,
-    const int32_t* __restrict__ kr_off, const int32_t* __restrict__ kr_len, TD* __restrict__ out,
-    int64_t ld_out) {
+    const int32_t* __restrict__ kr_off, const int32_t* __restrict__ kr_len, TD* __restrict__ out) {
   const int e = blockIdx.z;
   const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
   if (r0 >= kr_len[e]) return;
@@ -97,10 +135,11 @@ __global__ __launch_bounds__(256) void segment_transpose_kernel(
     tile[i][tx] = v;
   }
   __syncthreads();
-  const int64_t dst0 = kr_off[e];
+  const int64_t ld = kr_len[e];
+  TD* blk = out + (int64_t)kr_off[e] * ncols;
   for (int i = ty; i < 64; i += 4) {
     const int c = c0 + i, r = r0 + tx;
-    if (c < ncols) Elem<TD>::store(out + (int64_t)c * ld_out + dst0 + r, tile[tx][i]);
+    if (c < ncols) Elem<TD>::store(blk + (int64_t)c * ld + r, tile[tx][i]);
   }
 }
 

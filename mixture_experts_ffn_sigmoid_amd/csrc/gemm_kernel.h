@@ -22,8 +22,10 @@
 //   A_GATHER  grouped by expert: A row = z[order[offsets[e] + r] / k]   (routed, no padded copy)
 //   A_PADDED  grouped by expert: A row = padded[e * C + r]              (pages' [R, C, l] layout)
 //   A_SORTED  grouped by expert: A row = h[offsets[e] + r]              (rows in sorted pair order)
-//   A_KBATCH  dense A and B, batched: batch e multiplies the K range
-//             [kr_off[e], kr_off[e] + kr_len[e]) into out + e * o_batch_stride
+//   A_KBATCH  batched over experts e with their own K = kr_len[e]: A is the
+//             row-major [M, kr_len[e]] block at element kr_off[e] * M of a,
+//             B the [nb_rows, kr_len[e]] block at kr_off[e] * nb_rows of b0;
+//             the product goes to out + e * o_batch_stride
 //   B_SINGLE  one weight matrix (per expert in grouped mode)
 //   B_DUAL    gate and up matrices interleaved per tile (BN/2 rows of each)
 //   B_KSEG    B concatenated along K from up to kMaxSeg separate matrices
@@ -75,7 +77,7 @@ struct GemmArgs {
   const char* seg_base[kMaxSeg];
   int64_t seg_ld[kMaxSeg];
   int seg_kt0[kMaxSeg + 1];  // first K byte of each segment / kSegUnit (a multiple of KB / kSegUnit)
-  // A_KBATCH: per-batch K range (elements; multiples of KB / element size)
+  // A_KBATCH: per-batch K length and block start (elements; kr_len a multiple of KB / element size)
   const int32_t* kr_off;
   const int32_t* kr_len;
   int nbatch;
@@ -209,6 +211,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
   // K range of this workgroup (A_KBATCH: its batch's range), in elements
   const int kbeg = KBATCH ? args.kr_off[e_batch] : 0;
   const int klen = KBATCH ? args.kr_len[e_batch] : args.K;
+  const int64_t lda = KBATCH ? (int64_t)klen * (int64_t)sizeof(TA) : args.lda;  // bytes
+  const int64_t ldb = KBATCH ? (int64_t)klen * (int64_t)sizeof(TB) : args.ldb;
   char* const outp = args.out + (KBATCH ? e_batch * args.o_batch_stride : 0);
   // E_SLOTS: slot row q and weight p_q of every tile row, fetched now (their
   // latency hides behind the main loop) into LDS outside the operand ring;
@@ -242,13 +246,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
   if constexpr (AMODE == A_GATHER) a_base = args.a;
   else if constexpr (AMODE == A_PADDED) a_base = args.a + ((int64_t)e * args.cap + m0) * args.lda;
   else if constexpr (AMODE == A_SORTED) a_base = args.a + (off + m0) * args.lda;
-  else a_base = args.a + (int64_t)m0 * args.lda + (int64_t)kbeg * (int64_t)sizeof(TA);
+  else a_base = args.a + (int64_t)kbeg * args.M * (int64_t)sizeof(TA) + (int64_t)m0 * lda;
 #pragma unroll
   for (int ii = 0; ii < A_W; ++ii) {
     const int rr = min((wave * A_W + ii) * RPI + lane / NCH, rows_valid - 1);
     int64_t row = rr;
     if constexpr (AMODE == A_GATHER) row = args.order[off + m0 + rr] / args.top_k;
-    a_off[ii] = (uint32_t)(row * args.lda) + lane_chunk(wave * A_W + ii);
+    a_off[ii] = (uint32_t)(row * lda) + lane_chunk(wave * A_W + ii);
   }
   const char* b_base[B_W];  // workgroup-uniform
   uint32_t b_off[B_W];      // per lane, K step 0
@@ -260,10 +264,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
     const bool up = BMODE == B_DUAL && r >= H;
     const int br = min(up ? r - H : r, b_rows_here - 1);
     b_brow[ii] = br;
-    b_base[ii] = (up ? args.b1 : args.b0) + (int64_t)e * args.b_expert_stride + (int64_t)nt * H * args.ldb +
-                 (int64_t)kbeg * (int64_t)sizeof(TB);
+    b_base[ii] = (up ? args.b1 : args.b0) + (int64_t)e * args.b_expert_stride +
+                 (int64_t)kbeg * args.nb_rows * (int64_t)sizeof(TB) + (int64_t)nt * H * ldb;
     b_chunk[ii] = lane_chunk(wave * B_W + ii);
-    b_off[ii] = (uint32_t)(br * args.ldb) + b_chunk[ii];
+    b_off[ii] = (uint32_t)(br * ldb) + b_chunk[ii];
   }
 
   // DMA of one K step.  dma_a / dma_b issue instruction ii of this wave for

@@ -187,8 +187,9 @@ size_t carve_forward(const Plan& p, char* b, ForwardWs* w) {
 }
 
 // Routed-block backward.  Rows of the [pairs, *] buffers are in sorted pair
-// order; the transposed [cols, kpad] buffers hold each expert's pairs as a
-// zero-padded column range of a multiple of 64 (kpad bounds their total).
+// order; the transposed buffers hold, per expert, a row-major [cols, kr_len]
+// block of its pairs zero-padded to a multiple of 64 (kpad bounds the total
+// of kr_len).
 struct RoutedBwdWs {
   int32_t *counts, *offsets, *order, *chunk_hist, *chunk_bad, *meta, *tile_list, *inv, *kr_off, *kr_len;
   float *g, *up, *o, *dh;  // o also holds the dz rows once it is consumed
@@ -266,7 +267,9 @@ lmoe_status launch_gemm(GemmArgs a, hipStream_t st) {
 //     their weights (B) from HBM -- the deeper B ring keeps ~80 KB of weights
 //     in flight per CU while the A rows (L2-resident) need only three stages
 //   V  64 x 256, 4 waves, 3/6: the same for a handful of rows per expert
-enum Tile { TILE_S = 0, TILE_M = 1, TILE_L = 2, TILE_W = 3, TILE_V = 4 };
+//   M2 128 x 128, 4 waves, 2/2 (64 KB, two workgroups per CU): short-K
+//     products whose time goes into storing the output tile
+enum Tile { TILE_S = 0, TILE_M = 1, TILE_L = 2, TILE_W = 3, TILE_V = 4, TILE_M2 = 5 };
 
 template <typename TA, typename TB, typename OutT, int AM, int BMD, int EM, int BM, int BN, int WGM,
           int WGN, int SA, int SB, int KB = 64>
@@ -288,6 +291,7 @@ lmoe_status gemm(GemmArgs a, Tile t, hipStream_t st) {
     switch (t) {
       case TILE_S: return gemm_cfg<TA, TB, OutT, AM, BMD, EM, 64, dual ? 256 : 128, 1, 4, 3, 3, 128>(a, st);
       case TILE_M: return gemm_cfg<TA, TB, OutT, AM, BMD, EM, 128, 128, 2, 2, 3, 3, 128>(a, st);
+      case TILE_M2: return gemm_cfg<TA, TB, OutT, AM, BMD, EM, 128, 128, 2, 2, 2, 2, 128>(a, st);
       default: return gemm_cfg<TA, TB, OutT, AM, BMD, EM, 256, 256, 2, 4, 2, 2, 128>(a, st);
     }
   } else {
@@ -423,6 +427,23 @@ lmoe_status run_experts(const Plan& p, const lmoe_dims* dm, const void* a_src, i
   return gemm<TH, TW, TH, A_SORTED, B_SINGLE, E_SLOTS>(b, tile, st);
 }
 
+// Batched transpose out[b][c][col0 + r] = in[b][r][c] (16-byte accesses for
+// 16-bit elements), skipping batches without pairs.
+template <typename T>
+lmoe_status transpose_batched(const T* in, int64_t in_bstride, int ld_in, int rows, int cols, T* out,
+                              int64_t out_bstride, int ld_out, int col0, int nbatch, const int32_t* counts,
+                              hipStream_t st) {
+  const dim3 grid((cols + 63) / 64, (rows + 63) / 64, nbatch);
+  if constexpr (sizeof(T) == 2)
+    transpose16_batched_kernel<<<grid, 256, 0, st>>>((const uint16_t*)in, in_bstride, ld_in, rows, cols,
+                                                     (uint16_t*)out, out_bstride, ld_out, col0, counts);
+  else
+    transpose_batched_kernel<T><<<grid, 256, 0, st>>>(in, in_bstride, ld_in, rows, cols, out, out_bstride,
+                                                      ld_out, col0, counts);
+  LMOE_HIP(hipGetLastError());
+  return LMOE_OK;
+}
+
 // Routed-block backward (see latentmoe_routed_backward).  T: storage type of
 // z, the weights and the weight gradients; TI: intermediate type.
 template <typename T, typename TI>
@@ -483,21 +504,18 @@ lmoe_status run_routed_backward(const Plan& p, const lmoe_dims* dm, const void* 
   pair_grad_kernel<TI><<<(unsigned)P, 256, 0, st>>>(du, w.o, probs, w.order, p.k, l, dprobs, (TI*)w.dout);
   LMOE_HIP(hipGetLastError());
   // 4. dh = dout W_o (through W_o^T [R, f, l]), then the SiTU backward -> [dg | du]
-  transpose_batched_kernel<T><<<dim3(f / 64, l / 64, R), 256, 0, st>>>(
-      (const T*)w_o, (int64_t)l * f, f, l, f, (T*)w.w_oT, (int64_t)f * l, l, 0, w.counts);
-  LMOE_HIP(hipGetLastError());
+  LMOE_TRY(transpose_batched<T>((const T*)w_o, (int64_t)l * f, f, l, f, (T*)w.w_oT, (int64_t)f * l, l, 0, R,
+                                 w.counts, st));
   LMOE_TRY((gemm<TI, T, float, A_SORTED, B_SINGLE, E_STORE>(
       grouped(w.dout, l * ei, w.w_oT, l * es, (int64_t)f * l * es, f, l, w.dh, (int64_t)f * 4), tile, st)));
   situ_backward_kernel<TI><<<blocks(P * f), 256, 0, st>>>(w.dh, w.g, w.up, P * f, f, dm->beta1, dm->beta2,
                                                           (TI*)w.dgu);
   LMOE_HIP(hipGetLastError());
   // 5. dz rows = [dg | du] [W_g | W_u] (through [W_g^T | W_u^T] [R, l, 2f]), summed per token
-  transpose_batched_kernel<T><<<dim3(l / 64, f / 64, R), 256, 0, st>>>(
-      (const T*)w_g, (int64_t)f * l, l, f, l, (T*)w.w_guT, (int64_t)l * 2 * f, 2 * f, 0, w.counts);
-  LMOE_HIP(hipGetLastError());
-  transpose_batched_kernel<T><<<dim3(l / 64, f / 64, R), 256, 0, st>>>(
-      (const T*)w_u, (int64_t)f * l, l, f, l, (T*)w.w_guT, (int64_t)l * 2 * f, 2 * f, f, w.counts);
-  LMOE_HIP(hipGetLastError());
+  LMOE_TRY(transpose_batched<T>((const T*)w_g, (int64_t)f * l, l, f, l, (T*)w.w_guT, (int64_t)l * 2 * f, 2 * f,
+                                 0, R, w.counts, st));
+  LMOE_TRY(transpose_batched<T>((const T*)w_u, (int64_t)f * l, l, f, l, (T*)w.w_guT, (int64_t)l * 2 * f, 2 * f,
+                                 f, R, w.counts, st));
   float* dzrows = w.o;  // o is consumed
   LMOE_TRY((gemm<TI, T, float, A_SORTED, B_SINGLE, E_STORE>(
       grouped(w.dgu, 2 * f * ei, w.w_guT, 2 * f * es, (int64_t)l * 2 * f * es, l, 2 * f, dzrows,
@@ -509,19 +527,19 @@ lmoe_status run_routed_backward(const Plan& p, const lmoe_dims* dm, const void* 
   const unsigned ysegs = (unsigned)((C + 63) / 64);
   if (ysegs > 0) {
     segment_transpose_kernel<TI, TI><<<dim3(l / 64, ysegs, R), 256, 0, st>>>(
-        (const TI*)w.dout, l, 0, l, w.counts, w.offsets, nullptr, p.k, w.kr_off, w.kr_len, (TI*)w.doutT, w.kpad);
+        (const TI*)w.dout, l, 0, l, w.counts, w.offsets, nullptr, p.k, w.kr_off, w.kr_len, (TI*)w.doutT);
     LMOE_HIP(hipGetLastError());
     segment_transpose_kernel<TI, TI><<<dim3(f / 64, ysegs, R), 256, 0, st>>>(
-        (const TI*)w.hs, f, 0, f, w.counts, w.offsets, nullptr, p.k, w.kr_off, w.kr_len, (TI*)w.hT, w.kpad);
+        (const TI*)w.hs, f, 0, f, w.counts, w.offsets, nullptr, p.k, w.kr_off, w.kr_len, (TI*)w.hT);
     LMOE_HIP(hipGetLastError());
     segment_transpose_kernel<TI, TI><<<dim3(f / 64, ysegs, R), 256, 0, st>>>(
-        (const TI*)w.dgu, 2 * f, 0, f, w.counts, w.offsets, nullptr, p.k, w.kr_off, w.kr_len, (TI*)w.dgT, w.kpad);
+        (const TI*)w.dgu, 2 * f, 0, f, w.counts, w.offsets, nullptr, p.k, w.kr_off, w.kr_len, (TI*)w.dgT);
     LMOE_HIP(hipGetLastError());
     segment_transpose_kernel<TI, TI><<<dim3(f / 64, ysegs, R), 256, 0, st>>>(
-        (const TI*)w.dgu, 2 * f, f, f, w.counts, w.offsets, nullptr, p.k, w.kr_off, w.kr_len, (TI*)w.duT, w.kpad);
+        (const TI*)w.dgu, 2 * f, f, f, w.counts, w.offsets, nullptr, p.k, w.kr_off, w.kr_len, (TI*)w.duT);
     LMOE_HIP(hipGetLastError());
     segment_transpose_kernel<T, TI><<<dim3(l / 64, ysegs, R), 256, 0, st>>>(
-        (const T*)z, l, 0, l, w.counts, w.offsets, w.order, p.k, w.kr_off, w.kr_len, (TI*)w.zT, w.kpad);
+        (const T*)z, l, 0, l, w.counts, w.offsets, w.order, p.k, w.kr_off, w.kr_len, (TI*)w.zT);
     LMOE_HIP(hipGetLastError());
   }
   auto batched = [&](const char* a, int M, const char* b, int N, void* out) {
@@ -530,9 +548,7 @@ lmoe_status run_routed_backward(const Plan& p, const lmoe_dims* dm, const void* 
     g.N = N;
     g.K = 64;  // per-batch K comes from kr_len
     g.a = a;
-    g.lda = w.kpad * ei;
     g.b0 = b;
-    g.ldb = w.kpad * ei;
     g.nb_rows = N;
     g.kr_off = w.kr_off;
     g.kr_len = w.kr_len;
@@ -542,9 +558,10 @@ lmoe_status run_routed_backward(const Plan& p, const lmoe_dims* dm, const void* 
     g.o_batch_stride = (int64_t)M * N * es;
     return g;
   };
-  LMOE_TRY((gemm<TI, TI, T, A_KBATCH, B_SINGLE, E_STORE>(batched(w.doutT, l, w.hT, f, dw_o), dense_tile(l, f, false), st)));
-  LMOE_TRY((gemm<TI, TI, T, A_KBATCH, B_SINGLE, E_STORE>(batched(w.dgT, f, w.zT, l, dw_g), dense_tile(f, l, false), st)));
-  LMOE_TRY((gemm<TI, TI, T, A_KBATCH, B_SINGLE, E_STORE>(batched(w.duT, f, w.zT, l, dw_u), dense_tile(f, l, false), st)));
+  constexpr Tile kWgradTile = TILE_M2;
+  LMOE_TRY((gemm<TI, TI, T, A_KBATCH, B_SINGLE, E_STORE>(batched(w.doutT, l, w.hT, f, dw_o), kWgradTile, st)));
+  LMOE_TRY((gemm<TI, TI, T, A_KBATCH, B_SINGLE, E_STORE>(batched(w.dgT, f, w.zT, l, dw_g), kWgradTile, st)));
+  LMOE_TRY((gemm<TI, TI, T, A_KBATCH, B_SINGLE, E_STORE>(batched(w.duT, f, w.zT, l, dw_u), kWgradTile, st)));
   return LMOE_OK;
 }
 
@@ -930,9 +947,6 @@ lmoe_status latentmoe_routed_backward(const lmoe_dims* dims, const void* z, cons
   const size_t need = carve_routed_backward(p, nullptr, &w);
   if (!workspace || workspace_bytes < need)
     return fail(LMOE_ERR_WORKSPACE, "routed backward needs %zu workspace bytes", need);
-  // transposed segments are addressed with 32-bit row offsets
-  if ((int64_t)std::max(p.l, p.fr) * w.kpad * p.es >= ((int64_t)1 << 32))
-    return fail(LMOE_ERR_UNSUPPORTED, "too many pairs for the weight-gradient layout");
   carve_routed_backward(p, (char*)workspace, &w);
   hipStream_t st = launch_stream(stream);
   if (p.N == 0) {  // no pairs: every weight gradient is zero
