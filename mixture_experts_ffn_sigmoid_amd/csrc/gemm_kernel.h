@@ -460,7 +460,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
       });
       dma_step(clampt(kt + SA), ringA + (u % SA) * kStageA, clampt(kt + SB), ringB + (u % SB) * kStageB);
       sfor<NC - H>([&](auto c_c) { mfma_chunk(IntC<H + decltype(c_c)::value>{}); });
-      sched_interleave<(NC - H) * MPC, H * RPC, NI>();
+      // the next tile's reads first (phase 1 of the next step needs them at once),
+      // then the DMA spread over the MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, H * RPC, 0);
+      sched_interleave<(NC - H) * MPC, 0, NI>();
       __builtin_amdgcn_sched_barrier(0);
     };
     for (int kt = 0; kt < KT; kt += UNROLL) {

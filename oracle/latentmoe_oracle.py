@@ -408,3 +408,70 @@ def forward(x: np.ndarray, W: Weights, ids: np.ndarray | None = None, dense: boo
     s_sh = shared_sum(x, W.sh_g, W.sh_u, W.sh_o, W.beta1, W.beta2)
     y = s_sh + rmsnorm(u, W.rms_w, W.rms_eps) @ W.w_up.T
     return {"y": y, "z": z, "u": u, "s_sh": s_sh, "ids": ids, "p": p, "routes": r}
+
+
+def rmsnorm_backward(u: np.ndarray, w: np.ndarray, eps: float, dr: np.ndarray):
+    """Reverse-mode derivative of ``rmsnorm`` r = w u rho, rho = (mean(u^2) + eps)^(-1/2):
+    du_j = w_j dr_j rho - rho^3 u_j / l * sum_i dr_i w_i u_i,  dw = sum over rows of dr u rho."""
+    u = np.asarray(u, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    dr = np.asarray(dr, dtype=np.float64)
+    rho = 1.0 / np.sqrt(np.mean(u * u, axis=-1, keepdims=True) + eps)
+    dot = np.sum(dr * w * u, axis=-1, keepdims=True)
+    du = w * dr * rho - rho ** 3 * u * dot / u.shape[-1]
+    return du, np.sum(dr * u * rho, axis=0)
+
+
+def layer_backward(x: np.ndarray, W: Weights, dy: np.ndarray, ids: np.ndarray | None = None,
+                   want=None, only_want: bool = False) -> dict:
+    """Reverse-mode derivative of ``forward`` for an upstream gradient dy = dL/dy,
+    with the routes held fixed (TopK is piecewise constant; the bias only
+    selects and gets no gradient).  Step by step, last forward step first:
+      5. y = s_sh + W_up r:       dW_up = dy^T r, dr = dy W_up;  r = RMSNorm(u) -> du, drms_w
+      4. s_sh = sum_j S_o^j h_j:  dS_o^j = dy^T h_j, g_h = dy S_o^j, through SiTU to g_g, g_u:
+                                  dS_g^j = g_g^T x, dS_u^j = g_u^T x, dx += g_g S_g^j + g_u S_u^j
+      3. routed block:            ``routed_backward`` -> dz, dp, dW_g, dW_u, dW_o
+      2. p = s_T / sum_T s:       ds_i = (dp_i - sum_T p dp) / sum_T s on T (0 elsewhere),
+                                  dl = ds s (1 - s), dW_r = dl^T x, dx += dl W_r
+      1. z = W_down x:            dW_down = dz^T x, dx += dz W_down
+    ``want`` / ``only_want`` select routed experts as in ``routed_backward``
+    (with only_want, dx and the dense gradients miss the other experts' part)."""
+    x = np.asarray(x, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    f = forward(x, W, ids=ids)
+    ids, p, u, z = f["ids"], f["p"], f["u"], f["z"]
+    s = f["routes"].s
+    out = {}
+    rn = rmsnorm(u, W.rms_w, W.rms_eps)
+    out["w_up"] = dy.T @ rn
+    du, out["rms_w"] = rmsnorm_backward(u, W.rms_w, W.rms_eps, dy @ W.w_up)
+    dx = np.zeros_like(x)
+    gs = {"sh_g": np.zeros_like(W.sh_g), "sh_u": np.zeros_like(W.sh_u), "sh_o": np.zeros_like(W.sh_o)}
+    for j in range(W.sh_g.shape[0]):
+        a_g, a_u = x @ W.sh_g[j].T, x @ W.sh_u[j].T
+        h = situ_hidden(a_g, a_u, W.beta1, W.beta2)
+        gs["sh_o"][j] = dy.T @ h
+        g_h = dy @ W.sh_o[j]
+        dg, dgu = situ_hidden_grad(a_g, a_u, W.beta1, W.beta2)
+        g_g, g_u = g_h * dg, g_h * dgu
+        gs["sh_g"][j] = g_g.T @ x
+        gs["sh_u"][j] = g_u.T @ x
+        dx += g_g @ W.sh_g[j] + g_u @ W.sh_u[j]
+    out.update(gs)
+    rg = routed_backward(z, ids, p, W.experts, W.n_routed, W.beta1, W.beta2, du, want=want,
+                         only_want=only_want)
+    out["routed"] = rg.dw
+    dp = rg.dp
+    sel = np.take_along_axis(s, ids, axis=1)
+    S = sel.sum(axis=1, keepdims=True)
+    Sc = np.maximum(S, 1e-9)
+    ds_sel = dp / Sc - (S >= 1e-9) * np.sum(dp * sel, axis=1, keepdims=True) / (Sc * Sc)
+    dl = np.zeros_like(s)
+    np.put_along_axis(dl, ids, ds_sel * sel * (1.0 - sel), axis=1)
+    out["w_router"] = dl.T @ x
+    dx += dl @ W.w_router
+    out["w_down"] = rg.dz.T @ x
+    dx += rg.dz @ W.w_down
+    out["x"] = dx
+    out["dz"], out["du"], out["dl"] = rg.dz, du, dl
+    return out

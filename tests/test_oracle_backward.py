@@ -154,3 +154,103 @@ def test_only_want_restricts_to_wanted_experts():
     # dp of the wanted expert's pairs is complete, the others are left at zero
     mask = ids == e
     assert np.array_equal(only.dp[mask], full.dp[mask]) and np.all(only.dp[~mask] == 0)
+
+
+# ------------------------------------------------------------ whole layer
+
+
+def _tiny_layer(seed, d=10, ell=6, R=5, k=2, ns=2, fr=4, fs=7):
+    rng = np.random.default_rng(seed)
+    a = {
+        "w_down": rng.normal(size=(ell, d)) / np.sqrt(d),
+        "w_router": rng.normal(size=(R, d)) / np.sqrt(d),
+        "bias": rng.uniform(-0.05, 0.05, size=R),
+        "w_g": rng.normal(size=(R, fr, ell)) / np.sqrt(ell),
+        "w_u": rng.normal(size=(R, fr, ell)) / np.sqrt(ell),
+        "w_o": rng.normal(size=(R, ell, fr)) / np.sqrt(fr),
+        "sh_g": rng.normal(size=(ns, fs, d)) / np.sqrt(d),
+        "sh_u": rng.normal(size=(ns, fs, d)) / np.sqrt(d),
+        "sh_o": rng.normal(size=(ns, d, fs)) / np.sqrt(fs),
+        "w_up": rng.normal(size=(d, ell)) / np.sqrt(ell),
+        "rms_w": rng.uniform(0.5, 1.5, size=ell),
+    }
+    x = rng.normal(size=(6, d))
+    dy = rng.normal(size=(6, d))
+    return a, x, dy, k
+
+
+def test_rmsnorm_backward_equals_torch_autograd():
+    rng = np.random.default_rng(21)
+    u = torch.tensor(rng.normal(size=(5, 8)), dtype=torch.float64, requires_grad=True)
+    w = torch.tensor(rng.uniform(0.5, 1.5, 8), dtype=torch.float64, requires_grad=True)
+    dr = rng.normal(size=(5, 8))
+    r = torch.nn.functional.rms_norm(u, (8,), w, eps=1e-6)
+    (r * torch.as_tensor(dr)).sum().backward()
+    du, dw = O.rmsnorm_backward(u.detach().numpy(), w.detach().numpy(), 1e-6, dr)
+    np.testing.assert_allclose(du, u.grad.numpy(), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dw, w.grad.numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_layer_backward_matches_finite_differences():
+    a, x, dy, k = _tiny_layer(22)
+    W = O.weights_from_arrays(a, k)
+    ids = O.forward(x, W)["ids"]
+    g = O.layer_backward(x, W, dy, ids=ids)
+
+    def loss(aa, xx):
+        return float(np.sum(dy * O.forward(xx, O.weights_from_arrays(aa, k), ids=ids)["y"]))
+
+    rng = np.random.default_rng(23)
+    h = 1e-6
+    for _ in range(4):
+        i = tuple(rng.integers(0, s) for s in x.shape)
+        xp, xm = x.copy(), x.copy()
+        xp[i] += h
+        xm[i] -= h
+        assert abs((loss(a, xp) - loss(a, xm)) / (2 * h) - g["x"][i]) < 1e-6
+        for name in ("w_down", "w_router", "w_up", "rms_w", "sh_g", "sh_u", "sh_o", "w_g", "w_u", "w_o"):
+            arr = a[name]
+            i = tuple(rng.integers(0, s) for s in arr.shape)
+            ap, am = dict(a), dict(a)
+            ap[name], am[name] = arr.copy(), arr.copy()
+            ap[name][i] += h
+            am[name][i] -= h
+            fd = (loss(ap, x) - loss(am, x)) / (2 * h)
+            if name in ("w_g", "w_u", "w_o"):
+                got = g["routed"][i[0]][("w_g", "w_u", "w_o").index(name)][i[1:]]
+            else:
+                got = g[name][i]
+            assert abs(fd - got) < 1e-6, (name, fd, got)
+
+
+def test_layer_backward_equals_torch_autograd():
+    """The layer written with torch library ops (F.linear, sigmoid, a gather
+    over the fixed routes, SiTU, F.rms_norm) and differentiated by autograd."""
+    a, x, dy, k = _tiny_layer(24, R=6, k=3)
+    W = O.weights_from_arrays(a, k)
+    ids = O.forward(x, W)["ids"]
+    T = {n: torch.tensor(v, dtype=torch.float64, requires_grad=n != "bias") for n, v in a.items()}
+    xt = torch.tensor(x, dtype=torch.float64, requires_grad=True)
+    F = torch.nn.functional
+
+    def situ(v, g, u):
+        ag, au = F.linear(v, g), F.linear(v, u)
+        return (B1 * torch.tanh(ag / B1) * torch.sigmoid(ag)) * (B2 * torch.tanh(au / B2))
+
+    z = F.linear(xt, T["w_down"])
+    s = torch.sigmoid(F.linear(xt, T["w_router"]))
+    idt = torch.as_tensor(ids)
+    sel = torch.gather(s, 1, idt)
+    p = sel / sel.sum(1, keepdim=True)
+    outs = torch.stack([F.linear(situ(z, T["w_g"][e], T["w_u"][e]), T["w_o"][e]) for e in range(6)], 1)
+    u = sum(p[:, j:j + 1] * outs[torch.arange(x.shape[0]), idt[:, j]] for j in range(k))
+    s_sh = sum(F.linear(situ(xt, T["sh_g"][j], T["sh_u"][j]), T["sh_o"][j]) for j in range(2))
+    y = s_sh + F.linear(F.rms_norm(u, (u.shape[1],), T["rms_w"], eps=1e-6), T["w_up"])
+    (y * torch.as_tensor(dy)).sum().backward()
+    g = O.layer_backward(x, W, dy, ids=ids)
+    np.testing.assert_allclose(g["x"], xt.grad.numpy(), rtol=1e-10, atol=1e-12)
+    for n in ("w_down", "w_router", "w_up", "rms_w", "sh_g", "sh_u", "sh_o"):
+        np.testing.assert_allclose(g[n], T[n].grad.numpy(), rtol=1e-10, atol=1e-12, err_msg=n)
+    for e in range(6):
+        for j, n in enumerate(("w_g", "w_u", "w_o")):
+            np.testing.assert_allclose(g["routed"][e][j], T[n].grad[e].numpy(), rtol=1e-10, atol=1e-12)
