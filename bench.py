@@ -123,6 +123,55 @@ def backward_leg(cfg, ids, probs, steps: int, warmup: int):
     return out
 
 
+def layer_backward_leg(cfg, ids, probs, steps: int, warmup: int):
+    """Times latentmoe_backward (the whole layer: recomputed forward
+    quantities, every weight gradient and dx) on the routes of the forward
+    just run, with a seeded upstream gradient dy (generated in HBM)."""
+    import torch
+
+    import mixture_experts_ffn_sigmoid_amd as M
+
+    N, d, l, R, f, k = cfg.n_tokens, cfg.d_model, cfg.d_latent, cfg.n_routed, cfg.ff_routed, cfg.top_k
+    td = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    dev = S.gen.device_inputs(cfg)
+    dy = S.gen.device_tensor(cfg, "dy")
+    dx = torch.empty((N, d), dtype=torch.float32, device="cuda")
+    grads = {n: torch.empty_like(dev[n]) for n in ("w_down", "w_router", "w_g", "w_u", "w_o", "w_up")}
+    if cfg.n_shared:
+        grads.update({n: torch.empty_like(dev[n]) for n in ("sh_g", "sh_u", "sh_o")})
+    grads["rms_w"] = torch.empty((l,), dtype=torch.float32, device="cuda")
+    dims = M.dims_of(cfg)
+    ws = torch.empty(M.workspace_bytes(dims, M.ENTRY_BACKWARD), dtype=torch.uint8, device="cuda")
+
+    def call():
+        M.latentmoe_backward(dims, dev, dev["x"], ids, probs, dy, dx, grads, workspace=ws)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        call()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    P = N * k
+    nsf = cfg.n_shared * cfg.ff_shared
+    # backward products only (the forward's stored quantities are recomputed
+    # inside the call and not counted): dr and dh_shared, the routed block
+    # (dh 2, dz 4, weight gradients 6, x P l f), dx over [W_down; W_r; S_g; S_u],
+    # and the dense weight gradients (w_up, w_down, w_router, shared g/u/o)
+    flops = 2.0 * N * d * (l + nsf) + 12.0 * P * l * f + 2.0 * N * d * (l + R + 2 * nsf) \
+        + 2.0 * N * d * (2 * l + R + 3 * nsf)
+    out = {"ms": round(ms, 4), "tokens_per_s": round(N / ms * 1e3, 1), "tflops": round(flops / ms / 1e9, 1),
+           "algorithmic_flops": flops,
+           "note": "time includes recomputing z, logits, routed and shared forward quantities, and one host sync; algorithmic flops count the backward products only"}
+    del dev, dy, dx, grads, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 KERNEL_SOURCES = ("mixture_experts_ffn_sigmoid_amd/csrc/gemm_kernel.h",
                   "mixture_experts_ffn_sigmoid_amd/csrc/lmoe_common.h",
                   "mixture_experts_ffn_sigmoid_amd/csrc/route_kernels.h",
@@ -181,7 +230,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="k3full_n8192", choices=sorted(S.CONFIGS))
     ap.add_argument("--cpu-sample", type=int, default=24, help="tokens for the CPU oracle baseline (0: skip)")
-    ap.add_argument("--no-backward", action="store_true", help="skip the routed-block backward leg")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward legs (routed block and whole layer)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (FETCH_SIZE / WRITE_SIZE calibration)")
     args = ap.parse_args()
@@ -296,6 +345,7 @@ def main():
     }
     if not args.no_backward:
         out["routed_backward"] = backward_leg(cfg, bufs["ids"], bufs["probs"], max(2, args.steps // 4), 1)
+        out["layer_backward"] = layer_backward_leg(cfg, bufs["ids"], bufs["probs"], max(2, args.steps // 4), 1)
     if args.cpu_sample > 0:
         out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_sample)
     print(json.dumps(out), flush=True)

@@ -66,7 +66,8 @@ typedef enum {
   LMOE_ENTRY_DISPATCH = 1,
   LMOE_ENTRY_EXPERTS = 2,
   LMOE_ENTRY_FORWARD = 3,
-  LMOE_ENTRY_ROUTED_BACKWARD = 4
+  LMOE_ENTRY_ROUTED_BACKWARD = 4,
+  LMOE_ENTRY_BACKWARD = 5
 } lmoe_entry;
 
 /* Layer sizes (names after the chapter's component table). */
@@ -99,6 +100,21 @@ typedef struct {
   const float* rms_w;   /* [l] fp32        RMSNorm weight; NULL = ones */
   const void* w_up;     /* [d, l]          W_up */
 } lmoe_weights;
+
+/* Gradients of the layer's parameters (device pointers, caller-owned, the
+ * same shapes and dtypes as lmoe_weights; the bias gets none). */
+typedef struct {
+  void* w_down;   /* [l, d] */
+  void* w_router; /* [R, d] */
+  void* w_g;      /* [R, f_r, l] */
+  void* w_u;      /* [R, f_r, l] */
+  void* w_o;      /* [R, l, f_r] */
+  void* sh_g;     /* [n_s, f_s, d] (unused if n_s = 0) */
+  void* sh_u;     /* [n_s, f_s, d] */
+  void* sh_o;     /* [n_s, d, f_s] */
+  float* rms_w;   /* [l] fp32 */
+  void* w_up;     /* [d, l] */
+} lmoe_grads;
 
 /* Bytes of workspace an entry point needs for these dims. */
 size_t latentmoe_workspace_bytes(const lmoe_dims* dims, int32_t entry);
@@ -191,6 +207,28 @@ lmoe_status latentmoe_routed_backward(const lmoe_dims* dims, const void* z, cons
                                       const void* w_o, const float* du, float* dz, float* dprobs,
                                       void* dw_g, void* dw_u, void* dw_o, void* workspace,
                                       size_t workspace_bytes, void* stream);
+
+/* Backward of the whole layer (the five compute-flow steps differentiated in
+ * reverse order, routes held fixed: top-k is piecewise constant and the bias
+ * only selects) for an upstream gradient dy = dL/dy:
+ *   5. dW_up = dy^T r, dr = dy W_up; r = RMSNorm(u) -> du, drms_w
+ *   4. dS_o^j = dy^T h_j; through SiTU: dS_g^j, dS_u^j, dx += g_g S_g^j + g_u S_u^j
+ *   3. the routed block as in latentmoe_routed_backward -> dz, dprobs, dW_g, dW_u, dW_o
+ *   2. ds = (dp - sum_T p dp) / sum_T s on the selected experts, dl = ds s (1 - s),
+ *      dW_r = dl^T x, dx += dl W_r
+ *   1. dW_down = dz^T x, dx += dz W_down
+ * Inputs: x [N, d] and dy [N, d] in the storage dtype; ids [N, k] and probs
+ * [N, k] as returned by latentmoe_forward for this x.  Outputs: dx [N, d]
+ * fp32 and every parameter gradient in `grads` (storage dtype, rms_w fp32;
+ * fp32 accumulation, one rounding).  The forward quantities (z, u, the shared
+ * pre-activations) are recomputed.  Reads C back once; otherwise
+ * asynchronous.  Workspace: latentmoe_workspace_bytes(dims,
+ * LMOE_ENTRY_BACKWARD) bytes of device memory.  Errors: INVALID_ARGUMENT for
+ * bad dims, NULL pointers or ids outside [0, R); WORKSPACE. */
+lmoe_status latentmoe_backward(const lmoe_dims* dims, const lmoe_weights* weights, const void* x,
+                               const int32_t* ids, const float* probs, const void* dy, float* dx,
+                               const lmoe_grads* grads, void* workspace, size_t workspace_bytes,
+                               void* stream);
 
 /* Legacy router that the K3 sigmoid router replaced (compare page, forward
  * hunk of latent_moe.py): ids = the k largest raw logits = W_r x (equal values:

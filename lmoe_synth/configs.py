@@ -90,8 +90,8 @@ CONFIGS: dict[str, LayerConfig] = {
 TENSOR_IDS = {
     "x": 1, "w_down": 2, "w_router": 3, "w_g": 4, "w_u": 5, "w_o": 6,
     "sh_g": 7, "sh_u": 8, "sh_o": 9, "w_up": 10, "bias": 11,
-    # inputs of the routed-block backward: a latent z and an upstream gradient du
-    "z": 12, "du": 13,
+    # inputs of the backward: a latent z and upstream gradients du (routed block), dy (layer)
+    "z": 12, "du": 13, "dy": 14,
 }
 
 
@@ -123,6 +123,7 @@ def tensor_spec(cfg: LayerConfig, name: str):
         "rms_w": ((l,), "f32", None),
         "z": ((N, l), dt, 1.0),
         "du": ((N, l), "f32", 1.0),
+        "dy": ((N, d), dt, 1.0),
     }
     shape, sdt, scale = table[name]
     if name == "w_router" and cfg.router_skew_rows > 0:

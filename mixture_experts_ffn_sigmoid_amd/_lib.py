@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "liblatentmoe.so")
 
 LMOE_F32, LMOE_BF16 = 0, 1
-ENTRY_ROUTE, ENTRY_DISPATCH, ENTRY_EXPERTS, ENTRY_FORWARD, ENTRY_ROUTED_BACKWARD = 0, 1, 2, 3, 4
+ENTRY_ROUTE, ENTRY_DISPATCH, ENTRY_EXPERTS, ENTRY_FORWARD, ENTRY_ROUTED_BACKWARD, ENTRY_BACKWARD = 0, 1, 2, 3, 4, 5
 STATUS = {0: "OK", 1: "INVALID_ARGUMENT", 2: "UNSUPPORTED", 3: "CAPACITY", 4: "WORKSPACE", 5: "HIP"}
 
 # every symbol include/latentmoe.h declares
@@ -21,8 +21,9 @@ EXPORTS = (
     "latentmoe_workspace_bytes", "latentmoe_status_string", "latentmoe_last_error",
     "latentmoe_route", "latentmoe_dispatch", "latentmoe_experts", "latentmoe_forward",
     "latentmoe_forward_timed", "latentmoe_route_softmax", "latentmoe_router_losses_workspace_bytes",
-    "latentmoe_router_losses", "latentmoe_routed_backward",
+    "latentmoe_router_losses", "latentmoe_routed_backward", "latentmoe_backward",
 )
+GRAD_NAMES = ("w_down", "w_router", "w_g", "w_u", "w_o", "sh_g", "sh_u", "sh_o", "rms_w", "w_up")
 TIMING_EVENTS = 9
 STEP_NAMES = ("latent_gemm", "router", "dispatch", "shared_gateup", "routed_gateup", "routed_down",
               "combine_rmsnorm", "merge_gemm")
@@ -41,6 +42,10 @@ class Dims(ctypes.Structure):
         ("ff_routed", ctypes.c_int32), ("ff_shared", ctypes.c_int32), ("beta1", ctypes.c_float),
         ("beta2", ctypes.c_float), ("rms_eps", ctypes.c_float), ("dtype", ctypes.c_int32),
     ]
+
+
+class Grads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in GRAD_NAMES]
 
 
 class Weights(ctypes.Structure):
@@ -78,9 +83,11 @@ def load() -> ctypes.CDLL:
     lib.latentmoe_router_losses_workspace_bytes.restype = st
     lib.latentmoe_router_losses.argtypes = [D, vp, vp, vp, vp, st, vp]
     lib.latentmoe_routed_backward.argtypes = [D] + [vp] * 13 + [st, vp]
+    lib.latentmoe_backward.argtypes = [D, ctypes.POINTER(Weights), vp, vp, vp, vp, vp, ctypes.POINTER(Grads), vp,
+                                       st, vp]
     for fn in ("latentmoe_route", "latentmoe_dispatch", "latentmoe_experts", "latentmoe_forward",
                "latentmoe_forward_timed", "latentmoe_route_softmax", "latentmoe_router_losses",
-               "latentmoe_routed_backward"):
+               "latentmoe_routed_backward", "latentmoe_backward"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -159,6 +166,16 @@ def latentmoe_routed_backward(dims, z, ids, probs, w_g, w_u, w_o, du, dz, dprobs
                                            ptr(w_o), ptr(du), ptr(dz), ptr(dprobs), ptr(dw_g), ptr(dw_u),
                                            ptr(dw_o), ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
                                            stream_handle(stream)))
+
+
+def latentmoe_backward(dims, weights, x, ids, probs, dy, dx, grads: dict, workspace=None, stream=None):
+    """grads: dict of output tensors keyed by GRAD_NAMES (sh_* may be absent when n_s = 0)."""
+    W = weights if isinstance(weights, Weights) else weights_struct(weights)
+    G = Grads(*[ptr(grads.get(n)) for n in GRAD_NAMES])
+    ws = workspace
+    check(load().latentmoe_backward(ctypes.byref(dims), ctypes.byref(W), ptr(x), ptr(ids), ptr(probs), ptr(dy),
+                                    ptr(dx), ctypes.byref(G), ptr(ws),
+                                    0 if ws is None else ws.numel() * ws.element_size(), stream_handle(stream)))
 
 
 def latentmoe_dispatch(dims, ids, z, counts, offsets, order, padded=None, capacity=0,

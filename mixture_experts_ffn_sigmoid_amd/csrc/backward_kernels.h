@@ -185,11 +185,13 @@ __global__ __launch_bounds__(256) void pair_grad_kernel(const float* __restrict_
 //   dg = dh * G'(g) U(u),  du = dh * G(g) U'(u)
 //   G'(a) = (1 - tanh(a/b1)^2) sigmoid(a) + b1 tanh(a/b1) sigmoid(a) (1 - sigmoid(a)),
 //   U'(a) = 1 - tanh(a/b2)^2.
-// Row q of dgu holds [dg | du] (f columns each); n = pairs * f elements.
+// Row q of dgu (leading dimension ld, starting at column col0) holds
+// [dg | du] (f columns each); n = rows * f elements.
 template <typename TD>
 __global__ __launch_bounds__(256) void situ_backward_kernel(const float* __restrict__ dh, const float* __restrict__ g,
                                                             const float* __restrict__ u, int64_t n, int f,
-                                                            float beta1, float beta2, TD* __restrict__ dgu) {
+                                                            float beta1, float beta2, TD* __restrict__ dgu,
+                                                            int64_t ld, int64_t col0) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
     const float a = g[i], b = u[i], d = dh[i];
     const float tg = tanhf(a / beta1), tu = tanhf(b / beta2);
@@ -198,8 +200,8 @@ __global__ __launch_bounds__(256) void situ_backward_kernel(const float* __restr
     const float dgate = (1.0f - tg * tg) * sg + beta1 * tg * sg * (1.0f - sg);
     const float dup = 1.0f - tu * tu;
     const int64_t q = i / f, j = i - q * f;
-    Elem<TD>::store(dgu + q * 2 * f + j, d * dgate * up);
-    Elem<TD>::store(dgu + q * 2 * f + f + j, d * gate * dup);
+    Elem<TD>::store(dgu + q * ld + col0 + j, d * dgate * up);
+    Elem<TD>::store(dgu + q * ld + col0 + f + j, d * gate * dup);
   }
 }
 
@@ -210,14 +212,115 @@ __global__ __launch_bounds__(256) void inverse_order_kernel(const int32_t* __res
   if (i < pairs) inv[order[i]] = (int32_t)i;
 }
 
-// dz[n] = sum over slots j (in slot order) of rows[inv[n k + j]], one workgroup per token.
+// dz[n] (row stride ld) = sum over slots j (in slot order) of rows[inv[n k + j]],
+// one workgroup per token.
+template <typename TD>
 __global__ __launch_bounds__(256) void pair_sum_kernel(const float* __restrict__ rows, const int32_t* __restrict__ inv,
-                                                       int top_k, int ell, float* __restrict__ dz) {
+                                                       int top_k, int ell, TD* __restrict__ dz, int64_t ld) {
   const int64_t n = blockIdx.x;
   for (int c = threadIdx.x; c < ell; c += 256) {
     float acc = 0.f;
     for (int j = 0; j < top_k; ++j) acc += rows[(int64_t)inv[n * top_k + j] * ell + c];
-    dz[n * ell + c] = acc;
+    Elem<TD>::store(dz + n * ld + c, acc);
+  }
+}
+
+// RMSNorm backward, one workgroup per token (r = w u rho, rho = (mean(u^2) + eps)^(-1/2);
+// w NULL = ones):
+//   du_j = w_j dr_j rho - rho^3 u_j / l * sum_i dr_i w_i u_i ;  rho_out[n] = rho
+__global__ __launch_bounds__(256) void rmsnorm_backward_kernel(const float* __restrict__ u, const float* __restrict__ dr,
+                                                               const float* __restrict__ w, int ell, float eps,
+                                                               float* __restrict__ du, float* __restrict__ rho_out) {
+  const int64_t n = blockIdx.x;
+  const float* ur = u + n * ell;
+  const float* dr_r = dr + n * ell;
+  float ss = 0.f, dot = 0.f;
+  for (int c = threadIdx.x; c < ell; c += 256) {
+    const float v = ur[c];
+    ss += v * v;
+    dot += dr_r[c] * (w ? w[c] : 1.f) * v;
+  }
+  __shared__ float red[2][4];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    ss += __shfl_xor(ss, off);
+    dot += __shfl_xor(dot, off);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    red[0][threadIdx.x >> 6] = ss;
+    red[1][threadIdx.x >> 6] = dot;
+  }
+  __syncthreads();
+  ss = (red[0][0] + red[0][1]) + (red[0][2] + red[0][3]);
+  dot = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
+  const float rho = 1.0f / sqrtf(ss / ell + eps);
+  const float c3 = rho * rho * rho * dot / ell;
+  for (int c = threadIdx.x; c < ell; c += 256) du[n * ell + c] = (w ? w[c] : 1.f) * dr_r[c] * rho - c3 * ur[c];
+  if (threadIdx.x == 0) rho_out[n] = rho;
+}
+
+// dw[c] = sum over tokens n (in order) of dr[n, c] u[n, c] rho[n]; one thread per column.
+__global__ __launch_bounds__(256) void rmsnorm_wgrad_kernel(const float* __restrict__ u, const float* __restrict__ dr,
+                                                            const float* __restrict__ rho, int64_t N, int ell,
+                                                            float* __restrict__ dw) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= ell) return;
+  float acc = 0.f;
+  for (int64_t n = 0; n < N; ++n) acc += dr[n * ell + c] * u[n * ell + c] * rho[n];
+  dw[c] = acc;
+}
+
+// Router backward, one wave per token: with s = sigmoid(logits) at the token's
+// k selected experts, S = sum s and p = s / S,
+//   ds_i = dp_i / S - (sum_j dp_j s_j) / S^2   (ds = dp / 1e-9 under the clamp S < 1e-9)
+//   dl_i = ds_i s_i (1 - s_i)
+// The dl row (leading dimension ld, R columns plus zero padding up to rpad) is
+// zero except at the selected experts.
+template <typename TD>
+__global__ __launch_bounds__(256) void router_backward_kernel(const float* __restrict__ logits,
+                                                              const int32_t* __restrict__ ids,
+                                                              const float* __restrict__ dprobs, int64_t N, int R,
+                                                              int k, int rpad, TD* __restrict__ dl, int64_t ld) {
+  const int lane = threadIdx.x & 63;
+  const int64_t n = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (n >= N) return;
+  TD* row = dl + n * ld;
+  float s = 0.f, dp = 0.f;
+  int e = 0;
+  if (lane < k) {
+    e = ids[n * k + lane];
+    s = 1.0f / (1.0f + expf(-logits[n * R + e]));
+    dp = dprobs[n * k + lane];
+  }
+  float S = s, dot = dp * s;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    S += __shfl_xor(S, off);
+    dot += __shfl_xor(dot, off);
+  }
+  const float Sc = fmaxf(S, 1e-9f);
+  const float ds = dp / Sc - (S >= 1e-9f ? dot / (Sc * Sc) : 0.f);
+  const float g = lane < k ? ds * s * (1.0f - s) : 0.f;
+  // every column written once: the selected experts' dl, zero elsewhere
+  for (int c0 = 0; c0 < rpad; c0 += 64) {
+    const int c = c0 + lane;
+    float v = 0.f;
+    for (int j = 0; j < k; ++j) {
+      const int ej = __shfl(e, j);
+      const float gj = __shfl(g, j);
+      if (ej == c) v = gj;
+    }
+    if (c < rpad) Elem<TD>::store(row + c, v);
+  }
+}
+
+// Four ints into device memory (parameters of a one-segment transpose).
+__global__ void set_ints_kernel(int32_t* __restrict__ p, int32_t a, int32_t b, int32_t c, int32_t d) {
+  if (threadIdx.x == 0) {
+    p[0] = a;
+    p[1] = b;
+    p[2] = c;
+    p[3] = d;
   }
 }
 

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <type_traits>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -229,6 +230,57 @@ size_t carve_routed_backward(const Plan& p, char* b, RoutedBwdWs* w) {
   return c.off;
 }
 
+// Whole-layer backward: the routed block's workspace plus the dense parts.
+// dcat [N, kcat] = [dz | dl (R padded to rpad) | dg_shared | du_shared] feeds
+// one K-segmented product for dx; the [cols, npad] transposes (N zero-padded
+// to a multiple of 64) feed the dense weight gradients.
+struct LayerBwdWs {
+  RoutedBwdWs rw;
+  int64_t rpad, nsf, kcat, npad;
+  char *z, *rn, *hs, *dcat;            // intermediate type
+  float *logits, *u, *ag, *au, *dr, *dhs, *du, *rho, *dprobs;
+  char *w_upT, *shoT, *w_downT, *w_rT, *sgT, *suT;  // storage type
+  int32_t* seg;
+  char *dyT, *rnT, *hsT, *dcatT, *xT;  // intermediate type
+};
+size_t carve_layer_backward(const Plan& p, char* b, LayerBwdWs* w) {
+  Carver c{b};
+  const size_t rsz = carve_routed_backward(p, nullptr, &w->rw);
+  char* rbase = c.take<char>(rsz);
+  if (b) carve_routed_backward(p, rbase, &w->rw);
+  const int64_t N = p.N, ei = p.es, es = p.es;
+  w->rpad = (p.R + 63) / 64 * 64;
+  w->nsf = (int64_t)p.ns * p.fs;
+  w->kcat = p.l + w->rpad + 2 * w->nsf;
+  w->npad = (N + 63) / 64 * 64;
+  w->z = c.take<char>((size_t)N * p.l * ei);
+  w->rn = c.take<char>((size_t)N * p.l * ei);
+  w->hs = c.take<char>((size_t)N * w->nsf * ei);
+  w->dcat = c.take<char>((size_t)N * w->kcat * ei);
+  w->logits = c.take<float>((size_t)N * p.R * 4);
+  w->u = c.take<float>((size_t)N * p.l * 4);
+  w->ag = c.take<float>((size_t)N * w->nsf * 4);
+  w->au = c.take<float>((size_t)N * w->nsf * 4);
+  w->dr = c.take<float>((size_t)N * p.l * 4);
+  w->dhs = c.take<float>((size_t)N * w->nsf * 4);
+  w->du = c.take<float>((size_t)N * p.l * 4);
+  w->rho = c.take<float>((size_t)N * 4);
+  w->dprobs = c.take<float>((size_t)N * p.k * 4);
+  w->w_upT = c.take<char>((size_t)p.l * p.d * es);
+  w->shoT = c.take<char>((size_t)w->nsf * p.d * es);
+  w->w_downT = c.take<char>((size_t)p.d * p.l * es);
+  w->w_rT = c.take<char>((size_t)p.d * w->rpad * es);
+  w->sgT = c.take<char>((size_t)p.d * w->nsf * es);
+  w->suT = c.take<char>((size_t)p.d * w->nsf * es);
+  w->seg = c.take<int32_t>(16);
+  w->dyT = c.take<char>((size_t)p.d * w->npad * ei);
+  w->rnT = c.take<char>((size_t)p.l * w->npad * ei);
+  w->hsT = c.take<char>((size_t)w->nsf * w->npad * ei);
+  w->dcatT = c.take<char>((size_t)w->kcat * w->npad * ei);
+  w->xT = c.take<char>((size_t)p.d * w->npad * ei);
+  return c.off;
+}
+
 // Largest batch whose shared-expert GEMM runs on the second stream.
 constexpr int64_t kOverlapMaxTokens = 2048;
 
@@ -446,11 +498,12 @@ lmoe_status transpose_batched(const T* in, int64_t in_bstride, int ld_in, int ro
 
 // Routed-block backward (see latentmoe_routed_backward).  T: storage type of
 // z, the weights and the weight gradients; TI: intermediate type.
-template <typename T, typename TI>
+// TZ: type of z; dz is written as TDZ with row stride ld_dz.
+template <typename T, typename TI, typename TZ, typename TDZ>
 lmoe_status run_routed_backward(const Plan& p, const lmoe_dims* dm, const void* z, const int32_t* ids,
                                 const float* probs, const void* w_g, const void* w_u, const void* w_o,
-                                const float* du, float* dz, float* dprobs, void* dw_g, void* dw_u,
-                                void* dw_o, const RoutedBwdWs& w, hipStream_t st) {
+                                const float* du, void* dz, int64_t ld_dz, float* dprobs, void* dw_g,
+                                void* dw_u, void* dw_o, const RoutedBwdWs& w, hipStream_t st) {
   const int64_t P = p.pairs;
   const int f = p.fr, l = p.l, R = p.R;
   const int64_t es = sizeof(T), ei = sizeof(TI);
@@ -492,10 +545,11 @@ lmoe_status run_routed_backward(const Plan& p, const lmoe_dims* dm, const void* 
     return g;
   };
   // 2. pre-activations of every pair: g = z W_g^T, up = z W_u^T (fp32, sorted rows)
-  LMOE_TRY((gemm<T, T, float, A_GATHER, B_SINGLE, E_STORE>(
-      grouped(z, l * es, w_g, l * es, (int64_t)f * l * es, f, l, w.g, (int64_t)f * 4), tile, st)));
-  LMOE_TRY((gemm<T, T, float, A_GATHER, B_SINGLE, E_STORE>(
-      grouped(z, l * es, w_u, l * es, (int64_t)f * l * es, f, l, w.up, (int64_t)f * 4), tile, st)));
+  const int64_t ez = sizeof(TZ);
+  LMOE_TRY((gemm<TZ, T, float, A_GATHER, B_SINGLE, E_STORE>(
+      grouped(z, l * ez, w_g, l * es, (int64_t)f * l * es, f, l, w.g, (int64_t)f * 4), tile, st)));
+  LMOE_TRY((gemm<TZ, T, float, A_GATHER, B_SINGLE, E_STORE>(
+      grouped(z, l * ez, w_u, l * es, (int64_t)f * l * es, f, l, w.up, (int64_t)f * 4), tile, st)));
   situ_hidden_kernel<TI><<<blocks(P * f), 256, 0, st>>>(w.g, w.up, P * f, dm->beta1, dm->beta2, (TI*)w.hs);
   LMOE_HIP(hipGetLastError());
   // 3. expert outputs o = h W_o^T (fp32), then dprobs and dout = p * du (sorted rows)
@@ -509,7 +563,7 @@ lmoe_status run_routed_backward(const Plan& p, const lmoe_dims* dm, const void* 
   LMOE_TRY((gemm<TI, T, float, A_SORTED, B_SINGLE, E_STORE>(
       grouped(w.dout, l * ei, w.w_oT, l * es, (int64_t)f * l * es, f, l, w.dh, (int64_t)f * 4), tile, st)));
   situ_backward_kernel<TI><<<blocks(P * f), 256, 0, st>>>(w.dh, w.g, w.up, P * f, f, dm->beta1, dm->beta2,
-                                                          (TI*)w.dgu);
+                                                          (TI*)w.dgu, 2 * (int64_t)f, 0);
   LMOE_HIP(hipGetLastError());
   // 5. dz rows = [dg | du] [W_g | W_u] (through [W_g^T | W_u^T] [R, l, 2f]), summed per token
   LMOE_TRY(transpose_batched<T>((const T*)w_g, (int64_t)f * l, l, f, l, (T*)w.w_guT, (int64_t)l * 2 * f, 2 * f,
@@ -521,7 +575,7 @@ lmoe_status run_routed_backward(const Plan& p, const lmoe_dims* dm, const void* 
       grouped(w.dgu, 2 * f * ei, w.w_guT, 2 * f * es, (int64_t)l * 2 * f * es, l, 2 * f, dzrows,
               (int64_t)l * 4),
       tile, st)));
-  pair_sum_kernel<<<(unsigned)p.N, 256, 0, st>>>(dzrows, w.inv, p.k, l, dz);
+  pair_sum_kernel<TDZ><<<(unsigned)p.N, 256, 0, st>>>(dzrows, w.inv, p.k, l, (TDZ*)dz, ld_dz);
   LMOE_HIP(hipGetLastError());
   // 6. weight gradients: per expert, products over its pairs (K = padded pair range)
   const unsigned ysegs = (unsigned)((C + 63) / 64);
@@ -538,8 +592,8 @@ lmoe_status run_routed_backward(const Plan& p, const lmoe_dims* dm, const void* 
     segment_transpose_kernel<TI, TI><<<dim3(f / 64, ysegs, R), 256, 0, st>>>(
         (const TI*)w.dgu, 2 * f, f, f, w.counts, w.offsets, nullptr, p.k, w.kr_off, w.kr_len, (TI*)w.duT);
     LMOE_HIP(hipGetLastError());
-    segment_transpose_kernel<T, TI><<<dim3(l / 64, ysegs, R), 256, 0, st>>>(
-        (const T*)z, l, 0, l, w.counts, w.offsets, w.order, p.k, w.kr_off, w.kr_len, (TI*)w.zT);
+    segment_transpose_kernel<TZ, TI><<<dim3(l / 64, ysegs, R), 256, 0, st>>>(
+        (const TZ*)z, l, 0, l, w.counts, w.offsets, w.order, p.k, w.kr_off, w.kr_len, (TI*)w.zT);
     LMOE_HIP(hipGetLastError());
   }
   auto batched = [&](const char* a, int M, const char* b, int N, void* out) {
@@ -562,6 +616,143 @@ lmoe_status run_routed_backward(const Plan& p, const lmoe_dims* dm, const void* 
   LMOE_TRY((gemm<TI, TI, T, A_KBATCH, B_SINGLE, E_STORE>(batched(w.doutT, l, w.hT, f, dw_o), kWgradTile, st)));
   LMOE_TRY((gemm<TI, TI, T, A_KBATCH, B_SINGLE, E_STORE>(batched(w.dgT, f, w.zT, l, dw_g), kWgradTile, st)));
   LMOE_TRY((gemm<TI, TI, T, A_KBATCH, B_SINGLE, E_STORE>(batched(w.duT, f, w.zT, l, dw_u), kWgradTile, st)));
+  return LMOE_OK;
+}
+
+// Whole-layer backward (see latentmoe_backward).  T: storage type; TI: intermediate type.
+template <typename T, typename TI>
+lmoe_status run_layer_backward(const Plan& p, const lmoe_dims* dm, const lmoe_weights* W, const void* x,
+                               const int32_t* ids, const float* probs, const void* dy, float* dx,
+                               const lmoe_grads* G, const LayerBwdWs& w, hipStream_t st) {
+  const int64_t N = p.N, es = sizeof(T), ei = sizeof(TI);
+  const int d = p.d, l = p.l, R = p.R;
+  const int nsf = (int)w.nsf, rpad = (int)w.rpad;
+  const int64_t kcat = w.kcat, npad = w.npad;
+  auto blocks = [](int64_t n) { return (unsigned)std::min<int64_t>((n + 255) / 256, 65536); };
+  auto dense = [&](const void* a, int64_t lda, int M, const void* b, int64_t ldb, int Ncols, int K, void* out,
+                   int64_t ldo) {
+    GemmArgs g = base_args(dm);
+    g.M = M;
+    g.N = Ncols;
+    g.K = K;
+    g.a = (const char*)a;
+    g.lda = lda;
+    g.b0 = (const char*)b;
+    g.ldb = ldb;
+    g.nb_rows = Ncols;
+    g.out = (char*)out;
+    g.ldo = ldo;
+    return g;
+  };
+  // ---- recompute the forward quantities the gradients need
+  LMOE_TRY((gemm<T, T, TI, A_DENSE, B_SINGLE, E_STORE>(dense(x, d * es, (int)N, W->w_down, d * es, l, d, w.z, l * ei),
+                                                       dense_tile(N, l, false), st)));
+  LMOE_TRY((gemm<T, T, float, A_DENSE, B_SINGLE, E_STORE>(
+      dense(x, d * es, (int)N, W->w_router, d * es, R, d, w.logits, (int64_t)R * 4), dense_tile(N, R, false), st)));
+  const RoutedBwdWs& rw = w.rw;
+  LMOE_TRY(run_dispatch(p, ids, rw.chunk_hist, rw.chunk_bad, rw.counts, rw.offsets, rw.order, rw.meta, st));
+  LMOE_TRY((run_experts<TI, T, TI, A_GATHER>(p, dm, w.z, 0, rw.counts, rw.offsets, rw.order, probs, W->w_g,
+                                             W->w_u, W->w_o, rw.tile_list, rw.meta, rw.hs, rw.dout, st)));
+  combine_rmsnorm_kernel<TI, TI><<<(unsigned)N, 256, 0, st>>>((const TI*)rw.dout, p.k, l, w.u, W->rms_w,
+                                                              dm->rms_eps, (TI*)w.rn, l);
+  LMOE_HIP(hipGetLastError());
+  if (nsf > 0) {
+    LMOE_TRY((gemm<T, T, float, A_DENSE, B_SINGLE, E_STORE>(
+        dense(x, d * es, (int)N, W->sh_g, d * es, nsf, d, w.ag, (int64_t)nsf * 4), dense_tile(N, nsf, false), st)));
+    LMOE_TRY((gemm<T, T, float, A_DENSE, B_SINGLE, E_STORE>(
+        dense(x, d * es, (int)N, W->sh_u, d * es, nsf, d, w.au, (int64_t)nsf * 4), dense_tile(N, nsf, false), st)));
+    situ_hidden_kernel<TI><<<blocks(N * nsf), 256, 0, st>>>(w.ag, w.au, N * nsf, dm->beta1, dm->beta2, (TI*)w.hs);
+    LMOE_HIP(hipGetLastError());
+  }
+  // ---- step 5 backward: dr = dy W_up, dh_shared = dy [S_o^j], RMSNorm backward
+  LMOE_TRY(transpose_batched<T>((const T*)W->w_up, 0, l, d, l, (T*)w.w_upT, 0, d, 0, 1, nullptr, st));
+  LMOE_TRY((gemm<T, T, float, A_DENSE, B_SINGLE, E_STORE>(dense(dy, d * es, (int)N, w.w_upT, d * es, l, d, w.dr,
+                                                                (int64_t)l * 4),
+                                                          dense_tile(N, l, false), st)));
+  rmsnorm_backward_kernel<<<(unsigned)N, 256, 0, st>>>(w.u, w.dr, W->rms_w, l, dm->rms_eps, w.du, w.rho);
+  LMOE_HIP(hipGetLastError());
+  rmsnorm_wgrad_kernel<<<(unsigned)((l + 255) / 256), 256, 0, st>>>(w.u, w.dr, w.rho, N, l, G->rms_w);
+  LMOE_HIP(hipGetLastError());
+  if (nsf > 0) {
+    LMOE_TRY(transpose_batched<T>((const T*)W->sh_o, (int64_t)d * p.fs, p.fs, d, p.fs, (T*)w.shoT,
+                                   (int64_t)p.fs * d, d, 0, p.ns, nullptr, st));
+    LMOE_TRY((gemm<T, T, float, A_DENSE, B_SINGLE, E_STORE>(dense(dy, d * es, (int)N, w.shoT, d * es, nsf, d,
+                                                                  w.dhs, (int64_t)nsf * 4),
+                                                            dense_tile(N, nsf, false), st)));
+    situ_backward_kernel<TI><<<blocks(N * nsf), 256, 0, st>>>(w.dhs, w.ag, w.au, N * nsf, nsf, dm->beta1,
+                                                              dm->beta2, (TI*)w.dcat, kcat, l + rpad);
+    LMOE_HIP(hipGetLastError());
+  }
+  // ---- step 3 backward (routed block) -> dz into dcat[:, :l], dprobs
+  LMOE_TRY((run_routed_backward<T, TI, TI, TI>(p, dm, w.z, ids, probs, W->w_g, W->w_u, W->w_o, w.du, w.dcat,
+                                               kcat, w.dprobs, G->w_g, G->w_u, G->w_o, rw, st)));
+  // ---- step 2 backward -> dl into dcat[:, l:l+rpad]
+  router_backward_kernel<TI><<<(unsigned)((N + 3) / 4), 256, 0, st>>>(w.logits, ids, w.dprobs, N, R, p.k, rpad,
+                                                                      (TI*)w.dcat + l, kcat);
+  LMOE_HIP(hipGetLastError());
+  // ---- dx = [dz | dl | dg_sh | du_sh] [W_down ; W_r ; S_g ; S_u]  (K-segmented, transposed weights)
+  LMOE_TRY(transpose_batched<T>((const T*)W->w_down, 0, d, l, d, (T*)w.w_downT, 0, l, 0, 1, nullptr, st));
+  zero_words_kernel<<<256, 256, 0, st>>>((uint32_t*)w.w_rT, (int64_t)d * rpad * es / 4);
+  LMOE_HIP(hipGetLastError());
+  LMOE_TRY(transpose_batched<T>((const T*)W->w_router, 0, d, R, d, (T*)w.w_rT, 0, rpad, 0, 1, nullptr, st));
+  GemmArgs f = base_args(dm);
+  f.M = (int)N;
+  f.N = d;
+  f.K = (int)kcat;
+  f.a = w.dcat;
+  f.lda = kcat * ei;
+  f.nb_rows = d;
+  f.nseg = 0;
+  auto seg = [&](const char* base, int64_t kseg, int64_t k0) {
+    f.seg_base[f.nseg] = base;
+    f.seg_ld[f.nseg] = kseg * es;
+    f.seg_kt0[f.nseg] = (int)(k0 * ei / kSegUnit);
+    ++f.nseg;
+  };
+  seg(w.w_downT, l, 0);
+  seg(w.w_rT, rpad, l);
+  if (nsf > 0) {
+    LMOE_TRY(transpose_batched<T>((const T*)W->sh_g, 0, d, nsf, d, (T*)w.sgT, 0, nsf, 0, 1, nullptr, st));
+    LMOE_TRY(transpose_batched<T>((const T*)W->sh_u, 0, d, nsf, d, (T*)w.suT, 0, nsf, 0, 1, nullptr, st));
+    seg(w.sgT, nsf, l + rpad);
+    seg(w.suT, nsf, l + rpad + nsf);
+  }
+  f.seg_kt0[f.nseg] = (int)(kcat * ei / kSegUnit);
+  f.out = (char*)dx;
+  f.ldo = (int64_t)d * 4;
+  LMOE_TRY((gemm<TI, T, float, A_DENSE, B_KSEG, E_STORE>(f, dense_tile(N, d, false), st)));
+  // ---- dense weight gradients: products over tokens (K = npad, zero-padded transposes)
+  set_ints_kernel<<<1, 64, 0, st>>>(w.seg, (int32_t)N, 0, 0, (int32_t)npad);
+  LMOE_HIP(hipGetLastError());
+  const int32_t *cnt = w.seg, *off = w.seg + 1, *kro = w.seg + 2, *krl = w.seg + 3;
+  const unsigned ny = (unsigned)(npad / 64);
+  auto tr = [&](auto src_c, int64_t ld_src, int64_t col0, int ncols, char* out) -> lmoe_status {
+    using TS = std::remove_const_t<std::remove_pointer_t<decltype(src_c)>>;
+    segment_transpose_kernel<TS, TI><<<dim3((ncols + 63) / 64, ny, 1), 256, 0, st>>>(
+        src_c, ld_src, (int)col0, ncols, cnt, off, nullptr, 1, kro, krl, (TI*)out);
+    LMOE_HIP(hipGetLastError());
+    return LMOE_OK;
+  };
+  LMOE_TRY(tr((const T*)dy, d, 0, d, w.dyT));
+  LMOE_TRY(tr((const TI*)w.rn, l, 0, l, w.rnT));
+  LMOE_TRY(tr((const TI*)w.dcat, kcat, 0, (int)kcat, w.dcatT));
+  LMOE_TRY(tr((const T*)x, d, 0, d, w.xT));
+  const int64_t ldt = npad * ei;
+  auto wgrad = [&](const char* a, int M, const char* b, int Ncols, void* out) {
+    return gemm<TI, TI, T, A_DENSE, B_SINGLE, E_STORE>(dense(a, ldt, M, b, ldt, Ncols, (int)npad, out,
+                                                             (int64_t)Ncols * es),
+                                                       dense_tile(M, Ncols, false), st);
+  };
+  LMOE_TRY(wgrad(w.dyT, d, w.rnT, l, G->w_up));
+  LMOE_TRY(wgrad(w.dcatT, l, w.xT, d, G->w_down));
+  LMOE_TRY(wgrad(w.dcatT + (int64_t)l * ldt, R, w.xT, d, G->w_router));
+  if (nsf > 0) {
+    LMOE_TRY(tr((const TI*)w.hs, nsf, 0, nsf, w.hsT));
+    for (int j = 0; j < p.ns; ++j)
+      LMOE_TRY(wgrad(w.dyT, d, w.hsT + (int64_t)j * p.fs * ldt, p.fs, (char*)G->sh_o + (int64_t)j * d * p.fs * es));
+    LMOE_TRY(wgrad(w.dcatT + (int64_t)(l + rpad) * ldt, nsf, w.xT, d, G->sh_g));
+    LMOE_TRY(wgrad(w.dcatT + (int64_t)(l + rpad + nsf) * ldt, nsf, w.xT, d, G->sh_u));
+  }
   return LMOE_OK;
 }
 
@@ -722,6 +913,10 @@ size_t latentmoe_workspace_bytes(const lmoe_dims* dims, int32_t entry) {
     case LMOE_ENTRY_ROUTED_BACKWARD: {
       RoutedBwdWs w;
       return carve_routed_backward(p, nullptr, &w);
+    }
+    case LMOE_ENTRY_BACKWARD: {
+      LayerBwdWs w;
+      return carve_layer_backward(p, nullptr, &w);
     }
   }
   return 0;
@@ -958,10 +1153,53 @@ lmoe_status latentmoe_routed_backward(const lmoe_dims* dims, const void* z, cons
     return LMOE_OK;
   }
   if (p.bf16)
-    return run_routed_backward<bf16_t, f16_t>(p, dims, z, ids, probs, w_g, w_u, w_o, du, dz, dprobs, dw_g,
-                                              dw_u, dw_o, w, st);
-  return run_routed_backward<float, float>(p, dims, z, ids, probs, w_g, w_u, w_o, du, dz, dprobs, dw_g, dw_u,
-                                           dw_o, w, st);
+    return run_routed_backward<bf16_t, f16_t, bf16_t, float>(p, dims, z, ids, probs, w_g, w_u, w_o, du, dz, p.l,
+                                                             dprobs, dw_g, dw_u, dw_o, w, st);
+  return run_routed_backward<float, float, float, float>(p, dims, z, ids, probs, w_g, w_u, w_o, du, dz, p.l,
+                                                         dprobs, dw_g, dw_u, dw_o, w, st);
+}
+
+lmoe_status latentmoe_backward(const lmoe_dims* dims, const lmoe_weights* weights, const void* x,
+                               const int32_t* ids, const float* probs, const void* dy, float* dx,
+                               const lmoe_grads* grads, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  Plan p;
+  LMOE_TRY(check_dims(dims, &p));
+  if (!weights || !grads) return fail(LMOE_ERR_INVALID_ARGUMENT, "NULL weights or gradients");
+  const lmoe_weights* W = weights;
+  const lmoe_grads* G = grads;
+  if (!W->w_down || !W->w_router || !W->w_g || !W->w_u || !W->w_o || !W->w_up)
+    return fail(LMOE_ERR_INVALID_ARGUMENT, "NULL weight");
+  if (!G->w_down || !G->w_router || !G->w_g || !G->w_u || !G->w_o || !G->w_up || !G->rms_w)
+    return fail(LMOE_ERR_INVALID_ARGUMENT, "NULL gradient");
+  if (p.ns > 0 && (!W->sh_g || !W->sh_u || !W->sh_o || !G->sh_g || !G->sh_u || !G->sh_o))
+    return fail(LMOE_ERR_INVALID_ARGUMENT, "NULL shared expert weight or gradient");
+  if (p.N > 0 && (!x || !ids || !probs || !dy || !dx)) return fail(LMOE_ERR_INVALID_ARGUMENT, "NULL tensor");
+  LayerBwdWs w{};
+  const size_t need = carve_layer_backward(p, nullptr, &w);
+  if (!workspace || workspace_bytes < need)
+    return fail(LMOE_ERR_WORKSPACE, "backward needs %zu workspace bytes", need);
+  carve_layer_backward(p, (char*)workspace, &w);
+  hipStream_t st = launch_stream(stream);
+  if (p.N == 0) {  // no tokens: every gradient is zero
+    auto zero = [&](void* ptr, int64_t bytes) -> lmoe_status {
+      if (bytes <= 0) return LMOE_OK;
+      zero_words_kernel<<<1024, 256, 0, st>>>((uint32_t*)ptr, bytes / 4);
+      LMOE_HIP(hipGetLastError());
+      return LMOE_OK;
+    };
+    const int64_t es = p.es, nsf = (int64_t)p.ns * p.fs;
+    LMOE_TRY(zero(G->w_down, (int64_t)p.l * p.d * es));
+    LMOE_TRY(zero(G->w_router, (int64_t)p.R * p.d * es));
+    for (void* g : {G->w_g, G->w_u, G->w_o}) LMOE_TRY(zero(g, (int64_t)p.R * p.fr * p.l * es));
+    if (nsf > 0)
+      for (void* g : {G->sh_g, G->sh_u, G->sh_o}) LMOE_TRY(zero(g, nsf * p.d * es));
+    LMOE_TRY(zero(G->w_up, (int64_t)p.d * p.l * es));
+    LMOE_TRY(zero(G->rms_w, (int64_t)p.l * 4));
+    return LMOE_OK;
+  }
+  if (p.bf16) return run_layer_backward<bf16_t, f16_t>(p, dims, W, x, ids, probs, dy, dx, G, w, st);
+  return run_layer_backward<float, float>(p, dims, W, x, ids, probs, dy, dx, G, w, st);
 }
 
 }  // extern "C"

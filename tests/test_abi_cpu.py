@@ -29,7 +29,7 @@ def test_workspace_sizes_grow_with_tokens():
     for cfg in S.CONFIGS.values():
         d1 = M.dims_of(cfg)
         d2 = M.dims_of(cfg, n_tokens=2 * cfg.n_tokens)
-        for e in range(5):
+        for e in range(6):
             assert M.workspace_bytes(d1, e) > 0
             assert M.workspace_bytes(d2, e) >= M.workspace_bytes(d1, e)
     # forward needs at least z, the slots and the expert hidden of every pair (16-bit)
@@ -118,3 +118,19 @@ def test_routed_backward_argument_errors():
     c = S.CONFIGS["b05_n4096"]
     need = 3 * c.n_routed * c.ff_routed * c.d_latent * 2
     assert M.workspace_bytes(M.dims_of(c), M.ENTRY_ROUTED_BACKWARD) >= need
+
+
+def test_layer_backward_argument_errors():
+    lib = M.load()
+    dims = M.dims_of(S.CONFIGS["toy_n128"])
+    fake = 4096  # never dereferenced: validation fails first
+    W = M.Weights(*([fake] * 11))
+    G = M.Grads(*([fake] * 10))
+    assert lib.latentmoe_backward(ctypes.byref(dims), ctypes.byref(W), fake, fake, fake, fake, fake,
+                                  ctypes.byref(G), fake, 16, None) == 4
+    G0 = M.Grads(*([fake] * 9 + [None]))  # no W_up gradient
+    assert lib.latentmoe_backward(ctypes.byref(dims), ctypes.byref(W), fake, fake, fake, fake, fake,
+                                  ctypes.byref(G0), fake, 1 << 40, None) == 1
+    assert lib.latentmoe_backward(ctypes.byref(dims), ctypes.byref(W), fake, None, fake, fake, fake,
+                                  ctypes.byref(G), fake, 1 << 40, None) == 1
+    assert M.workspace_bytes(dims, M.ENTRY_BACKWARD) > M.workspace_bytes(dims, M.ENTRY_ROUTED_BACKWARD)

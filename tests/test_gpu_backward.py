@@ -185,3 +185,157 @@ def test_routed_backward_k3_decode_sample():
 @pytest.mark.slow
 def test_routed_backward_k3_prefill_sample():
     _full_size("k3full_n8192", [0, 4097, 8191], 2)
+
+
+# ------------------------------------------------------------ whole layer
+
+
+def _layer_cfgs():
+    base = S.CONFIGS
+    return [
+        base["toy_n128"],
+        base["b05_n4096"],
+        base["b05skew_n4096"],
+        base["toy_n128"].with_(name="toy_n77_ragged", n_tokens=77),
+        base["toy_n128"].with_(name="toy_noshared", n_shared=0),
+        S.LayerConfig("kR_bf16", 70, 128, 64, 6, 6, 3, 128, 64, "bf16", seed=8, bias="uniform"),
+        S.LayerConfig("wide_k_bf16", 333, 256, 128, 40, 9, 1, 192, 256, "bf16", seed=9, bias="uniform"),
+    ]
+
+
+def _grad_bufs(cfg):
+    N, d, l, R, f = cfg.n_tokens, cfg.d_model, cfg.d_latent, cfg.n_routed, cfg.ff_routed
+    td = G.torch_dtype(cfg.dtype)
+    nan = float("nan")
+    g = {n: torch.full(S.tensor_spec(cfg, n)[0], nan, dtype=td, device="cuda")
+         for n in ("w_down", "w_router", "w_g", "w_u", "w_o", "w_up")}
+    if cfg.n_shared > 0:
+        for n in ("sh_g", "sh_u", "sh_o"):
+            g[n] = torch.full(S.tensor_spec(cfg, n)[0], nan, dtype=td, device="cuda")
+    g["rms_w"] = torch.full((l,), nan, dtype=torch.float32, device="cuda")
+    return g
+
+
+def _run_layer_gpu(cfg, ids, probs, dev):
+    N, d = cfg.n_tokens, cfg.d_model
+    dims = M.dims_of(cfg)
+    dx = torch.full((N, d), float("nan"), dtype=torch.float32, device="cuda")
+    grads = _grad_bufs(cfg)
+    ws = torch.empty(max(M.workspace_bytes(dims, M.ENTRY_BACKWARD), 1), dtype=torch.uint8, device="cuda")
+    M.latentmoe_backward(dims, dev, dev["x"], torch.from_numpy(ids).cuda(), torch.from_numpy(probs).cuda(),
+                         dev["dy"], dx, grads, workspace=ws)
+    torch.cuda.synchronize()
+    return dx, grads
+
+
+def _layer_routes(cfg, W, x=None):
+    x = O.config_x(cfg) if x is None else x
+    r = O.route(x, W.w_router, W.bias, cfg.top_k)
+    return r.ids.astype(np.int32), r.p.astype(np.float32)
+
+
+@pytest.mark.parametrize("cfg", _layer_cfgs(), ids=lambda c: c.name)
+def test_layer_backward_parity(cfg):
+    _say(f"[layer_backward] {cfg.name}")
+    host = S.host_inputs(cfg)
+    dev = G.device_layer_inputs(cfg, host=host)
+    dev["dy"] = G.upload(S.host_tensor(cfg, "dy"), cfg.dtype).reshape(cfg.n_tokens, cfg.d_model)
+    W = O.config_weights(cfg, cache_experts=cfg.n_routed)
+    x = O.config_x(cfg)
+    ids, probs = _layer_routes(cfg, W, x)
+    dx, grads = _run_layer_gpu(cfg, ids, probs, dev)
+    dy = S.to_f64(S.host_tensor(cfg, "dy"), cfg.dtype).reshape(cfg.n_tokens, cfg.d_model)
+    ref = O.layer_backward(x, W, dy, ids=ids)
+    _check("dx", G.download_f64(dx), ref["x"], G.TOL[cfg.dtype])
+    names = ["w_down", "w_router", "w_up"] + (["sh_g", "sh_u", "sh_o"] if cfg.n_shared else [])
+    for n in names:
+        err = _check_wgrad(n, G.download_f64(grads[n]).reshape(ref[n].shape), ref[n], cfg.dtype)
+        _say(f"   {n}: err {err:.3e}")
+    _check("rms_w", G.download_f64(grads["rms_w"]), ref["rms_w"], G.TOL[cfg.dtype])
+    used = set(ids.reshape(-1).tolist())
+    for e in range(cfg.n_routed):
+        for j, n in enumerate(("w_g", "w_u", "w_o")):
+            got = G.download_f64(grads[n][e])
+            if e not in used:
+                assert np.all(got == 0.0), (n, e)
+            else:
+                _check_wgrad(f"{n}[{e}]", got, ref["routed"][e][j], cfg.dtype)
+
+
+def test_layer_backward_empty_batch():
+    cfg = S.CONFIGS["toy_n128"].with_(name="toy_n0", n_tokens=0)
+    base = S.CONFIGS["toy_n128"]
+    dev = G.device_layer_inputs(base, host=S.host_inputs(base))
+    dims = M.dims_of(cfg)
+    grads = _grad_bufs(cfg)
+    ws = torch.empty(max(M.workspace_bytes(dims, M.ENTRY_BACKWARD), 1), dtype=torch.uint8, device="cuda")
+    e = torch.empty(0, device="cuda")
+    M.latentmoe_backward(dims, dev, e, e, e, e, e, grads, workspace=ws)
+    torch.cuda.synchronize()
+    for n, t in grads.items():
+        assert torch.all(t == 0), n
+
+
+@pytest.mark.slow
+def test_layer_backward_k3_decode_full():
+    """Full-K3 decode shape: dx and every gradient except the routed experts'
+    (sampled experts, all their pairs)."""
+    cfg = S.CONFIGS["k3full_n64"]
+    _say(f"[layer_backward full] {cfg.name}")
+    dev = G.device_layer_inputs(cfg)
+    dev["dy"] = S.gen.device_tensor(cfg, "dy")
+    W = O.config_weights(cfg, cache_experts=2)
+    x = O.config_x(cfg)
+    ids, probs = _layer_routes(cfg, W)
+    dx, grads = _run_layer_gpu(cfg, ids, probs, dev)
+    del dev
+    dy = S.to_f64(S.host_tensor(cfg, "dy"), cfg.dtype).reshape(cfg.n_tokens, cfg.d_model)
+    counts = np.bincount(ids.reshape(-1), minlength=cfg.n_routed)
+    used = np.nonzero(counts)[0]
+    picks = [int(used[0]), int(used[len(used) // 2])]
+    ref = O.layer_backward(x, W, dy, ids=ids, want=picks)
+    _check("dx", G.download_f64(dx), ref["x"], G.TOL[cfg.dtype])
+    for n in ("w_down", "w_router", "w_up", "sh_g", "sh_u", "sh_o"):
+        err = _check_wgrad(n, G.download_f64(grads[n]).reshape(ref[n].shape), ref[n], cfg.dtype)
+        _say(f"   {n}: err {err:.3e}")
+    _check("rms_w", G.download_f64(grads["rms_w"]), ref["rms_w"], G.TOL[cfg.dtype])
+    for e in picks:
+        for j, n in enumerate(("w_g", "w_u", "w_o")):
+            _check_wgrad(f"{n}[{e}]", G.download_f64(grads[n][e]), ref["routed"][e][j], cfg.dtype)
+
+
+@pytest.mark.slow
+def test_layer_backward_k3_prefill_sample():
+    """Full-K3 prefill shape: dx of sampled tokens (tokens are independent
+    given the routes, so the oracle runs on those rows alone)."""
+    cfg = S.CONFIGS["k3full_n8192"]
+    _say(f"[layer_backward full] {cfg.name}")
+    dev = G.device_layer_inputs(cfg)
+    dev["dy"] = S.gen.device_tensor(cfg, "dy")
+    W = O.config_weights(cfg, cache_experts=2)
+    ids, probs = _layer_routes(cfg, W, O.config_x(cfg))
+    dx, grads = _run_layer_gpu(cfg, ids, probs, dev)
+    del dev, grads
+    rows = np.array([0, 4097, 8191])
+    x = O.config_x(cfg, rows=rows)
+    d = cfg.d_model
+    dy = np.stack([S.to_f64(S.host_tensor(cfg, "dy", int(r) * d, d), cfg.dtype) for r in rows])
+    ref = O.layer_backward(x, W, dy, ids=ids[rows], want=[])
+    _check("dx (sampled tokens)", G.download_f64(dx[torch.as_tensor(rows)]), ref["x"], G.TOL[cfg.dtype])
+
+
+def test_layer_backward_is_deterministic():
+    cfg = S.CONFIGS["b05skew_n4096"]
+    host = S.host_inputs(cfg)
+    dev = G.device_layer_inputs(cfg, host=host)
+    dev["dy"] = G.upload(S.host_tensor(cfg, "dy"), cfg.dtype).reshape(cfg.n_tokens, cfg.d_model)
+    W = O.config_weights(cfg)
+    ids, probs = _layer_routes(cfg, W)
+    a = _run_layer_gpu(cfg, ids, probs, dev)
+    b = _run_layer_gpu(cfg, ids, probs, dev)
+    assert torch.equal(a[0], b[0])
+    for n in a[1]:
+        t, u = a[1][n], b[1][n]
+        if t.dtype == torch.bfloat16:
+            t, u = t.view(torch.int16), u.view(torch.int16)
+        assert torch.equal(t, u), n
