@@ -212,15 +212,19 @@ __global__ __launch_bounds__(256) void inverse_order_kernel(const int32_t* __res
   if (i < pairs) inv[order[i]] = (int32_t)i;
 }
 
-// dz[n] (row stride ld) = sum over slots j (in slot order) of rows[inv[n k + j]],
-// one workgroup per token.
+// dz[n] (row stride ld) = sum over slots j (in slot order) of wts[n k + j] *
+// rows[inv[n k + j]] (wts NULL = ones), one workgroup per token.
 template <typename TD>
 __global__ __launch_bounds__(256) void pair_sum_kernel(const float* __restrict__ rows, const int32_t* __restrict__ inv,
-                                                       int top_k, int ell, TD* __restrict__ dz, int64_t ld) {
+                                                       int top_k, int ell, const float* __restrict__ wts,
+                                                       TD* __restrict__ dz, int64_t ld) {
   const int64_t n = blockIdx.x;
   for (int c = threadIdx.x; c < ell; c += 256) {
     float acc = 0.f;
-    for (int j = 0; j < top_k; ++j) acc += rows[(int64_t)inv[n * top_k + j] * ell + c];
+    for (int j = 0; j < top_k; ++j) {
+      const float v = rows[(int64_t)inv[n * top_k + j] * ell + c];
+      acc += wts ? wts[n * top_k + j] * v : v;
+    }
     Elem<TD>::store(dz + n * ld + c, acc);
   }
 }
@@ -259,14 +263,30 @@ __global__ __launch_bounds__(256) void rmsnorm_backward_kernel(const float* __re
   if (threadIdx.x == 0) rho_out[n] = rho;
 }
 
-// dw[c] = sum over tokens n (in order) of dr[n, c] u[n, c] rho[n]; one thread per column.
-__global__ __launch_bounds__(256) void rmsnorm_wgrad_kernel(const float* __restrict__ u, const float* __restrict__ dr,
-                                                            const float* __restrict__ rho, int64_t N, int ell,
-                                                            float* __restrict__ dw) {
+// dw[c] = sum over tokens n of dr[n, c] u[n, c] rho[n], in two passes with a
+// fixed order: pass 1 sums chunks of `chunk` tokens into part[chunk index, c]
+// (grid: column blocks x chunks), pass 2 adds the chunks in order.
+constexpr int kWgradChunk = 64;  // tokens per chunk (more past 65535 chunks)
+__global__ __launch_bounds__(256) void rmsnorm_wgrad_partial_kernel(const float* __restrict__ u,
+                                                                    const float* __restrict__ dr,
+                                                                    const float* __restrict__ rho, int64_t N,
+                                                                    int64_t chunk, int ell,
+                                                                    float* __restrict__ part) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= ell) return;
+  const int64_t n0 = (int64_t)blockIdx.y * chunk;
+  const int64_t n1 = n0 + chunk < N ? n0 + chunk : N;
+  float acc = 0.f;
+  for (int64_t n = n0; n < n1; ++n) acc += dr[n * ell + c] * u[n * ell + c] * rho[n];
+  part[(int64_t)blockIdx.y * ell + c] = acc;
+}
+
+__global__ __launch_bounds__(256) void rmsnorm_wgrad_final_kernel(const float* __restrict__ part, int nchunks,
+                                                                  int ell, float* __restrict__ dw) {
   const int c = blockIdx.x * 256 + threadIdx.x;
   if (c >= ell) return;
   float acc = 0.f;
-  for (int64_t n = 0; n < N; ++n) acc += dr[n * ell + c] * u[n * ell + c] * rho[n];
+  for (int i = 0; i < nchunks; ++i) acc += part[(int64_t)i * ell + c];
   dw[c] = acc;
 }
 

@@ -236,9 +236,9 @@ size_t carve_routed_backward(const Plan& p, char* b, RoutedBwdWs* w) {
 // to a multiple of 64) feed the dense weight gradients.
 struct LayerBwdWs {
   RoutedBwdWs rw;
-  int64_t rpad, nsf, kcat, npad;
+  int64_t rpad, nsf, kcat, npad, rms_chunk;
   char *z, *rn, *hs, *dcat;            // intermediate type
-  float *logits, *u, *ag, *au, *dr, *dhs, *du, *rho, *dprobs;
+  float *logits, *u, *ag, *au, *dr, *dhs, *du, *rho, *dprobs, *rms_part;
   char *w_upT, *shoT, *w_downT, *w_rT, *sgT, *suT;  // storage type
   int32_t* seg;
   char *dyT, *rnT, *hsT, *dcatT, *xT;  // intermediate type
@@ -266,6 +266,8 @@ size_t carve_layer_backward(const Plan& p, char* b, LayerBwdWs* w) {
   w->du = c.take<float>((size_t)N * p.l * 4);
   w->rho = c.take<float>((size_t)N * 4);
   w->dprobs = c.take<float>((size_t)N * p.k * 4);
+  w->rms_chunk = std::max<int64_t>(kWgradChunk, (N + 65534) / 65535);
+  w->rms_part = c.take<float>((size_t)((N + w->rms_chunk - 1) / w->rms_chunk) * p.l * 4);
   w->w_upT = c.take<char>((size_t)p.l * p.d * es);
   w->shoT = c.take<char>((size_t)w->nsf * p.d * es);
   w->w_downT = c.take<char>((size_t)p.d * p.l * es);
@@ -343,7 +345,7 @@ lmoe_status gemm(GemmArgs a, Tile t, hipStream_t st) {
     switch (t) {
       case TILE_S: return gemm_cfg<TA, TB, OutT, AM, BMD, EM, 64, dual ? 256 : 128, 1, 4, 3, 3, 128>(a, st);
       case TILE_M: return gemm_cfg<TA, TB, OutT, AM, BMD, EM, 128, 128, 2, 2, 3, 3, 128>(a, st);
-      case TILE_M2: return gemm_cfg<TA, TB, OutT, AM, BMD, EM, 128, 128, 2, 2, 2, 2, 128>(a, st);
+      case TILE_M2: return gemm_cfg<TA, TB, OutT, AM, BMD, EM, 128, 128, 2, 2, 3, 3, 64>(a, st);
       default: return gemm_cfg<TA, TB, OutT, AM, BMD, EM, 256, 256, 2, 4, 2, 2, 128>(a, st);
     }
   } else {
@@ -496,14 +498,41 @@ lmoe_status transpose_batched(const T* in, int64_t in_bstride, int ld_in, int ro
   return LMOE_OK;
 }
 
-// Routed-block backward (see latentmoe_routed_backward).  T: storage type of
-// z, the weights and the weight gradients; TI: intermediate type.
-// TZ: type of z; dz is written as TDZ with row stride ld_dz.
-template <typename T, typename TI, typename TZ, typename TDZ>
-lmoe_status run_routed_backward(const Plan& p, const lmoe_dims* dm, const void* z, const int32_t* ids,
-                                const float* probs, const void* w_g, const void* w_u, const void* w_o,
-                                const float* du, void* dz, int64_t ld_dz, float* dprobs, void* dw_g,
-                                void* dw_u, void* dw_o, const RoutedBwdWs& w, hipStream_t st) {
+// Grouped-GEMM arguments over the routed pairs of a backward workspace.
+GemmArgs routed_grouped(const Plan& p, const lmoe_dims* dm, const RoutedBwdWs& w, const void* a, int64_t lda,
+                        const void* bw, int64_t ldb, int64_t bstride, int nrows, int K, void* out, int64_t ldo) {
+  GemmArgs g = base_args(dm);
+  g.N = nrows;
+  g.K = K;
+  g.m_tiles = (int)p.tile_bound;
+  g.a = (const char*)a;
+  g.lda = lda;
+  g.order = w.order;
+  g.top_k = p.k;
+  g.tile_list = w.tile_list;
+  g.tile_count = w.meta + 1;
+  g.counts = w.counts;
+  g.offsets = w.offsets;
+  g.b0 = (const char*)bw;
+  g.ldb = ldb;
+  g.b_expert_stride = bstride;
+  g.nb_rows = nrows;
+  g.out = (char*)out;
+  g.ldo = ldo;
+  return g;
+}
+
+Tile routed_tile(const Plan& p) { return p.tile_m == 64 ? TILE_V : p.tile_m == 128 ? TILE_M : TILE_W; }
+
+// Forward part of the routed-block backward: the dispatch bookkeeping, the
+// pre-activations g = z W_g^T and up = z W_u^T (fp32), the hidden h (TI) and
+// the expert outputs o = h W_o^T (fp32), all in sorted pair order.  Returns
+// the capacity C (one host read-back).  T: storage type of the weights;
+// TI: intermediate type; TZ: type of z.
+template <typename T, typename TI, typename TZ>
+lmoe_status routed_recompute(const Plan& p, const lmoe_dims* dm, const void* z, const int32_t* ids,
+                             const void* w_g, const void* w_u, const void* w_o, const RoutedBwdWs& w,
+                             int* C_out, hipStream_t st) {
   const int64_t P = p.pairs;
   const int f = p.fr, l = p.l, R = p.R;
   const int64_t es = sizeof(T), ei = sizeof(TI);
@@ -516,33 +545,15 @@ lmoe_status run_routed_backward(const Plan& p, const lmoe_dims* dm, const void* 
   LMOE_HIP(hipMemcpyAsync(meta, w.meta, sizeof(meta), hipMemcpyDeviceToHost, st));
   LMOE_HIP(hipStreamSynchronize(st));
   if (meta[2] != 0) return fail(LMOE_ERR_INVALID_ARGUMENT, "%d expert ids outside [0, R)", meta[2]);
-  const int C = meta[0];
+  *C_out = meta[0];
   inverse_order_kernel<<<(unsigned)((P + 255) / 256), 256, 0, st>>>(w.order, P, w.inv);
   LMOE_HIP(hipGetLastError());
   padded_ranges_kernel<<<1, 1024, 0, st>>>(w.counts, R, w.kr_off, w.kr_len);
   LMOE_HIP(hipGetLastError());
-  const Tile tile = p.tile_m == 64 ? TILE_V : p.tile_m == 128 ? TILE_M : TILE_W;
+  const Tile tile = routed_tile(p);
   auto grouped = [&](const void* a, int64_t lda, const void* bw, int64_t ldb, int64_t bstride, int nrows,
                      int K, void* out, int64_t ldo) {
-    GemmArgs g = base_args(dm);
-    g.N = nrows;
-    g.K = K;
-    g.m_tiles = (int)p.tile_bound;
-    g.a = (const char*)a;
-    g.lda = lda;
-    g.order = w.order;
-    g.top_k = p.k;
-    g.tile_list = w.tile_list;
-    g.tile_count = w.meta + 1;
-    g.counts = w.counts;
-    g.offsets = w.offsets;
-    g.b0 = (const char*)bw;
-    g.ldb = ldb;
-    g.b_expert_stride = bstride;
-    g.nb_rows = nrows;
-    g.out = (char*)out;
-    g.ldo = ldo;
-    return g;
+    return routed_grouped(p, dm, w, a, lda, bw, ldb, bstride, nrows, K, out, ldo);
   };
   // 2. pre-activations of every pair: g = z W_g^T, up = z W_u^T (fp32, sorted rows)
   const int64_t ez = sizeof(TZ);
@@ -552,9 +563,29 @@ lmoe_status run_routed_backward(const Plan& p, const lmoe_dims* dm, const void* 
       grouped(z, l * ez, w_u, l * es, (int64_t)f * l * es, f, l, w.up, (int64_t)f * 4), tile, st)));
   situ_hidden_kernel<TI><<<blocks(P * f), 256, 0, st>>>(w.g, w.up, P * f, dm->beta1, dm->beta2, (TI*)w.hs);
   LMOE_HIP(hipGetLastError());
-  // 3. expert outputs o = h W_o^T (fp32), then dprobs and dout = p * du (sorted rows)
-  LMOE_TRY((gemm<TI, T, float, A_SORTED, B_SINGLE, E_STORE>(
-      grouped(w.hs, f * ei, w_o, f * es, (int64_t)l * f * es, l, f, w.o, (int64_t)l * 4), tile, st)));
+  // 3. expert outputs o = h W_o^T (fp32, sorted rows)
+  return gemm<TI, T, float, A_SORTED, B_SINGLE, E_STORE>(
+      grouped(w.hs, f * ei, w_o, f * es, (int64_t)l * f * es, l, f, w.o, (int64_t)l * 4), tile, st);
+}
+
+// Gradient part of the routed-block backward, on the quantities
+// routed_recompute left in the workspace.  dz is written as TDZ with row
+// stride ld_dz.
+template <typename T, typename TI, typename TZ, typename TDZ>
+lmoe_status routed_gradients(const Plan& p, const lmoe_dims* dm, const void* z, const float* probs,
+                             const void* w_g, const void* w_u, const void* w_o, const float* du, void* dz,
+                             int64_t ld_dz, float* dprobs, void* dw_g, void* dw_u, void* dw_o, const RoutedBwdWs& w,
+                             int C, hipStream_t st) {
+  const int64_t P = p.pairs;
+  const int f = p.fr, l = p.l, R = p.R;
+  const int64_t es = sizeof(T), ei = sizeof(TI);
+  auto blocks = [](int64_t n) { return (unsigned)std::min<int64_t>((n + 255) / 256, 65536); };
+  const Tile tile = routed_tile(p);
+  auto grouped = [&](const void* a, int64_t lda, const void* bw, int64_t ldb, int64_t bstride, int nrows,
+                     int K, void* out, int64_t ldo) {
+    return routed_grouped(p, dm, w, a, lda, bw, ldb, bstride, nrows, K, out, ldo);
+  };
+  // 3b. dprobs and dout = p * du (sorted rows)
   pair_grad_kernel<TI><<<(unsigned)P, 256, 0, st>>>(du, w.o, probs, w.order, p.k, l, dprobs, (TI*)w.dout);
   LMOE_HIP(hipGetLastError());
   // 4. dh = dout W_o (through W_o^T [R, f, l]), then the SiTU backward -> [dg | du]
@@ -575,7 +606,7 @@ lmoe_status run_routed_backward(const Plan& p, const lmoe_dims* dm, const void* 
       grouped(w.dgu, 2 * f * ei, w.w_guT, 2 * f * es, (int64_t)l * 2 * f * es, l, 2 * f, dzrows,
               (int64_t)l * 4),
       tile, st)));
-  pair_sum_kernel<TDZ><<<(unsigned)p.N, 256, 0, st>>>(dzrows, w.inv, p.k, l, (TDZ*)dz, ld_dz);
+  pair_sum_kernel<TDZ><<<(unsigned)p.N, 256, 0, st>>>(dzrows, w.inv, p.k, l, nullptr, (TDZ*)dz, ld_dz);
   LMOE_HIP(hipGetLastError());
   // 6. weight gradients: per expert, products over its pairs (K = padded pair range)
   const unsigned ysegs = (unsigned)((C + 63) / 64);
@@ -612,11 +643,27 @@ lmoe_status run_routed_backward(const Plan& p, const lmoe_dims* dm, const void* 
     g.o_batch_stride = (int64_t)M * N * es;
     return g;
   };
+  // short K (an expert's padded pairs): 64-byte K steps in a 3-stage ring keep
+  // 48 KB of LDS per workgroup, so three tiles share a compute unit and hide
+  // each other's operand latency
   constexpr Tile kWgradTile = TILE_M2;
   LMOE_TRY((gemm<TI, TI, T, A_KBATCH, B_SINGLE, E_STORE>(batched(w.doutT, l, w.hT, f, dw_o), kWgradTile, st)));
   LMOE_TRY((gemm<TI, TI, T, A_KBATCH, B_SINGLE, E_STORE>(batched(w.dgT, f, w.zT, l, dw_g), kWgradTile, st)));
   LMOE_TRY((gemm<TI, TI, T, A_KBATCH, B_SINGLE, E_STORE>(batched(w.duT, f, w.zT, l, dw_u), kWgradTile, st)));
   return LMOE_OK;
+}
+
+// Routed-block backward (see latentmoe_routed_backward).  T: storage type of
+// the weights and the weight gradients; TI: intermediate type; TZ: type of z.
+template <typename T, typename TI, typename TZ, typename TDZ>
+lmoe_status run_routed_backward(const Plan& p, const lmoe_dims* dm, const void* z, const int32_t* ids,
+                                const float* probs, const void* w_g, const void* w_u, const void* w_o,
+                                const float* du, void* dz, int64_t ld_dz, float* dprobs, void* dw_g,
+                                void* dw_u, void* dw_o, const RoutedBwdWs& w, hipStream_t st) {
+  int C = 0;
+  LMOE_TRY((routed_recompute<T, TI, TZ>(p, dm, z, ids, w_g, w_u, w_o, w, &C, st)));
+  return routed_gradients<T, TI, TZ, TDZ>(p, dm, z, probs, w_g, w_u, w_o, du, dz, ld_dz, dprobs, dw_g, dw_u,
+                                          dw_o, w, C, st);
 }
 
 // Whole-layer backward (see latentmoe_backward).  T: storage type; TI: intermediate type.
@@ -649,12 +696,16 @@ lmoe_status run_layer_backward(const Plan& p, const lmoe_dims* dm, const lmoe_we
                                                        dense_tile(N, l, false), st)));
   LMOE_TRY((gemm<T, T, float, A_DENSE, B_SINGLE, E_STORE>(
       dense(x, d * es, (int)N, W->w_router, d * es, R, d, w.logits, (int64_t)R * 4), dense_tile(N, R, false), st)));
+  // the routed block's forward quantities (pre-activations, hidden, expert
+  // outputs), kept for its gradients below
   const RoutedBwdWs& rw = w.rw;
-  LMOE_TRY(run_dispatch(p, ids, rw.chunk_hist, rw.chunk_bad, rw.counts, rw.offsets, rw.order, rw.meta, st));
-  LMOE_TRY((run_experts<TI, T, TI, A_GATHER>(p, dm, w.z, 0, rw.counts, rw.offsets, rw.order, probs, W->w_g,
-                                             W->w_u, W->w_o, rw.tile_list, rw.meta, rw.hs, rw.dout, st)));
-  combine_rmsnorm_kernel<TI, TI><<<(unsigned)N, 256, 0, st>>>((const TI*)rw.dout, p.k, l, w.u, W->rms_w,
-                                                              dm->rms_eps, (TI*)w.rn, l);
+  int C = 0;
+  LMOE_TRY((routed_recompute<T, TI, TI>(p, dm, w.z, ids, W->w_g, W->w_u, W->w_o, rw, &C, st)));
+  // u = sum over the token's pairs (slot order) of p o, then RMSNorm(u)
+  pair_sum_kernel<float><<<(unsigned)N, 256, 0, st>>>(rw.o, rw.inv, p.k, l, probs, w.u, l);
+  LMOE_HIP(hipGetLastError());
+  combine_rmsnorm_kernel<float, TI><<<(unsigned)N, 256, 0, st>>>(w.u, 1, l, nullptr, W->rms_w, dm->rms_eps,
+                                                                 (TI*)w.rn, l);
   LMOE_HIP(hipGetLastError());
   if (nsf > 0) {
     LMOE_TRY((gemm<T, T, float, A_DENSE, B_SINGLE, E_STORE>(
@@ -671,8 +722,14 @@ lmoe_status run_layer_backward(const Plan& p, const lmoe_dims* dm, const lmoe_we
                                                           dense_tile(N, l, false), st)));
   rmsnorm_backward_kernel<<<(unsigned)N, 256, 0, st>>>(w.u, w.dr, W->rms_w, l, dm->rms_eps, w.du, w.rho);
   LMOE_HIP(hipGetLastError());
-  rmsnorm_wgrad_kernel<<<(unsigned)((l + 255) / 256), 256, 0, st>>>(w.u, w.dr, w.rho, N, l, G->rms_w);
-  LMOE_HIP(hipGetLastError());
+  {
+    const int nch = (int)((N + w.rms_chunk - 1) / w.rms_chunk);
+    rmsnorm_wgrad_partial_kernel<<<dim3((l + 255) / 256, nch), 256, 0, st>>>(w.u, w.dr, w.rho, N, w.rms_chunk, l,
+                                                                              w.rms_part);
+    LMOE_HIP(hipGetLastError());
+    rmsnorm_wgrad_final_kernel<<<(unsigned)((l + 255) / 256), 256, 0, st>>>(w.rms_part, nch, l, G->rms_w);
+    LMOE_HIP(hipGetLastError());
+  }
   if (nsf > 0) {
     LMOE_TRY(transpose_batched<T>((const T*)W->sh_o, (int64_t)d * p.fs, p.fs, d, p.fs, (T*)w.shoT,
                                    (int64_t)p.fs * d, d, 0, p.ns, nullptr, st));
@@ -684,8 +741,8 @@ lmoe_status run_layer_backward(const Plan& p, const lmoe_dims* dm, const lmoe_we
     LMOE_HIP(hipGetLastError());
   }
   // ---- step 3 backward (routed block) -> dz into dcat[:, :l], dprobs
-  LMOE_TRY((run_routed_backward<T, TI, TI, TI>(p, dm, w.z, ids, probs, W->w_g, W->w_u, W->w_o, w.du, w.dcat,
-                                               kcat, w.dprobs, G->w_g, G->w_u, G->w_o, rw, st)));
+  LMOE_TRY((routed_gradients<T, TI, TI, TI>(p, dm, w.z, probs, W->w_g, W->w_u, W->w_o, w.du, w.dcat, kcat,
+                                            w.dprobs, G->w_g, G->w_u, G->w_o, rw, C, st)));
   // ---- step 2 backward -> dl into dcat[:, l:l+rpad]
   router_backward_kernel<TI><<<(unsigned)((N + 3) / 4), 256, 0, st>>>(w.logits, ids, w.dprobs, N, R, p.k, rpad,
                                                                       (TI*)w.dcat + l, kcat);
