@@ -29,6 +29,12 @@
 //   B_SINGLE  one weight matrix (per expert in grouped mode)
 //   B_DUAL    gate and up matrices interleaved per tile (BN/2 rows of each)
 //   B_KSEG    B concatenated along K from up to kMaxSeg separate matrices
+//   B_KMAJOR  B stored K-major: element (n, k) at b[k * ldb + n] (a weight used
+//             through its transpose), per expert at b_expert_stride; K rows
+//             from kmaj_split on come from b1 (two matrices stacked along K).
+//             LDS holds the tile as KB/2 K-rows of BN values and the MFMA
+//             fragments come out of it through gfx950's transposing LDS read
+//             (ds_read_b64_tr_b16); 16-bit operands only
 //   E_STORE   plain store (fp32 or storage dtype), masked to valid rows/cols
 //   E_SITU    SiTU-GLU hidden of the (gate, up) accumulator pair, stored as OutT
 //   E_SLOTS   p-weighted result of sorted pair q written to its own slot row q
@@ -39,7 +45,7 @@
 namespace lmoe {
 
 enum { A_DENSE = 0, A_GATHER = 1, A_PADDED = 2, A_SORTED = 3, A_KBATCH = 4 };
-enum { B_SINGLE = 0, B_DUAL = 1, B_KSEG = 2 };
+enum { B_SINGLE = 0, B_DUAL = 1, B_KSEG = 2, B_KMAJOR = 3 };
 enum { E_STORE = 0, E_SITU = 1, E_SLOTS = 2 };
 
 template <int V>
@@ -72,6 +78,7 @@ struct GemmArgs {
   const char* b1;
   int64_t ldb;            // bytes
   int64_t b_expert_stride;  // bytes
+  int kmaj_split;           // B_KMAJOR: first K row taken from b1 (a multiple of KB / 2)
   int nb_rows;            // rows of each B matrix (clamp)
   int nseg;
   const char* seg_base[kMaxSeg];
@@ -159,6 +166,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
   static_assert(NW == 4 || NW == 8, "4 or 8 waves per workgroup");
   static_assert(TM >= 1 && TN >= 1 && WTM % 32 == 0 && WTN % 32 == 0, "32x32 sub-tiles");
   static_assert(BMODE != B_DUAL || TN % 2 == 0, "dual tile needs gate and up sub-tiles");
+  static_assert(BMODE != B_KMAJOR || (kHalf && (1024 % (2 * BN) == 0 || (2 * BN) % 1024 == 0)),
+                "K-major B: 16-bit operands, whole K rows per DMA instruction");
   static_assert(A_INST % NW == 0 && B_INST % NW == 0 && BM % RPI == 0 && BN % RPI == 0, "DMA split");
   static_assert(SA >= 2 && SB >= SA && UNROLL <= 8, "ring shape");
   __shared__ __attribute__((aligned(1024))) char smem[RING];
@@ -254,12 +263,37 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
     if constexpr (AMODE == A_GATHER) row = args.order[off + m0 + rr] / args.top_k;
     a_off[ii] = (uint32_t)(row * lda) + lane_chunk(wave * A_W + ii);
   }
+  // B_KMAJOR stage: KE = KB / 2 K-rows of BN values (ROWK bytes, NCR 16-byte
+  // chunks each).  DMA instruction `block` of a step fills bytes
+  // [block * 1024, +1024) of it: lane l lands at byte l * 16 and fetches the
+  // global chunk that belongs there.  Chunks are XOR-swizzled per K-row
+  // (kmaj_sw) so that a transposing fragment read, which takes 64 bytes from
+  // each of 8 K-rows (0-3 and 8-11 of a 16-row group), hits distinct banks.
+  constexpr int KE = KB / 2, ROWK = 2 * BN, NCR = ROWK / 16;
+  auto kmaj_sw = [](int r) -> int { return (4 * (r & 3) + 16 * ((r >> 3) & 1)) & (NCR - 1); };
+  auto kmaj_pos = [&](int r, int n) -> int {  // LDS byte of value (K-row r, column n)
+    return r * ROWK + (((n >> 3) ^ kmaj_sw(r)) << 4) + (n & 7) * 2;
+  };
+  const char* kmaj_b0 = args.b0 + (int64_t)e * args.b_expert_stride;
+  const char* kmaj_b1 = args.b1 + (int64_t)e * args.b_expert_stride;
+
   const char* b_base[B_W];  // workgroup-uniform
   uint32_t b_off[B_W];      // per lane, K step 0
   uint32_t b_chunk[B_W];    // per lane swizzled chunk offset
   int b_brow[B_W];          // clamped row inside the tile's slice of its matrix
 #pragma unroll
   for (int ii = 0; ii < B_W; ++ii) {
+    if constexpr (BMODE == B_KMAJOR) {
+      const int byte = (wave * B_W + ii) * 1024 + lane * 16;
+      const int r = byte / ROWK, c = (byte % ROWK) / 16;
+      // first column of the chunk, clamped to the last valid chunk (nb_rows % 8 == 0)
+      const int n = min(nt * BN + ((c ^ kmaj_sw(r)) << 3), args.nb_rows - 8);
+      b_base[ii] = kmaj_b0;
+      b_off[ii] = (uint32_t)((int64_t)r * ldb + (int64_t)n * 2);
+      b_chunk[ii] = 0;
+      b_brow[ii] = 0;
+      continue;
+    }
     const int r = (wave * B_W + ii) * RPI + lane / NCH;
     const bool up = BMODE == B_DUAL && r >= H;
     const int br = min(up ? r - H : r, b_rows_here - 1);
@@ -295,8 +329,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
   };
   auto dma_b = [&](int kt, const BStep& bs, char* stage, int ii) {
     const char* g;
-    if constexpr (BMODE == B_KSEG) g = bs.base + ((uint32_t)(b_brow[ii] * bs.ld) + b_chunk[ii]);
-    else g = b_base[ii] + (b_off[ii] + (uint32_t)kt * ROWB);
+    if constexpr (BMODE == B_KSEG) {
+      g = bs.base + ((uint32_t)(b_brow[ii] * bs.ld) + b_chunk[ii]);
+    } else if constexpr (BMODE == B_KMAJOR) {
+      const int k0 = kt * KE;  // first K row of the step (workgroup-uniform)
+      const char* rows = k0 < args.kmaj_split ? kmaj_b0 + (int64_t)k0 * ldb
+                                              : kmaj_b1 + (int64_t)(k0 - args.kmaj_split) * ldb;
+      g = rows + b_off[ii];
+    } else {
+      g = b_base[ii] + (b_off[ii] + (uint32_t)kt * ROWB);
+    }
     __builtin_amdgcn_global_load_lds((const void*)g, (lds_void_t*)(stage + (wave * B_W + ii) * RPI * ROWB), 16, 0, 0);
   };
 
@@ -316,6 +358,19 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
       return wn * WTN + j * 32;
     }
   };
+  // B_KMAJOR fragment reads.  Lane = 16 g + q: the 16 lanes of group g read
+  // K-rows r..r+3 (4 columns each) and the transposing read hands lane q
+  // column n0 + q of those rows; g / 2 picks the MFMA's K half, g % 2 the
+  // column half of the 32-column sub-tile.  The swizzle of K-row
+  // 16 c + rb (+ 4) equals that of rb, so one byte offset per sub-tile
+  // serves every chunk c (+ 16 c K-rows) and both reads (+ 4 K-rows).
+  uint32_t kmaj_frag[BMODE == B_KMAJOR ? TN : 1];
+  if constexpr (BMODE == B_KMAJOR) {
+    const int rb = 8 * (lane >> 5) + ((lane >> 2) & 3);
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      kmaj_frag[j] = (uint32_t)kmaj_pos(rb, b_tile_row(j) + 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+  }
   // physical byte offset of logical 16-byte chunk c of tile row `row`
   auto swz = [](int row, int c) -> int { return row * ROWB + ((c ^ ((row / RSH) % NCH)) << 4); };
 
@@ -401,7 +456,18 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
 #pragma unroll
       for (int i = 0; i < NA; ++i) fa[c][i] = *(const u32x4*)(As + swz(wm * WTM + i * 32 + lr, ch));
 #pragma unroll
-      for (int j = 0; j < TN; ++j) fb[c][j] = *(const u32x4*)(Bs + swz(b_tile_row(j) + lr, ch));
+      for (int j = 0; j < TN; ++j) {
+        if constexpr (BMODE == B_KMAJOR) {
+          typedef __attribute__((address_space(3))) i16x4* lds_i16x4_t;
+          const char* q = Bs + kmaj_frag[j] + c * 16 * ROWK;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t)q);
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t)(q + 4 * ROWK));
+          const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+          fb[c][j] = u32x4{l2[0], l2[1], h2[0], h2[1]};
+        } else {
+          fb[c][j] = *(const u32x4*)(Bs + swz(b_tile_row(j) + lr, ch));
+        }
+      }
     };
     auto mfma_chunk = [&](auto c_c) {
       constexpr int c = decltype(c_c)::value;
@@ -431,7 +497,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
       }
     };
     constexpr int MPC = NA * TN * (kHalf ? 1 : 4);  // MFMAs per chunk
-    constexpr int RPC = NA + TN;                     // fragment reads per chunk
+    constexpr int RPC = NA + TN * (BMODE == B_KMAJOR ? 2 : 1);  // fragment reads per chunk
     // tile 0 landed and visible; its first chunks into registers
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(kNewer0));
     barrier();

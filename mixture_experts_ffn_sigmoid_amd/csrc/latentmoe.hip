@@ -220,8 +220,10 @@ size_t carve_routed_backward(const Plan& p, char* b, RoutedBwdWs* w) {
   w->hs = c.take<char>((size_t)P * p.fr * ei);
   w->dout = c.take<char>((size_t)P * p.l * ei);
   w->dgu = c.take<char>((size_t)P * 2 * p.fr * ei);
-  w->w_oT = c.take<char>((size_t)p.R * p.fr * p.l * p.es);
-  w->w_guT = c.take<char>((size_t)p.R * p.l * 2 * p.fr * p.es);
+  // transposed routed weights: fp32 only (16-bit weights are read K-major)
+  const bool transposed = p.es == 4;
+  w->w_oT = c.take<char>(transposed ? (size_t)p.R * p.fr * p.l * p.es : 0);
+  w->w_guT = c.take<char>(transposed ? (size_t)p.R * p.l * 2 * p.fr * p.es : 0);
   w->doutT = c.take<char>((size_t)p.l * w->kpad * ei);
   w->hT = c.take<char>((size_t)p.fr * w->kpad * ei);
   w->dgT = c.take<char>((size_t)p.fr * w->kpad * ei);
@@ -313,15 +315,15 @@ lmoe_status launch_gemm(GemmArgs a, hipStream_t st) {
   return LMOE_OK;
 }
 
-// Block tiles (rows x cols, waves, A / B LDS stages):
-//   S  64 x 128 (256 for gate/up pairs), 4 waves, 4/4: few-row dense products
-//   M 128 x 128, 4 waves, 4/4
-//   L 256 x 256, 8 waves, 4/4 (128 KB of LDS): large dense products
-//   W 192 x 256, 4 waves, 3/6 (132 KB): grouped expert products that stream
-//     their weights (B) from HBM -- the deeper B ring keeps ~80 KB of weights
-//     in flight per CU while the A rows (L2-resident) need only three stages
-//   V  64 x 256, 4 waves, 3/6: the same for a handful of rows per expert
-//   M2 128 x 128, 4 waves, 2/2 (64 KB, two workgroups per CU): short-K
+// Block tiles (rows x cols, waves, A / B LDS stages, bytes of K per step):
+//   S  64 x 128 (256 for gate/up pairs), 4 waves, 3/3, 128: few-row dense products
+//   M 128 x 128, 4 waves, 3/3, 128
+//   L 256 x 256, 8 waves, 2/2, 128 (128 KB of LDS): large dense products
+//   W 192 x 256, 8 waves, 2/3, 128 (144 KB): grouped expert products that
+//     stream their weights (B) from HBM; the B ring is one stage deeper than
+//     the ring of the (L2-resident) A rows
+//   V  64 x 256, 4 waves, 2/3, 128: the same for a handful of rows per expert
+//   M2 128 x 128, 4 waves, 3/3, 64 (48 KB, three workgroups per CU): short-K
 //     products whose time goes into storing the output tile
 enum Tile { TILE_S = 0, TILE_M = 1, TILE_L = 2, TILE_W = 3, TILE_V = 4, TILE_M2 = 5 };
 
@@ -332,6 +334,11 @@ lmoe_status gemm_cfg(GemmArgs a, hipStream_t st) {
   a.n_tiles = (a.N + cols - 1) / cols;
   if (AM == A_DENSE || AM == A_KBATCH) a.m_tiles = (a.M + BM - 1) / BM;
   if ((int64_t)a.K * (int64_t)sizeof(TA) % KB != 0) return fail(LMOE_ERR_UNSUPPORTED, "K not a multiple of the K step");
+  if constexpr (BMD == B_KMAJOR) {
+    if (a.nb_rows < 8 || a.nb_rows % 8 != 0) return fail(LMOE_ERR_UNSUPPORTED, "K-major B needs a multiple of 8 columns");
+    if (a.kmaj_split % (KB / (int)sizeof(TB)) != 0 && a.kmaj_split < a.K)
+      return fail(LMOE_ERR_UNSUPPORTED, "K-major B split not a multiple of the K step");
+  }
   if (BMD == B_KSEG)
     for (int s = 0; s <= a.nseg; ++s)
       if (a.seg_kt0[s] % (KB / kSegUnit) != 0) return fail(LMOE_ERR_UNSUPPORTED, "K segment not a multiple of the K step");
@@ -588,24 +595,39 @@ lmoe_status routed_gradients(const Plan& p, const lmoe_dims* dm, const void* z, 
   // 3b. dprobs and dout = p * du (sorted rows)
   pair_grad_kernel<TI><<<(unsigned)P, 256, 0, st>>>(du, w.o, probs, w.order, p.k, l, dprobs, (TI*)w.dout);
   LMOE_HIP(hipGetLastError());
-  // 4. dh = dout W_o (through W_o^T [R, f, l]), then the SiTU backward -> [dg | du]
-  LMOE_TRY(transpose_batched<T>((const T*)w_o, (int64_t)l * f, f, l, f, (T*)w.w_oT, (int64_t)f * l, l, 0, R,
-                                 w.counts, st));
-  LMOE_TRY((gemm<TI, T, float, A_SORTED, B_SINGLE, E_STORE>(
-      grouped(w.dout, l * ei, w.w_oT, l * es, (int64_t)f * l * es, f, l, w.dh, (int64_t)f * 4), tile, st)));
+  // 4. dh = dout W_o, then the SiTU backward -> [dg | du].  16-bit weights are
+  // read as stored (K-major B: K-row k of W_o[e] is its latent row k); fp32
+  // ones through a transposed copy W_o^T [R, f, l]
+  if constexpr (sizeof(T) == 2) {
+    GemmArgs g = grouped(w.dout, l * ei, w_o, f * es, (int64_t)l * f * es, f, l, w.dh, (int64_t)f * 4);
+    g.kmaj_split = l;
+    LMOE_TRY((gemm<TI, T, float, A_SORTED, B_KMAJOR, E_STORE>(g, tile, st)));
+  } else {
+    LMOE_TRY(transpose_batched<T>((const T*)w_o, (int64_t)l * f, f, l, f, (T*)w.w_oT, (int64_t)f * l, l, 0, R,
+                                   w.counts, st));
+    LMOE_TRY((gemm<TI, T, float, A_SORTED, B_SINGLE, E_STORE>(
+        grouped(w.dout, l * ei, w.w_oT, l * es, (int64_t)f * l * es, f, l, w.dh, (int64_t)f * 4), tile, st)));
+  }
   situ_backward_kernel<TI><<<blocks(P * f), 256, 0, st>>>(w.dh, w.g, w.up, P * f, f, dm->beta1, dm->beta2,
                                                           (TI*)w.dgu, 2 * (int64_t)f, 0);
   LMOE_HIP(hipGetLastError());
-  // 5. dz rows = [dg | du] [W_g | W_u] (through [W_g^T | W_u^T] [R, l, 2f]), summed per token
-  LMOE_TRY(transpose_batched<T>((const T*)w_g, (int64_t)f * l, l, f, l, (T*)w.w_guT, (int64_t)l * 2 * f, 2 * f,
-                                 0, R, w.counts, st));
-  LMOE_TRY(transpose_batched<T>((const T*)w_u, (int64_t)f * l, l, f, l, (T*)w.w_guT, (int64_t)l * 2 * f, 2 * f,
-                                 f, R, w.counts, st));
+  // 5. dz rows = [dg | du] [W_g ; W_u] (K = 2f: W_g's rows, then W_u's), summed per token
   float* dzrows = w.o;  // o is consumed
-  LMOE_TRY((gemm<TI, T, float, A_SORTED, B_SINGLE, E_STORE>(
-      grouped(w.dgu, 2 * f * ei, w.w_guT, 2 * f * es, (int64_t)l * 2 * f * es, l, 2 * f, dzrows,
-              (int64_t)l * 4),
-      tile, st)));
+  if constexpr (sizeof(T) == 2) {
+    GemmArgs g = grouped(w.dgu, 2 * f * ei, w_g, l * es, (int64_t)f * l * es, l, 2 * f, dzrows, (int64_t)l * 4);
+    g.b1 = (const char*)w_u;
+    g.kmaj_split = f;
+    LMOE_TRY((gemm<TI, T, float, A_SORTED, B_KMAJOR, E_STORE>(g, tile, st)));
+  } else {
+    LMOE_TRY(transpose_batched<T>((const T*)w_g, (int64_t)f * l, l, f, l, (T*)w.w_guT, (int64_t)l * 2 * f,
+                                   2 * f, 0, R, w.counts, st));
+    LMOE_TRY(transpose_batched<T>((const T*)w_u, (int64_t)f * l, l, f, l, (T*)w.w_guT, (int64_t)l * 2 * f,
+                                   2 * f, f, R, w.counts, st));
+    LMOE_TRY((gemm<TI, T, float, A_SORTED, B_SINGLE, E_STORE>(
+        grouped(w.dgu, 2 * f * ei, w.w_guT, 2 * f * es, (int64_t)l * 2 * f * es, l, 2 * f, dzrows,
+                (int64_t)l * 4),
+        tile, st)));
+  }
   pair_sum_kernel<TDZ><<<(unsigned)p.N, 256, 0, st>>>(dzrows, w.inv, p.k, l, nullptr, (TDZ*)dz, ld_dz);
   LMOE_HIP(hipGetLastError());
   // 6. weight gradients: per expert, products over its pairs (K = padded pair range)
