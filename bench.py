@@ -177,6 +177,7 @@ KERNEL_SOURCES = ("mixture_experts_ffn_sigmoid_amd/csrc/gemm_kernel.h",
                   "mixture_experts_ffn_sigmoid_amd/csrc/route_kernels.h",
                   "mixture_experts_ffn_sigmoid_amd/csrc/merge_kernels.h",
                   "mixture_experts_ffn_sigmoid_amd/csrc/backward_kernels.h",
+                  "mixture_experts_ffn_sigmoid_amd/csrc/wgrad_kernel.h",
                   "mixture_experts_ffn_sigmoid_amd/csrc/latentmoe.hip")
 
 

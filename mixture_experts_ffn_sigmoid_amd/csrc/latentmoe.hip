@@ -14,6 +14,7 @@
 #include "gemm_kernel.h"
 #include "merge_kernels.h"
 #include "route_kernels.h"
+#include "wgrad_kernel.h"
 
 using namespace lmoe;
 
@@ -665,13 +666,29 @@ lmoe_status routed_gradients(const Plan& p, const lmoe_dims* dm, const void* z, 
     g.o_batch_stride = (int64_t)M * N * es;
     return g;
   };
-  // short K (an expert's padded pairs): 64-byte K steps in a 3-stage ring keep
-  // 48 KB of LDS per workgroup, so three tiles share a compute unit and hide
-  // each other's operand latency
-  constexpr Tile kWgradTile = TILE_M2;
-  LMOE_TRY((gemm<TI, TI, T, A_KBATCH, B_SINGLE, E_STORE>(batched(w.doutT, l, w.hT, f, dw_o), kWgradTile, st)));
-  LMOE_TRY((gemm<TI, TI, T, A_KBATCH, B_SINGLE, E_STORE>(batched(w.dgT, f, w.zT, l, dw_g), kWgradTile, st)));
-  LMOE_TRY((gemm<TI, TI, T, A_KBATCH, B_SINGLE, E_STORE>(batched(w.duT, f, w.zT, l, dw_u), kWgradTile, st)));
+  // Every expert's K is its padded pair count (at most C rounded up to 64).
+  // Up to kWgradKMax, with 16-bit operands and 128-multiple widths, one
+  // workgroup per 128-row strip keeps its A fragments in registers and sweeps
+  // the columns; otherwise batched GEMM tiles (128 x 128, 64-byte K steps in
+  // a 3-stage ring: 48 KB of LDS, three tiles per compute unit).
+  if constexpr (sizeof(TI) == 2 && sizeof(T) == 2) {
+    if ((C + 63) / 64 * 64 <= kWgradKMax && l % kWgradTile == 0 && f % kWgradTile == 0) {
+      auto strips = [&](const void* a, int M, const void* b, int N, void* out) -> lmoe_status {
+        wgrad_kernel<TI, T><<<(unsigned)((int64_t)R * (M / kWgradTile)), 512, 0, st>>>(
+            (const TI*)a, (const TI*)b, w.kr_off, w.kr_len, M, N, (T*)out);
+        LMOE_HIP(hipGetLastError());
+        return LMOE_OK;
+      };
+      LMOE_TRY(strips(w.doutT, l, w.hT, f, dw_o));
+      LMOE_TRY(strips(w.dgT, f, w.zT, l, dw_g));
+      LMOE_TRY(strips(w.duT, f, w.zT, l, dw_u));
+      return LMOE_OK;
+    }
+  }
+  constexpr Tile kWgradGemmTile = TILE_M2;
+  LMOE_TRY((gemm<TI, TI, T, A_KBATCH, B_SINGLE, E_STORE>(batched(w.doutT, l, w.hT, f, dw_o), kWgradGemmTile, st)));
+  LMOE_TRY((gemm<TI, TI, T, A_KBATCH, B_SINGLE, E_STORE>(batched(w.dgT, f, w.zT, l, dw_g), kWgradGemmTile, st)));
+  LMOE_TRY((gemm<TI, TI, T, A_KBATCH, B_SINGLE, E_STORE>(batched(w.duT, f, w.zT, l, dw_u), kWgradGemmTile, st)));
   return LMOE_OK;
 }
 

@@ -1,0 +1,182 @@
+// Per-expert weight gradients with a short reduction:
+//
+//   dW[e] (M x N, row-major) = A_e B_e^T,
+//
+// A_e the row-major [M, K_e] block at element kr_off[e] * M of `a`, B_e the
+// [N, K_e] block at kr_off[e] * N of `b`, K_e = kr_len[e] in {0, 64, 128, 192}
+// (an expert's pairs, zero-padded to a multiple of 64).  M and N are
+// multiples of 128; 16-bit operands, fp32 accumulation.
+//
+// A general GEMM tile spends most of its life waiting for its few K steps'
+// operands.  Here one workgroup (8 waves, 2 x 4) owns an expert's 128-row
+// strip of M: the strip passes through LDS into registers once (the A
+// fragments of every K step, at most 96 VGPRs per lane), then the workgroup
+// sweeps all N / 128 column tiles, with the B operands of the next two
+// column tiles streaming into LDS (LDS-DMA, two buffers) while the current
+// output tile is multiplied, staged in LDS and written back as 16-byte row
+// chunks.
+#pragma once
+
+#include "lmoe_common.h"
+
+namespace lmoe {
+
+constexpr int kWgradKMax = 192;  // largest K_e this kernel takes
+constexpr int kWgradTile = 128;  // rows / columns of a tile
+constexpr int kWgradBuf = kWgradTile * kWgradKMax * 2;  // bytes of one operand tile (48 KB)
+
+typedef __attribute__((address_space(3))) void wg_lds_void_t;
+
+// gfx9 s_waitcnt immediates (expcnt / the counter not named left at "no wait")
+constexpr int wg_vmcnt(int n) { return (n & 0xF) | (((n >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8); }
+constexpr int wg_lgkm0() { return 0xF | (0x3 << 14) | (0x7 << 4); }
+
+// LDS operand layout: KG groups of 32 K values; group g holds the tile's 128
+// rows x 64 bytes at g * 8 KB, row r's four 16-byte chunks XOR-swizzled by
+// (r / 4) % 4 so that a fragment read of 32 consecutive rows hits every bank
+// group evenly.
+__device__ __forceinline__ int wg_pos(int g, int row, int chunk) {
+  return g * (kWgradTile * 64) + row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4);
+}
+
+// LDS-DMA of the [128, K] row slice at `blk` (row stride K elements) into an
+// operand buffer.  Group g is 8 instructions of 1 KB; wave w of NWAVE issues
+// instructions w, w + NWAVE, ...  Instruction i lands rows 16 i .. 16 i + 15:
+// lane l takes row 16 i + l / 4 and the global chunk (l % 4) ^ ((l / 16) % 4),
+// its row's swizzle, so one per-lane byte offset serves every instruction.
+template <int KG, int NWAVE>
+__device__ __forceinline__ void wg_dma(const char* blk, int K, char* buf, int wave, uint32_t lane_off) {
+#pragma unroll
+  for (int g = 0; g < KG; ++g) {
+#pragma unroll
+    for (int ii = 0; ii < 8 / NWAVE; ++ii) {
+      const int inst = wave + NWAVE * ii;
+      const char* src = blk + ((int64_t)inst * 16 * K * 2 + g * 64) + lane_off;
+      __builtin_amdgcn_global_load_lds((const void*)src,
+                                       (wg_lds_void_t*)(buf + g * (kWgradTile * 64) + inst * 1024), 16, 0, 0);
+    }
+  }
+}
+
+// Staged output tile: 128 rows of 256 bytes, 16-byte chunk c of row r at
+// chunk c ^ (r % 16).
+__device__ __forceinline__ int wg_spos(int row, int chunk) { return row * 256 + ((chunk ^ (row & 15)) << 4); }
+
+template <typename TO, int KG>
+__device__ __forceinline__ void wgrad_strip(const char* a_blk, const char* b_blk, int K, int N, char* out,
+                                            int64_t ldo, char* smem) {
+  constexpr int NWAVE = 8, NTHR = 64 * NWAVE;
+  constexpr int KS = 2 * KG;  // MFMA K steps of 16
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // waves 2 (rows) x 4 (columns): 64 x 32 of the tile each
+  const int wm = wave >> 2, wn = wave & 3, lr = lane & 31, lh = lane >> 5;
+  const int NT = N / kWgradTile;
+  char* const S = smem + 2 * kWgradBuf;  // staged output tile
+  auto buf = [&](int t) -> char* { return smem + kWgradBuf * (t & 1); };
+  auto b_tile = [&](int t) { return b_blk + (int64_t)min(t, NT - 1) * kWgradTile * K * 2; };
+  const uint32_t lane_off = (uint32_t)((lane >> 2) * K * 2 + (((lane & 3) ^ ((lane >> 4) & 3)) << 4));
+  auto sync_lds = [&]() {  // this wave's LDS accesses are done, then the workgroup barrier
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(wg_lgkm0());
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+
+  // the A strip through LDS (buffer 1) into registers, B tile 0 meanwhile
+  wg_dma<KG, NWAVE>(a_blk, K, buf(1), wave, lane_off);
+  wg_dma<KG, NWAVE>(b_tile(0), K, buf(0), wave, lane_off);
+  __builtin_amdgcn_s_waitcnt(wg_vmcnt(KG * 8 / NWAVE));  // the A strip has landed
+  __builtin_amdgcn_s_barrier();
+  u32x4 fa[KS][2];
+#pragma unroll
+  for (int s = 0; s < KS; ++s)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      fa[s][i] = *(const u32x4*)(buf(1) + wg_pos(s >> 1, wm * 64 + i * 32 + lr, 2 * (s & 1) + lh));
+  sync_lds();
+  wg_dma<KG, NWAVE>(b_tile(1), K, buf(1), wave, lane_off);
+
+  // per-lane parts of the staging address: row wm*64 + 4*lh (+ constants),
+  // chunk (wn*4 + lr/8) ^ 4*lh (^ constants), byte (lr % 8) * 2
+  const int st_base = (wm * 64 + 4 * lh) * 256 + (lr & 7) * 2;
+  const int st_chunk = (wn * 4 + (lr >> 3)) ^ (4 * lh);
+  constexpr int kStores = kWgradTile * 256 / 16 / NTHR;  // 16-byte stores per thread per tile
+  for (int t = 0; t < NT; ++t) {
+    char* B = buf(t);
+    // B tile t has landed: issued after it are B tile t+1 (t == 0), or the
+    // stores of tile t-1 and B tile t+1
+    if (t == 0) __builtin_amdgcn_s_waitcnt(wg_vmcnt(KG * 8 / NWAVE));
+    else __builtin_amdgcn_s_waitcnt(wg_vmcnt(kStores + KG * 8 / NWAVE));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    f32x16 acc[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][v] = 0.f;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const u32x4 fb = *(const u32x4*)(B + wg_pos(s >> 1, wn * 32 + lr, 2 * (s & 1) + lh));
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, fa[s][i]),
+                                                        __builtin_bit_cast(f16x8, fb), acc[i], 0, 0, 0);
+    }
+    // stage tile t (every wave is past its reads of the staged tile t-1)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        // row = wm*64 + 4*lh + i*32 + 8*(v/4) + v%4, whose low 4 bits are 4*lh + 8*((v/4)%2) + v%4
+        const int rc = i * 32 + 8 * (v >> 2) + (v & 3);
+        const int cx = 8 * ((v >> 2) & 1) + (v & 3);
+        Elem<TO>::store((TO*)(S + st_base + rc * 256 + ((st_chunk ^ cx) << 4)), acc[i][v]);
+      }
+    sync_lds();
+    char* otile = out + (int64_t)t * kWgradTile * 2;
+#pragma unroll
+    for (int q = 0; q < kStores; ++q) {
+      const int id = q * NTHR + tid, row = id >> 4, c = id & 15;
+      *(u32x4*)(otile + row * ldo + c * 16) = *(const u32x4*)(S + wg_spos(row, c));
+    }
+    // every wave is done with B tile t and with the staged tile: the buffer
+    // takes B tile t+2 (tile NT-1 again past the end: the DMA count per step
+    // stays fixed, which keeps the waits above exact)
+    sync_lds();
+    wg_dma<KG, NWAVE>(b_tile(t + 2), K, B, wave, lane_off);
+  }
+  // no LDS-DMA may still be writing when the workgroup's LDS is handed on
+  __builtin_amdgcn_s_waitcnt(wg_vmcnt(0));
+}
+
+template <typename TI, typename TO>
+__global__ __launch_bounds__(512) void wgrad_kernel(const TI* __restrict__ a, const TI* __restrict__ b,
+                                                    const int32_t* __restrict__ kr_off,
+                                                    const int32_t* __restrict__ kr_len, int M, int N,
+                                                    TO* __restrict__ out) {
+  static_assert(sizeof(TI) == 2 && sizeof(TO) == 2, "16-bit operands and output");
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kWgradBuf + kWgradTile * 256];  // 128 KB
+  const int strips = M / kWgradTile;
+  // the strips of one expert are neighbours on one XCD: they share B_e in its L2
+  const int L = xcd_contiguous_id(blockIdx.x, gridDim.x);
+  const int e = L / strips, ms = L % strips;
+  const int K = kr_len[e];
+  const int64_t ldo = (int64_t)N * 2;
+  char* o = (char*)(out + ((int64_t)e * M + (int64_t)ms * kWgradTile) * N);
+  const char* ab = (const char*)(a + (int64_t)kr_off[e] * M + (int64_t)ms * kWgradTile * K);
+  const char* bb = (const char*)(b + (int64_t)kr_off[e] * N);
+  switch (K) {
+    case 64: wgrad_strip<TO, 2>(ab, bb, K, N, o, ldo, smem); break;
+    case 128: wgrad_strip<TO, 4>(ab, bb, K, N, o, ldo, smem); break;
+    case 192: wgrad_strip<TO, 6>(ab, bb, K, N, o, ldo, smem); break;
+    default: {  // no pairs: a zero gradient (K above the maximum never reaches here)
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      const int chunks = N / 8;  // 16-byte chunks per row
+      for (int id = threadIdx.x; id < kWgradTile * chunks; id += 512)
+        *(u32x4*)(o + (int64_t)(id / chunks) * ldo + (id % chunks) * 16) = z;
+    }
+  }
+}
+
+}  // namespace lmoe

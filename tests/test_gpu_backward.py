@@ -97,7 +97,16 @@ def _cfgs():
         base["toy_n128"].with_(name="toy_n3_sparse", n_tokens=3),
         S.LayerConfig("kR_bf16", 70, 128, 64, 6, 6, 3, 128, 64, "bf16", seed=8, bias="uniform"),
         S.LayerConfig("wide_k_bf16", 333, 256, 128, 40, 9, 1, 192, 256, "bf16", seed=9, bias="uniform"),
+        # 128-multiple widths with every padded pair count 0/64/128/192 (largest 182):
+        # the strip weight-gradient kernel; 420 tokens push one expert to 194
+        # pairs and the batched GEMM path instead
+        _STRIP,
+        _STRIP.with_(name="strip_over_bf16", n_tokens=420),
     ]
+
+
+_STRIP = S.LayerConfig("strip_bf16", 400, 256, 256, 24, 2, 1, 256, 256, "bf16", seed=11, bias="quadratic",
+                       router_skew_rows=3, router_skew=2.5)
 
 
 @pytest.mark.parametrize("cfg", _cfgs(), ids=lambda c: c.name)
@@ -200,6 +209,7 @@ def _layer_cfgs():
         base["toy_n128"].with_(name="toy_noshared", n_shared=0),
         S.LayerConfig("kR_bf16", 70, 128, 64, 6, 6, 3, 128, 64, "bf16", seed=8, bias="uniform"),
         S.LayerConfig("wide_k_bf16", 333, 256, 128, 40, 9, 1, 192, 256, "bf16", seed=9, bias="uniform"),
+        _STRIP,
     ]
 
 
