@@ -674,7 +674,7 @@ lmoe_status routed_gradients(const Plan& p, const lmoe_dims* dm, const void* z, 
   if constexpr (sizeof(TI) == 2 && sizeof(T) == 2) {
     if ((C + 63) / 64 * 64 <= kWgradKMax && l % kWgradTile == 0 && f % kWgradTile == 0) {
       auto strips = [&](const void* a, int M, const void* b, int N, void* out) -> lmoe_status {
-        wgrad_kernel<TI, T><<<(unsigned)((int64_t)R * (M / kWgradTile)), 512, 0, st>>>(
+        wgrad_kernel<TI, T><<<(unsigned)((int64_t)R * (M / kWgradTile)), 256, 0, st>>>(
             (const TI*)a, (const TI*)b, w.kr_off, w.kr_len, M, N, (T*)out);
         LMOE_HIP(hipGetLastError());
         return LMOE_OK;

@@ -8,13 +8,13 @@
 // multiples of 128; 16-bit operands, fp32 accumulation.
 //
 // A general GEMM tile spends most of its life waiting for its few K steps'
-// operands.  Here one workgroup (8 waves, 2 x 4) owns an expert's 128-row
+// operands.  Here one workgroup (4 waves, 2 x 2) owns an expert's 128-row
 // strip of M: the strip passes through LDS into registers once (the A
 // fragments of every K step, at most 96 VGPRs per lane), then the workgroup
-// sweeps all N / 128 column tiles, with the B operands of the next two
-// column tiles streaming into LDS (LDS-DMA, two buffers) while the current
-// output tile is multiplied, staged in LDS and written back as 16-byte row
-// chunks.
+// sweeps all N / 128 column tiles.  The next column tile's B operand streams
+// into LDS (LDS-DMA) while the current output tile is staged in LDS and
+// written back as 16-byte row chunks; with 80 KB of LDS two workgroups share
+// a compute unit, so one multiplies while the other stages and stores.
 #pragma once
 
 #include "lmoe_common.h"
@@ -65,14 +65,14 @@ __device__ __forceinline__ int wg_spos(int row, int chunk) { return row * 256 + 
 template <typename TO, int KG>
 __device__ __forceinline__ void wgrad_strip(const char* a_blk, const char* b_blk, int K, int N, char* out,
                                             int64_t ldo, char* smem) {
-  constexpr int NWAVE = 8, NTHR = 64 * NWAVE;
+  constexpr int NWAVE = 4, NTHR = 64 * NWAVE;
   constexpr int KS = 2 * KG;  // MFMA K steps of 16
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // waves 2 (rows) x 4 (columns): 64 x 32 of the tile each
-  const int wm = wave >> 2, wn = wave & 3, lr = lane & 31, lh = lane >> 5;
+  // waves 2 (rows) x 2 (columns): 64 x 64 of the tile each
+  const int wm = wave >> 1, wn = wave & 1, lr = lane & 31, lh = lane >> 5;
   const int NT = N / kWgradTile;
-  char* const S = smem + 2 * kWgradBuf;  // staged output tile
-  auto buf = [&](int t) -> char* { return smem + kWgradBuf * (t & 1); };
+  char* const B = smem;               // operand tile (the A strip first, then B tiles)
+  char* const S = smem + kWgradBuf;   // staged output tile
   auto b_tile = [&](int t) { return b_blk + (int64_t)min(t, NT - 1) * kWgradTile * K * 2; };
   const uint32_t lane_off = (uint32_t)((lane >> 2) * K * 2 + (((lane & 3) ^ ((lane >> 4) & 3)) << 4));
   auto sync_lds = [&]() {  // this wave's LDS accesses are done, then the workgroup barrier
@@ -82,57 +82,65 @@ __device__ __forceinline__ void wgrad_strip(const char* a_blk, const char* b_blk
     asm volatile("" ::: "memory");
   };
 
-  // the A strip through LDS (buffer 1) into registers, B tile 0 meanwhile
-  wg_dma<KG, NWAVE>(a_blk, K, buf(1), wave, lane_off);
-  wg_dma<KG, NWAVE>(b_tile(0), K, buf(0), wave, lane_off);
-  __builtin_amdgcn_s_waitcnt(wg_vmcnt(KG * 8 / NWAVE));  // the A strip has landed
+  // the A strip through LDS into registers
+  wg_dma<KG, NWAVE>(a_blk, K, B, wave, lane_off);
+  __builtin_amdgcn_s_waitcnt(wg_vmcnt(0));
   __builtin_amdgcn_s_barrier();
   u32x4 fa[KS][2];
 #pragma unroll
   for (int s = 0; s < KS; ++s)
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-      fa[s][i] = *(const u32x4*)(buf(1) + wg_pos(s >> 1, wm * 64 + i * 32 + lr, 2 * (s & 1) + lh));
+      fa[s][i] = *(const u32x4*)(B + wg_pos(s >> 1, wm * 64 + i * 32 + lr, 2 * (s & 1) + lh));
   sync_lds();
-  wg_dma<KG, NWAVE>(b_tile(1), K, buf(1), wave, lane_off);
+  wg_dma<KG, NWAVE>(b_tile(0), K, B, wave, lane_off);
 
   // per-lane parts of the staging address: row wm*64 + 4*lh (+ constants),
-  // chunk (wn*4 + lr/8) ^ 4*lh (^ constants), byte (lr % 8) * 2
+  // chunk (wn*8 + lr/8) ^ 4*lh (^ constants), byte (lr % 8) * 2
   const int st_base = (wm * 64 + 4 * lh) * 256 + (lr & 7) * 2;
-  const int st_chunk = (wn * 4 + (lr >> 3)) ^ (4 * lh);
+  const int st_chunk = (wn * 8 + (lr >> 3)) ^ (4 * lh);
   constexpr int kStores = kWgradTile * 256 / 16 / NTHR;  // 16-byte stores per thread per tile
   for (int t = 0; t < NT; ++t) {
-    char* B = buf(t);
-    // B tile t has landed: issued after it are B tile t+1 (t == 0), or the
-    // stores of tile t-1 and B tile t+1
-    if (t == 0) __builtin_amdgcn_s_waitcnt(wg_vmcnt(KG * 8 / NWAVE));
-    else __builtin_amdgcn_s_waitcnt(wg_vmcnt(kStores + KG * 8 / NWAVE));
+    // B tile t has landed: issued after it are the stores of tile t-1 (none before tile 0)
+    if (t == 0) __builtin_amdgcn_s_waitcnt(wg_vmcnt(0));
+    else __builtin_amdgcn_s_waitcnt(wg_vmcnt(kStores));
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    f32x16 acc[2];
+    f32x16 acc[2][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][v] = 0.f;
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const u32x4 fb = *(const u32x4*)(B + wg_pos(s >> 1, wn * 32 + lr, 2 * (s & 1) + lh));
+      u32x4 fb[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) fb[j] = *(const u32x4*)(B + wg_pos(s >> 1, wn * 64 + j * 32 + lr, 2 * (s & 1) + lh));
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, fa[s][i]),
-                                                        __builtin_bit_cast(f16x8, fb), acc[i], 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, fa[s][i]),
+                                                             __builtin_bit_cast(f16x8, fb[j]), acc[i][j], 0, 0, 0);
     }
-    // stage tile t (every wave is past its reads of the staged tile t-1)
+    // every wave is done with B tile t and with the staged tile t-1: B tile
+    // t+1 streams in while tile t is staged and stored
+    sync_lds();
+    if (t + 1 < NT) wg_dma<KG, NWAVE>(b_tile(t + 1), K, B, wave, lane_off);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        // row = wm*64 + 4*lh + i*32 + 8*(v/4) + v%4, whose low 4 bits are 4*lh + 8*((v/4)%2) + v%4
-        const int rc = i * 32 + 8 * (v >> 2) + (v & 3);
-        const int cx = 8 * ((v >> 2) & 1) + (v & 3);
-        Elem<TO>::store((TO*)(S + st_base + rc * 256 + ((st_chunk ^ cx) << 4)), acc[i][v]);
-      }
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          // row = wm*64 + 4*lh + i*32 + 8*(v/4) + v%4, whose low 4 bits are 4*lh + 8*((v/4)%2) + v%4
+          const int rc = i * 32 + 8 * (v >> 2) + (v & 3);
+          const int cx = 8 * ((v >> 2) & 1) + (v & 3);
+          Elem<TO>::store((TO*)(S + st_base + rc * 256 + ((st_chunk ^ (4 * j) ^ cx) << 4)), acc[i][j][v]);
+        }
     sync_lds();
     char* otile = out + (int64_t)t * kWgradTile * 2;
 #pragma unroll
@@ -140,23 +148,18 @@ __device__ __forceinline__ void wgrad_strip(const char* a_blk, const char* b_blk
       const int id = q * NTHR + tid, row = id >> 4, c = id & 15;
       *(u32x4*)(otile + row * ldo + c * 16) = *(const u32x4*)(S + wg_spos(row, c));
     }
-    // every wave is done with B tile t and with the staged tile: the buffer
-    // takes B tile t+2 (tile NT-1 again past the end: the DMA count per step
-    // stays fixed, which keeps the waits above exact)
-    sync_lds();
-    wg_dma<KG, NWAVE>(b_tile(t + 2), K, B, wave, lane_off);
   }
   // no LDS-DMA may still be writing when the workgroup's LDS is handed on
   __builtin_amdgcn_s_waitcnt(wg_vmcnt(0));
 }
 
 template <typename TI, typename TO>
-__global__ __launch_bounds__(512) void wgrad_kernel(const TI* __restrict__ a, const TI* __restrict__ b,
+__global__ __launch_bounds__(256, 2) void wgrad_kernel(const TI* __restrict__ a, const TI* __restrict__ b,
                                                     const int32_t* __restrict__ kr_off,
                                                     const int32_t* __restrict__ kr_len, int M, int N,
                                                     TO* __restrict__ out) {
   static_assert(sizeof(TI) == 2 && sizeof(TO) == 2, "16-bit operands and output");
-  __shared__ __attribute__((aligned(1024))) char smem[2 * kWgradBuf + kWgradTile * 256];  // 128 KB
+  __shared__ __attribute__((aligned(1024))) char smem[kWgradBuf + kWgradTile * 256];  // 80 KB: two per CU
   const int strips = M / kWgradTile;
   // the strips of one expert are neighbours on one XCD: they share B_e in its L2
   const int L = xcd_contiguous_id(blockIdx.x, gridDim.x);
@@ -173,7 +176,7 @@ __global__ __launch_bounds__(512) void wgrad_kernel(const TI* __restrict__ a, co
     default: {  // no pairs: a zero gradient (K above the maximum never reaches here)
       const u32x4 z = {0u, 0u, 0u, 0u};
       const int chunks = N / 8;  // 16-byte chunks per row
-      for (int id = threadIdx.x; id < kWgradTile * chunks; id += 512)
+      for (int id = threadIdx.x; id < kWgradTile * chunks; id += 256)
         *(u32x4*)(o + (int64_t)(id / chunks) * ldo + (id % chunks) * 16) = z;
     }
   }
