@@ -117,7 +117,7 @@ def backward_leg(cfg, ids, probs, steps: int, warmup: int):
     out = {"ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 1), "algorithmic_flops": flops,
            "algorithmic_bytes": by, "hbm_gbs": round(by / ms / 1e6, 1),
            "roofline_frac_hbm": round(by / ms / 1e6 / PEAK_HBM_GBS, 4),
-           "note": "includes per-call transposes of the routed weights (2 x their bytes) and one host sync"}
+           "note": "includes recomputing the routed forward quantities and one host sync"}
     del dev, dw, ws
     torch.cuda.empty_cache()
     return out
