@@ -88,7 +88,16 @@ struct GemmArgs {
   const int32_t* kr_off;
   const int32_t* kr_len;
   int nbatch;
-  int64_t o_batch_stride;  // bytes
+  int64_t o_batch_stride;  // bytes (A_KBATCH: per batch; split K: per K slice)
+  // split K (A_DENSE with E_STORE, ksplit > 1): slice s covers K steps
+  // [s * kslice, min((s + 1) * kslice, K steps)) and stores its partial
+  // product at out + s * o_batch_stride
+  int ksplit;
+  int kslice;
+  // host side only: fp32 workspace for the K slices of few-row products
+  // (NULL: no split)
+  char* part;
+  int64_t part_bytes;
   // out
   char* out;
   int64_t ldo;  // bytes (E_SLOTS: fp32 elements per slot row * 4)
@@ -150,6 +159,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
   constexpr int TM = WTM / 32, TN = WTN / 32;
   constexpr bool GROUPED = AMODE == A_GATHER || AMODE == A_PADDED || AMODE == A_SORTED;
   constexpr bool KBATCH = AMODE == A_KBATCH;
+  const bool split = AMODE == A_DENSE && EMODE == E_STORE && args.ksplit > 1;  // uniform
   // K step: KB bytes of every tile row = NCH 16-byte chunks.  One LDS-DMA
   // wave instruction moves 64 lanes x 16 bytes = RPI tile rows.
   static_assert(KB == 64 || KB == 128, "K step of 64 or 128 bytes");
@@ -191,9 +201,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
     nt = L % args.n_tiles;
   } else {
     const int per = args.m_tiles * args.n_tiles;
-    const int total = per * (KBATCH ? args.nbatch : 1);
+    const int total = per * (KBATCH ? args.nbatch : split ? args.ksplit : 1);
     int L = xcd_contiguous_id(blockIdx.x, total);
-    if constexpr (KBATCH) {
+    if (KBATCH || split) {  // batch / K slice
       e_batch = L / per;
       L -= e_batch * per;
     }
@@ -222,7 +232,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
   const int klen = KBATCH ? args.kr_len[e_batch] : args.K;
   const int64_t lda = KBATCH ? (int64_t)klen * (int64_t)sizeof(TA) : args.lda;  // bytes
   const int64_t ldb = KBATCH ? (int64_t)klen * (int64_t)sizeof(TB) : args.ldb;
-  char* const outp = args.out + (KBATCH ? e_batch * args.o_batch_stride : 0);
+  char* const outp = args.out + ((KBATCH || split) ? e_batch * args.o_batch_stride : 0);
+  const int kt0 = split ? e_batch * args.kslice : 0;  // first K step of this workgroup's slice
+  const int64_t k0b = (int64_t)kt0 * ROWB;
   // E_SLOTS: slot row q and weight p_q of every tile row, fetched now (their
   // latency hides behind the main loop) into LDS outside the operand ring;
   // the main loop's barriers publish them to every wave.
@@ -255,7 +267,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
   if constexpr (AMODE == A_GATHER) a_base = args.a;
   else if constexpr (AMODE == A_PADDED) a_base = args.a + ((int64_t)e * args.cap + m0) * args.lda;
   else if constexpr (AMODE == A_SORTED) a_base = args.a + (off + m0) * args.lda;
-  else a_base = args.a + (int64_t)kbeg * args.M * (int64_t)sizeof(TA) + (int64_t)m0 * lda;
+  else a_base = args.a + (int64_t)kbeg * args.M * (int64_t)sizeof(TA) + (int64_t)m0 * lda + k0b;
 #pragma unroll
   for (int ii = 0; ii < A_W; ++ii) {
     const int rr = min((wave * A_W + ii) * RPI + lane / NCH, rows_valid - 1);
@@ -299,7 +311,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
     const int br = min(up ? r - H : r, b_rows_here - 1);
     b_brow[ii] = br;
     b_base[ii] = (up ? args.b1 : args.b0) + (int64_t)e * args.b_expert_stride +
-                 (int64_t)kbeg * args.nb_rows * (int64_t)sizeof(TB) + (int64_t)nt * H * ldb;
+                 (int64_t)kbeg * args.nb_rows * (int64_t)sizeof(TB) + (int64_t)nt * H * ldb + k0b;
     b_chunk[ii] = lane_chunk(wave * B_W + ii);
     b_off[ii] = (uint32_t)(br * ldb) + b_chunk[ii];
   }
@@ -313,11 +325,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
   auto b_step = [&](int kt) -> BStep {
     if constexpr (BMODE == B_KSEG) {
       constexpr int U = KB / kSegUnit;  // segment units per K step
+      const int kta = kt + kt0;         // K step within the whole K range
       int s = 0;
-      while (s + 1 < args.nseg && kt * U >= args.seg_kt0[s + 1]) ++s;
+      while (s + 1 < args.nseg && kta * U >= args.seg_kt0[s + 1]) ++s;
       const int64_t ld = args.seg_ld[s];
       return {args.seg_base[s] + (int64_t)nt * BN * ld +
-                  ((int64_t)kt * ROWB - (int64_t)args.seg_kt0[s] * kSegUnit),
+                  ((int64_t)kta * ROWB - (int64_t)args.seg_kt0[s] * kSegUnit),
               ld};
     } else {
       return {nullptr, 0};
@@ -332,7 +345,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
     if constexpr (BMODE == B_KSEG) {
       g = bs.base + ((uint32_t)(b_brow[ii] * bs.ld) + b_chunk[ii]);
     } else if constexpr (BMODE == B_KMAJOR) {
-      const int k0 = kt * KE;  // first K row of the step (workgroup-uniform)
+      const int k0 = (kt + kt0) * KE;  // first K row of the step (workgroup-uniform)
       const char* rows = k0 < args.kmaj_split ? kmaj_b0 + (int64_t)k0 * ldb
                                               : kmaj_b1 + (int64_t)(k0 - args.kmaj_split) * ldb;
       g = rows + b_off[ii];
@@ -397,7 +410,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
   constexpr int kNewer = (kAFirst ? B_W : 0) + (SA - 2) * NI;  // vmcnt at the barrier of a step
   constexpr int kNewer0 = kNewer + NI;                          // vmcnt before step 0
   static_assert(kNewer0 < 64, "vmcnt range");
-  const int KT = klen * (int)sizeof(TA) / ROWB;  // 0 only for an empty A_KBATCH range
+  const int KT_all = klen * (int)sizeof(TA) / ROWB;  // 0 only for an empty A_KBATCH range
+  const int KT = split ? min(args.kslice, KT_all - kt0) : KT_all;  // K steps of this workgroup
   auto clampt = [&](int t) { return t < KT ? t : KT - 1; };
   // issue the DMA of A tile ta into A stage sa and B tile tb into B stage sb
   auto dma_step = [&](int ta, char* sa, int tb, char* sb) {
@@ -650,6 +664,19 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
         }
       }
     }
+  }
+}
+
+// Sum of the K slices' fp32 partial products in slice order, stored as OutT:
+// out[m, n] = sum over s of part[s][m][n]  (part [S, M, N], out row stride ldo bytes).
+template <typename OutT>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int S, int M, int N,
+                                                            char* __restrict__ out, int64_t ldo) {
+  const int64_t MN = (int64_t)M * N;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < MN; i += (int64_t)gridDim.x * 256) {
+    float acc = 0.f;
+    for (int sl = 0; sl < S; ++sl) acc += part[sl * MN + i];
+    Elem<OutT>::store((OutT*)(out + (i / N) * ldo) + i % N, acc);
   }
 }
 

@@ -112,6 +112,27 @@ lmoe_status check_dims(const lmoe_dims* dm, Plan* p) {
 }
 
 // Bump allocator over the caller's workspace (256-byte aligned regions).
+// Split K for few-row dense products (the 64-row tile): with M <= 64 a
+// product has only N / 128 tiles, too few to stream its weights at HBM rate,
+// so K is cut into S slices (>= 8 K steps each) until about 512 workgroups
+// run; each slice stores an fp32 partial product and one pass sums them in
+// slice order.  Returns the slice count (1: no split) and its workspace bytes.
+int splitk_slices(int64_t M, int64_t N, int64_t k_bytes, int64_t part_bytes, int* kslice) {
+  const int64_t steps = k_bytes / 128;  // K steps of the 64-row tile
+  const int64_t tiles = ((M + 63) / 64) * ((N + 127) / 128);
+  int64_t S = std::min<int64_t>({(512 + tiles - 1) / tiles, steps / 8, 32});
+  while (S > 1 && S * M * N * 4 > part_bytes) --S;
+  if (S < 2) return 1;
+  const int64_t per = (steps + S - 1) / S;
+  *kslice = (int)per;
+  return (int)((steps + per - 1) / per);  // every slice non-empty
+}
+int64_t splitk_bytes(int64_t M, int64_t N, int64_t k_bytes) {
+  int kslice = 0;
+  const int S = splitk_slices(M, N, k_bytes, INT64_MAX, &kslice);
+  return S > 1 ? (int64_t)S * M * N * 4 : 0;
+}
+
 struct Carver {
   char* base;
   size_t off = 0;
@@ -150,6 +171,8 @@ struct ForwardWs {
   char* h;
   char* slots;
   char* hcat;
+  char* part;  // fp32 K-slice partials of the few-row dense products
+  int64_t part_bytes;
 };
 
 size_t carve_route(const Plan& p, char* b, RouteWs* w) {
@@ -185,6 +208,12 @@ size_t carve_forward(const Plan& p, char* b, ForwardWs* w) {
   w->h = c.take<char>((size_t)p.pairs * p.fr * p.es);
   w->slots = c.take<char>((size_t)p.pairs * p.l * p.es);
   w->hcat = c.take<char>((size_t)p.N * p.ldh * p.es);
+  // split-K partials of the latent, router and merge products (used up to 64
+  // rows; sized for min(N, 64) rows so the workspace never shrinks as N grows)
+  const int64_t pr = std::min<int64_t>(p.N, 64);
+  w->part_bytes = std::max({splitk_bytes(pr, p.l, (int64_t)p.d * p.es), splitk_bytes(pr, p.R, (int64_t)p.d * p.es),
+                            splitk_bytes(pr, p.d, p.ldh * p.es)});
+  w->part = c.take<char>((size_t)w->part_bytes);
   return c.off;
 }
 
@@ -307,7 +336,7 @@ lmoe_status side_stream(hipStream_t* out) {
 template <typename TA, typename TB, typename OutT, int BM, int BN, int WGM, int WGN, int AM, int BMD,
           int EM, int SA, int SB, int KB>
 lmoe_status launch_gemm(GemmArgs a, hipStream_t st) {
-  const int64_t grid = (int64_t)a.m_tiles * a.n_tiles * (AM == A_KBATCH ? a.nbatch : 1);
+  const int64_t grid = (int64_t)a.m_tiles * a.n_tiles * (AM == A_KBATCH ? a.nbatch : a.ksplit > 1 ? a.ksplit : 1);
   if (grid <= 0) return LMOE_OK;
   if (grid > INT32_MAX) return fail(LMOE_ERR_UNSUPPORTED, "GEMM grid too large");
   gemm_kernel<TA, TB, OutT, BM, BN, WGM, WGN, AM, BMD, EM, SA, SB, KB>
@@ -349,6 +378,28 @@ lmoe_status gemm_cfg(GemmArgs a, hipStream_t st) {
 template <typename TA, typename TB, typename OutT, int AM, int BMD, int EM>
 lmoe_status gemm(GemmArgs a, Tile t, hipStream_t st) {
   constexpr bool dual = BMD == B_DUAL;
+  if constexpr (AM == A_DENSE && EM == E_STORE && !dual) {
+    int kslice = 0;
+    const int S = (t == TILE_S && a.part && a.M <= 64)
+                      ? splitk_slices(a.M, a.N, (int64_t)a.K * sizeof(TA), a.part_bytes, &kslice)
+                      : 1;
+    if (S > 1) {
+      GemmArgs g = a;
+      g.out = a.part;
+      g.ldo = (int64_t)a.N * 4;
+      g.o_batch_stride = (int64_t)a.M * a.N * 4;
+      g.ksplit = S;
+      g.kslice = kslice;
+      g.part = nullptr;
+      const lmoe_status ps = gemm_cfg<TA, TB, float, AM, BMD, EM, 64, 128, 1, 4, 3, 3, 128>(g, st);
+      if (ps != LMOE_OK) return ps;
+      const int64_t mn = (int64_t)a.M * a.N;
+      splitk_reduce_kernel<OutT><<<(unsigned)std::min<int64_t>((mn + 255) / 256, 2048), 256, 0, st>>>(
+          (const float*)a.part, S, a.M, a.N, a.out, a.ldo);
+      LMOE_HIP(hipGetLastError());
+      return LMOE_OK;
+    }
+  }
   if constexpr (AM == A_DENSE || AM == A_KBATCH) {
     switch (t) {
       case TILE_S: return gemm_cfg<TA, TB, OutT, AM, BMD, EM, 64, dual ? 256 : 128, 1, 4, 3, 3, 128>(a, st);
@@ -393,7 +444,7 @@ GemmArgs base_args(const lmoe_dims* dm) {
 template <typename T>
 lmoe_status run_route(const Plan& p, const lmoe_dims* dm, const void* x, const void* w_router,
                       const float* bias, int32_t* ids, float* probs, float* logits, hipStream_t st,
-                      bool softmax = false) {
+                      bool softmax = false, char* part = nullptr, int64_t part_bytes = 0) {
   GemmArgs a = base_args(dm);
   a.M = (int)p.N;
   a.N = p.R;
@@ -405,6 +456,8 @@ lmoe_status run_route(const Plan& p, const lmoe_dims* dm, const void* x, const v
   a.nb_rows = p.R;
   a.out = (char*)logits;
   a.ldo = (int64_t)p.R * 4;
+  a.part = part;
+  a.part_bytes = part_bytes;
   LMOE_TRY((gemm<T, T, float, A_DENSE, B_SINGLE, E_STORE>(a, dense_tile(p.N, p.R, false), st)));
   const unsigned blocks = (unsigned)((p.N + 3) / 4);
   if (softmax)
@@ -919,10 +972,12 @@ lmoe_status run_forward(const Plan& p, const lmoe_dims* dm, const lmoe_weights* 
   a.nb_rows = p.l;
   a.out = w.z;
   a.ldo = (int64_t)p.l * p.es;
+  a.part = w.part;
+  a.part_bytes = w.part_bytes;
   LMOE_TRY((gemm<T, T, TI, A_DENSE, B_SINGLE, E_STORE>(a, dense_tile(p.N, p.l, false), st)));
   LMOE_TRY(mark());
   // 2. routing
-  LMOE_TRY(run_route<T>(p, dm, x, W->w_router, W->bias, ids, probs, w.logits, st));
+  LMOE_TRY(run_route<T>(p, dm, x, W->w_router, W->bias, ids, probs, w.logits, st, false, w.part, w.part_bytes));
   LMOE_TRY(mark());
   // 3a. dispatch bookkeeping
   LMOE_TRY(run_dispatch(p, ids, w.chunk_hist, w.chunk_bad, counts, w.offsets, w.order, w.meta, st));
@@ -963,6 +1018,8 @@ lmoe_status run_forward(const Plan& p, const lmoe_dims* dm, const lmoe_weights* 
   f.seg_kt0[p.ns + 1] = (int)(p.ldh * p.es / kSegUnit);
   f.out = (char*)y;
   f.ldo = (int64_t)p.d * p.es;
+  f.part = w.part;
+  f.part_bytes = w.part_bytes;
   LMOE_TRY((gemm<TI, T, T, A_DENSE, B_KSEG, E_STORE>(f, dense_tile(p.N, p.d, false), st)));
   return mark();
 }

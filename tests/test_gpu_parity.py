@@ -39,6 +39,10 @@ def _small_cfgs():
         S.LayerConfig("kR_f32", 50, 128, 64, 8, 8, 1, 64, 128, "f32", seed=7),
         S.LayerConfig("kR_bf16", 70, 128, 64, 6, 6, 3, 128, 64, "bf16", seed=8, bias="uniform"),
         S.LayerConfig("wide_k_bf16", 333, 256, 128, 40, 9, 1, 192, 256, "bf16", seed=9, bias="uniform"),
+        # few rows with a long K: the latent, router and merge products run split-K
+        # (4 slices each, the merge's slices crossing its shared / W_up segment boundary)
+        S.LayerConfig("wide_d_bf16_n40", 40, 2048, 256, 16, 4, 1, 256, 2048, "bf16", seed=13, bias="uniform"),
+        S.LayerConfig("wide_d_f32_n17", 17, 1024, 128, 16, 2, 1, 128, 1024, "f32", seed=14),
     ]
 
 
