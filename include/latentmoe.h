@@ -199,8 +199,10 @@ lmoe_status latentmoe_forward(const lmoe_dims* dims, const lmoe_weights* weights
  * intermediates are fp16 (as in the forward).  The pre-activations are
  * recomputed from z.  Reads C back (waits on `stream` once); the rest is
  * asynchronous.  Workspace: latentmoe_workspace_bytes(dims,
- * LMOE_ENTRY_ROUTED_BACKWARD) bytes of device memory (it holds transposed
- * copies of the routed weights).  Errors: INVALID_ARGUMENT for bad dims, NULL
+ * LMOE_ENTRY_ROUTED_BACKWARD) bytes of device memory (the recomputed pair
+ * quantities and per-expert transposed pair blocks; with fp32 storage also
+ * transposed copies of the routed weights, 16-bit weights are read as stored).
+ * Errors: INVALID_ARGUMENT for bad dims, NULL
  * pointers or ids outside [0, R); WORKSPACE. */
 lmoe_status latentmoe_routed_backward(const lmoe_dims* dims, const void* z, const int32_t* ids,
                                       const float* probs, const void* w_g, const void* w_u,

@@ -287,7 +287,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
     return r * ROWK + (((n >> 3) ^ kmaj_sw(r)) << 4) + (n & 7) * 2;
   };
   const char* kmaj_b0 = args.b0 + (int64_t)e * args.b_expert_stride;
-  const char* kmaj_b1 = args.b1 + (int64_t)e * args.b_expert_stride;
+  const char* kmaj_b1 = args.b1 ? args.b1 + (int64_t)e * args.b_expert_stride : kmaj_b0;
 
   const char* b_base[B_W];  // workgroup-uniform
   uint32_t b_off[B_W];      // per lane, K step 0
