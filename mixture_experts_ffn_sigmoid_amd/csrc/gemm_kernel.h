@@ -669,14 +669,39 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
 
 // Sum of the K slices' fp32 partial products in slice order, stored as OutT:
 // out[m, n] = sum over s of part[s][m][n]  (part [S, M, N], out row stride ldo bytes).
+// Four consecutive columns per thread (N % 4 == 0: 16-byte loads), the slice
+// loads issued four at a time.
 template <typename OutT>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int S, int M, int N,
                                                             char* __restrict__ out, int64_t ldo) {
   const int64_t MN = (int64_t)M * N;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < MN; i += (int64_t)gridDim.x * 256) {
-    float acc = 0.f;
-    for (int sl = 0; sl < S; ++sl) acc += part[sl * MN + i];
-    Elem<OutT>::store((OutT*)(out + (i / N) * ldo) + i % N, acc);
+  const bool vec = (N & 3) == 0;
+  for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; i < MN; i += (int64_t)gridDim.x * 1024) {
+    const int64_t m = i / N, n = i % N;
+    OutT* dst = (OutT*)(out + m * ldo) + n;
+    if (vec) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      int sl = 0;
+      for (; sl + 4 <= S; sl += 4) {
+        const f32x4 a = *(const f32x4*)(part + sl * MN + i), b = *(const f32x4*)(part + (sl + 1) * MN + i);
+        const f32x4 c = *(const f32x4*)(part + (sl + 2) * MN + i), d = *(const f32x4*)(part + (sl + 3) * MN + i);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[q] = (((acc[q] + a[q]) + b[q]) + c[q]) + d[q];
+      }
+      for (; sl < S; ++sl) {
+        const f32x4 a = *(const f32x4*)(part + sl * MN + i);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[q] += a[q];
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) Elem<OutT>::store(dst + q, acc[q]);
+    } else {
+      for (int64_t j = i; j < i + 4 && j < MN; ++j) {
+        float acc = 0.f;
+        for (int sl = 0; sl < S; ++sl) acc += part[sl * MN + j];
+        Elem<OutT>::store((OutT*)(out + (j / N) * ldo) + j % N, acc);
+      }
+    }
   }
 }
 

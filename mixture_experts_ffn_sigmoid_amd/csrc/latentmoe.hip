@@ -394,7 +394,7 @@ lmoe_status gemm(GemmArgs a, Tile t, hipStream_t st) {
       const lmoe_status ps = gemm_cfg<TA, TB, float, AM, BMD, EM, 64, 128, 1, 4, 3, 3, 128>(g, st);
       if (ps != LMOE_OK) return ps;
       const int64_t mn = (int64_t)a.M * a.N;
-      splitk_reduce_kernel<OutT><<<(unsigned)std::min<int64_t>((mn + 255) / 256, 2048), 256, 0, st>>>(
+      splitk_reduce_kernel<OutT><<<(unsigned)std::min<int64_t>((mn + 1023) / 1024, 2048), 256, 0, st>>>(
           (const float*)a.part, S, a.M, a.N, a.out, a.ldo);
       LMOE_HIP(hipGetLastError());
       return LMOE_OK;
@@ -479,7 +479,7 @@ lmoe_status run_dispatch(const Plan& p, const int32_t* ids, int32_t* chunk_hist,
   LMOE_HIP(hipGetLastError());
   dispatch_scan_kernel<<<1, 1024, 0, st>>>(chunk_hist, p.nchunks, p.R, counts, offsets, chunk_bad, meta);
   LMOE_HIP(hipGetLastError());
-  dispatch_scatter_kernel<<<p.nchunks, 64, (p.R + 64) * sizeof(int32_t), st>>>(ids, p.pairs, p.R,
+  dispatch_scatter_kernel<<<p.nchunks, 64, p.R * sizeof(int32_t), st>>>(ids, p.pairs, p.R,
                                                                               chunk_hist, order);
   LMOE_HIP(hipGetLastError());
   return LMOE_OK;

@@ -8,6 +8,21 @@ namespace lmoe {
 
 constexpr int kMaxLatent = 8192;  // 8 float4 per thread of a 256-thread workgroup
 
+// Four consecutive elements (8- or 16-byte aligned) widened to fp32.
+template <typename TS>
+__device__ __forceinline__ f32x4 load4(const TS* p) {
+  f32x4 r;
+  if constexpr (sizeof(TS) == 4) {
+    r = *(const f32x4*)p;
+  } else {
+    TS tmp[4];
+    *(u32x2*)tmp = *(const u32x2*)p;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r[q] = Elem<TS>::load(tmp + q);
+  }
+  return r;
+}
+
 // One workgroup per token n (slots of type TS, summed in fp32):
 //   u[c] = sum_{j < k} slots[(n k + j) l + c]      (slot order)
 //   u_out[n, c] = u[c]                               (if u_out)
@@ -29,10 +44,18 @@ __global__ __launch_bounds__(256) void combine_rmsnorm_kernel(const TS* __restri
     const int c = 4 * t + 1024 * i;
     u[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (c < ell) {
-      for (int j = 0; j < k; ++j) {
-        const TS* src = slots + ((n * k + j) * ell + c);
+      const TS* src = slots + (n * k * ell + c);
+      int j = 0;
+      for (; j + 4 <= k; j += 4) {  // four slots' loads in flight, summed in slot order
+        const f32x4 a = load4(src + (int64_t)j * ell), b = load4(src + (int64_t)(j + 1) * ell);
+        const f32x4 cc = load4(src + (int64_t)(j + 2) * ell), d = load4(src + (int64_t)(j + 3) * ell);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) u[i][q] += Elem<TS>::load(src + q);
+        for (int q = 0; q < 4; ++q) u[i][q] = (((u[i][q] + a[q]) + b[q]) + cc[q]) + d[q];
+      }
+      for (; j < k; ++j) {
+        const f32x4 a = load4(src + (int64_t)j * ell);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) u[i][q] += a[q];
       }
       ss += u[i][0] * u[i][0] + u[i][1] * u[i][1] + u[i][2] * u[i][2] + u[i][3] * u[i][3];
       if (u_out) *(f32x4*)(u_out + n * ell + c) = u[i];

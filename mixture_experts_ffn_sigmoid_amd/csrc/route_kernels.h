@@ -31,6 +31,7 @@ __global__ __launch_bounds__(256) void topk_route_kernel(const float* __restrict
 
   float best = -INFINITY;
   int best_id = 0x7fffffff;
+#pragma unroll 8
   for (int e = lane; e < R; e += 64) {
     const float ve = kSoftmax ? lrow[e] : sigmoidf_(lrow[e]) + (bias ? bias[e] : 0.f);
     v[e] = ve;
@@ -41,7 +42,6 @@ __global__ __launch_bounds__(256) void topk_route_kernel(const float* __restrict
   }
 
   int my_id = 0;  // lane j keeps the j-th winner
-  float ssum = 0.f, lmax = 0.f;
   for (int j = 0; j < k; ++j) {
     float bv = best;
     int bi = best_id;
@@ -56,16 +56,11 @@ __global__ __launch_bounds__(256) void topk_route_kernel(const float* __restrict
     }
     if (bi >= R) bi = 0;  // only reachable with NaN scores; keeps every index in range
     if (lane == j) my_id = bi;
-    if constexpr (kSoftmax) {
-      if (j == 0) lmax = lrow[bi];  // the first winner holds the largest logit
-      ssum += expf(lrow[bi] - lmax);
-    } else {
-      ssum += sigmoidf_(lrow[bi]);
-    }
     if ((bi & 63) == lane) {  // owner lane removes the winner and rescans its experts
       v[bi] = -INFINITY;
       best = -INFINITY;
       best_id = 0x7fffffff;
+#pragma unroll 8
       for (int e = lane; e < R; e += 64) {
         const float ve = v[e];
         if (ve > best) {
@@ -75,10 +70,22 @@ __global__ __launch_bounds__(256) void topk_route_kernel(const float* __restrict
       }
     }
   }
+  // weights of the k winners, lane j holding winner j: s_j (softmax: exp of the
+  // logit minus the first winner's, the largest) over their sum, which is
+  // reduced across the wave in a fixed order and taken from lane 0
+  float w = 0.f;
+  if (lane < k) w = kSoftmax ? lrow[my_id] : sigmoidf_(lrow[my_id]);
+  if constexpr (kSoftmax) {
+    const float lmax = __shfl(w, 0);
+    w = lane < k ? expf(w - lmax) : 0.f;
+  }
+  float ssum = w;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) ssum += __shfl_xor(ssum, off);
+  ssum = __shfl(ssum, 0);
   if (lane < k) {
     ids[n * k + lane] = my_id;
-    if constexpr (kSoftmax) probs[n * k + lane] = expf(lrow[my_id] - lmax) / ssum;
-    else probs[n * k + lane] = sigmoidf_(lrow[my_id]) / fmaxf(ssum, 1e-9f);
+    probs[n * k + lane] = kSoftmax ? w / ssum : w / fmaxf(ssum, 1e-9f);
   }
 }
 
@@ -265,40 +272,48 @@ __global__ __launch_bounds__(1024) void tile_list_kernel(const int32_t* __restri
 }
 
 // Dispatch step 3: stable scatter.  One wave per chunk walks its pairs in
-// order, 64 at a time; a pair's rank among equal experts of its batch is the
-// number of lower lanes with the same expert, and a per-expert cursor in LDS
-// (seeded with the chunk's first positions) carries the order across batches.
+// order, 64 at a time (all of the chunk's ids are fetched up front);
+// a pair's rank among equal experts of its batch is the number of lower lanes
+// with the same expert (lane values read across the wave with readlane, no
+// LDS round trip), and a per-expert cursor in LDS (seeded with the chunk's
+// first positions) carries the order across batches.
 __global__ __launch_bounds__(64) void dispatch_scatter_kernel(const int32_t* __restrict__ ids,
                                                               int64_t pairs, int R,
                                                               const int32_t* __restrict__ chunk_base,
                                                               int32_t* __restrict__ order) {
-  extern __shared__ int32_t cursor[];  // [R] then [64] batch experts
-  int32_t* batch = cursor + R;
+  extern __shared__ int32_t cursor[];  // [R]
   const int lane = threadIdx.x;
-  for (int e = lane; e < R; e += 64) cursor[e] = chunk_base[(int64_t)blockIdx.x * R + e];
+  const int32_t* base = chunk_base + (int64_t)blockIdx.x * R;
+#pragma unroll 16
+  for (int e = lane; e < R; e += 64) cursor[e] = base[e];  // loads issued together, not one latency each
   __syncthreads();
   const int64_t q0 = (int64_t)blockIdx.x * kDispatchChunk;
   const int64_t q1 = min(q0 + kDispatchChunk, pairs);
-  for (int64_t qb = q0; qb < q1; qb += 64) {
-    const int64_t q = qb + lane;
-    const bool valid = q < q1;
-    int e = valid ? ids[q] : -1;
-    if (e < 0 || e >= R) e = -1;  // not counted by the histogram either
-    batch[lane] = e;
-    __syncthreads();
+  auto expert_of = [&](int64_t q) -> int {  // -1: past the chunk, or an id outside [0, R) (not counted)
+    if (q >= q1) return -1;
+    const int e = ids[q];
+    return (e >= 0 && e < R) ? e : -1;
+  };
+  constexpr int kBatches = kDispatchChunk / 64;
+  int eb[kBatches];  // the chunk's ids, fetched together
+#pragma unroll
+  for (int b = 0; b < kBatches; ++b) eb[b] = expert_of(q0 + b * 64 + lane);
+#pragma unroll
+  for (int b = 0; b < kBatches; ++b) {
+    const int64_t q = q0 + b * 64 + lane;
+    const int e = eb[b];
     int before = 0, after = 0;
+#pragma unroll 2  // a rolled loop: unrolled, its readlane results exhaust the scalar registers
     for (int j = 0; j < 64; ++j) {
-      const int ej = batch[j];
+      const int ej = __builtin_amdgcn_readlane(e, j);
       before += (j < lane && ej == e) ? 1 : 0;
       after += (j > lane && ej == e) ? 1 : 0;
     }
-    int pos = 0;
     if (e >= 0) {
-      pos = cursor[e] + before;
+      const int pos = cursor[e] + before;
       order[pos] = (int32_t)q;
+      if (after == 0) cursor[e] = pos + 1;  // the batch's last pair of expert e
     }
-    __syncthreads();
-    if (e >= 0 && after == 0) cursor[e] = pos + 1;
     __syncthreads();
   }
 }
