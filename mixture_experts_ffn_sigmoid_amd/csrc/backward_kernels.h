@@ -143,6 +143,58 @@ __global__ __launch_bounds__(256) void segment_transpose_kernel(
   }
 }
 
+// The same segment transpose for 16-bit elements with 16-byte global accesses
+// (TS -> TD converted as the tile is loaded): the 64 x 64 tile is read as
+// 8-element chunks of its source rows and written as 8-element chunks of the
+// block's rows.  ncols, col_off and ld_src are multiples of 8, the buffers
+// 16-byte aligned (kr_len and kr_off are multiples of 64).
+template <typename TS, typename TD>
+__global__ __launch_bounds__(256) void segment_transpose16_kernel(
+    const TS* __restrict__ src, int64_t ld_src, int col_off, int ncols, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ order, int top_k,
+    const int32_t* __restrict__ kr_off, const int32_t* __restrict__ kr_len, TD* __restrict__ out) {
+  static_assert(sizeof(TS) == 2 && sizeof(TD) == 2, "16-bit elements");
+  const int e = blockIdx.z;
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  if (r0 >= kr_len[e]) return;
+  constexpr int LD = 72;  // padded row of the LDS tile (elements)
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64 * LD];
+  const int cnt = counts[e];
+  const int64_t base = offsets[e];
+  const int t = threadIdx.x, q = t & 7;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {  // 64 segment rows x 8 chunks of 8 columns
+    const int r = (t >> 3) + 32 * i, c = c0 + q * 8;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (r0 + r < cnt && c < ncols) {
+      const int64_t row = order ? (int64_t)(order[base + r0 + r] / top_k) : base + r0 + r;
+      v = *(const u32x4*)(src + row * ld_src + col_off + c);
+      if constexpr (!__is_same(TS, TD)) {
+        const TS* in = (const TS*)&v;
+        TD cv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) Elem<TD>::store(cv + j, Elem<TS>::load(in + j));
+        v = *(const u32x4*)cv;
+      }
+    }
+    *(u32x4*)(tile + r * LD + q * 8) = v;
+  }
+  __syncthreads();
+  const int64_t ld = kr_len[e];
+  TD* blk = out + (int64_t)kr_off[e] * ncols;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {  // 64 block rows (columns c) x 8 chunks of 8 segment rows
+    const int c = (t >> 3) + 32 * i;
+    if (c0 + c >= ncols) continue;
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      w[j] = (uint32_t)tile[(q * 8 + 2 * j) * LD + c] | ((uint32_t)tile[(q * 8 + 2 * j + 1) * LD + c] << 16);
+    const u32x4 v = {w[0], w[1], w[2], w[3]};
+    *(u32x4*)(blk + (int64_t)(c0 + c) * ld + r0 + q * 8) = v;
+  }
+}
+
 // h = SiTU hidden of the (gate, up) pre-activations, n elements.
 template <typename TD>
 __global__ __launch_bounds__(256) void situ_hidden_kernel(const float* __restrict__ g, const float* __restrict__ u,

@@ -559,6 +559,26 @@ lmoe_status transpose_batched(const T* in, int64_t in_bstride, int ld_in, int ro
   return LMOE_OK;
 }
 
+// Expert-segment transpose (see segment_transpose_kernel); 16-bit data with
+// 8-element-aligned columns and strides goes through the 16-byte kernel.
+template <typename TS, typename TD>
+lmoe_status segment_transpose(dim3 grid, const TS* src, int64_t ld_src, int col_off, int ncols,
+                              const int32_t* counts, const int32_t* offsets, const int32_t* order, int top_k,
+                              const int32_t* kr_off, const int32_t* kr_len, TD* out, hipStream_t st) {
+  if constexpr (sizeof(TS) == 2 && sizeof(TD) == 2) {
+    if (ncols % 8 == 0 && col_off % 8 == 0 && ld_src % 8 == 0 && (((uintptr_t)src | (uintptr_t)out) & 15) == 0) {
+      segment_transpose16_kernel<TS, TD><<<grid, 256, 0, st>>>(src, ld_src, col_off, ncols, counts, offsets,
+                                                               order, top_k, kr_off, kr_len, out);
+      LMOE_HIP(hipGetLastError());
+      return LMOE_OK;
+    }
+  }
+  segment_transpose_kernel<TS, TD><<<grid, 256, 0, st>>>(src, ld_src, col_off, ncols, counts, offsets, order,
+                                                         top_k, kr_off, kr_len, out);
+  LMOE_HIP(hipGetLastError());
+  return LMOE_OK;
+}
+
 // Grouped-GEMM arguments over the routed pairs of a backward workspace.
 GemmArgs routed_grouped(const Plan& p, const lmoe_dims* dm, const RoutedBwdWs& w, const void* a, int64_t lda,
                         const void* bw, int64_t ldb, int64_t bstride, int nrows, int K, void* out, int64_t ldo) {
@@ -687,21 +707,17 @@ lmoe_status routed_gradients(const Plan& p, const lmoe_dims* dm, const void* z, 
   // 6. weight gradients: per expert, products over its pairs (K = padded pair range)
   const unsigned ysegs = (unsigned)((C + 63) / 64);
   if (ysegs > 0) {
-    segment_transpose_kernel<TI, TI><<<dim3(l / 64, ysegs, R), 256, 0, st>>>(
-        (const TI*)w.dout, l, 0, l, w.counts, w.offsets, nullptr, p.k, w.kr_off, w.kr_len, (TI*)w.doutT);
-    LMOE_HIP(hipGetLastError());
-    segment_transpose_kernel<TI, TI><<<dim3(f / 64, ysegs, R), 256, 0, st>>>(
-        (const TI*)w.hs, f, 0, f, w.counts, w.offsets, nullptr, p.k, w.kr_off, w.kr_len, (TI*)w.hT);
-    LMOE_HIP(hipGetLastError());
-    segment_transpose_kernel<TI, TI><<<dim3(f / 64, ysegs, R), 256, 0, st>>>(
-        (const TI*)w.dgu, 2 * f, 0, f, w.counts, w.offsets, nullptr, p.k, w.kr_off, w.kr_len, (TI*)w.dgT);
-    LMOE_HIP(hipGetLastError());
-    segment_transpose_kernel<TI, TI><<<dim3(f / 64, ysegs, R), 256, 0, st>>>(
-        (const TI*)w.dgu, 2 * f, f, f, w.counts, w.offsets, nullptr, p.k, w.kr_off, w.kr_len, (TI*)w.duT);
-    LMOE_HIP(hipGetLastError());
-    segment_transpose_kernel<TZ, TI><<<dim3(l / 64, ysegs, R), 256, 0, st>>>(
-        (const TZ*)z, l, 0, l, w.counts, w.offsets, w.order, p.k, w.kr_off, w.kr_len, (TI*)w.zT);
-    LMOE_HIP(hipGetLastError());
+    const dim3 gl(l / 64, ysegs, R), gf(f / 64, ysegs, R);
+    LMOE_TRY((segment_transpose<TI, TI>(gl, (const TI*)w.dout, l, 0, l, w.counts, w.offsets, nullptr, p.k,
+                                        w.kr_off, w.kr_len, (TI*)w.doutT, st)));
+    LMOE_TRY((segment_transpose<TI, TI>(gf, (const TI*)w.hs, f, 0, f, w.counts, w.offsets, nullptr, p.k,
+                                        w.kr_off, w.kr_len, (TI*)w.hT, st)));
+    LMOE_TRY((segment_transpose<TI, TI>(gf, (const TI*)w.dgu, 2 * f, 0, f, w.counts, w.offsets, nullptr, p.k,
+                                        w.kr_off, w.kr_len, (TI*)w.dgT, st)));
+    LMOE_TRY((segment_transpose<TI, TI>(gf, (const TI*)w.dgu, 2 * f, f, f, w.counts, w.offsets, nullptr, p.k,
+                                        w.kr_off, w.kr_len, (TI*)w.duT, st)));
+    LMOE_TRY((segment_transpose<TZ, TI>(gl, (const TZ*)z, l, 0, l, w.counts, w.offsets, w.order, p.k,
+                                        w.kr_off, w.kr_len, (TI*)w.zT, st)));
   }
   auto batched = [&](const char* a, int M, const char* b, int N, void* out) {
     GemmArgs g = base_args(dm);
@@ -877,10 +893,8 @@ lmoe_status run_layer_backward(const Plan& p, const lmoe_dims* dm, const lmoe_we
   const unsigned ny = (unsigned)(npad / 64);
   auto tr = [&](auto src_c, int64_t ld_src, int64_t col0, int ncols, char* out) -> lmoe_status {
     using TS = std::remove_const_t<std::remove_pointer_t<decltype(src_c)>>;
-    segment_transpose_kernel<TS, TI><<<dim3((ncols + 63) / 64, ny, 1), 256, 0, st>>>(
-        src_c, ld_src, (int)col0, ncols, cnt, off, nullptr, 1, kro, krl, (TI*)out);
-    LMOE_HIP(hipGetLastError());
-    return LMOE_OK;
+    return segment_transpose<TS, TI>(dim3((ncols + 63) / 64, ny, 1), src_c, ld_src, (int)col0, ncols, cnt, off,
+                                     nullptr, 1, kro, krl, (TI*)out, st);
   };
   LMOE_TRY(tr((const T*)dy, d, 0, d, w.dyT));
   LMOE_TRY(tr((const TI*)w.rn, l, 0, l, w.rnT));
