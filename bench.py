@@ -224,33 +224,17 @@ def copy_calibration(nbytes: int = 1 << 30, reps: int = 5):
     print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "reps": reps}))
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="k3full_n8192", choices=sorted(S.CONFIGS))
-    ap.add_argument("--cpu-sample", type=int, default=24, help="tokens for the CPU oracle baseline (0: skip)")
-    ap.add_argument("--no-backward", action="store_true", help="skip the backward legs (routed block and whole layer)")
-    ap.add_argument("--calibrate-copy", action="store_true",
-                    help="only run a 1 GiB device copy (FETCH_SIZE / WRITE_SIZE calibration)")
-    args = ap.parse_args()
-    if args.calibrate_copy:
-        copy_calibration()
-        return
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the layer would shard tokens or experts; see the design notes).", file=sys.stderr)
-        sys.exit(2)
-
+def measure_forward(cfg, steps: int, warmup: int) -> dict:
+    """Timed forwards on seeded inputs generated in HBM: region 1 (the entry
+    point as a user calls it) gives the step time, region 2 (per-step events,
+    steps in order on one stream) the per-step times and the roofline of the
+    slowest step."""
     import numpy as np
     import torch
 
     import mixture_experts_ffn_sigmoid_amd as M
     from tests.gpu_util import alloc_forward, device_layer_inputs
 
-    cfg = S.CONFIGS[args.workload]
-    M.load()
     dev = device_layer_inputs(cfg)  # generated in HBM by the seeded generator
     bufs = alloc_forward(cfg)
     W = M.weights_struct(dev)
@@ -260,7 +244,7 @@ def main():
         M.latentmoe_forward(bufs["dims"], W, dev["x"], bufs["y"], bufs["ids"], bufs["probs"],
                             bufs["counts"], want_capacity=False, workspace=bufs["ws"])
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         fwd_plain()
     torch.cuda.synchronize()
 
@@ -270,22 +254,22 @@ def main():
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     start.record()
-    for _ in range(args.steps):
+    for _ in range(steps):
         fwd_plain()
     end.record()
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
-    ms_step = start.elapsed_time(end) / args.steps
+    ms_step = start.elapsed_time(end) / steps
 
     # Timed region 2: K forwards with per-step events (steps run in order on
     # one stream) -> per-kernel device times and the roofline of the slowest.
     ev_sets = [[torch.cuda.Event(enable_timing=True) for _ in range(M.TIMING_EVENTS)]
-               for _ in range(args.steps)]
+               for _ in range(steps)]
     for evs in ev_sets:  # torch creates the underlying hipEvent on first record
         for e in evs:
             e.record()
     torch.cuda.synchronize()
-    for s in range(args.steps):
+    for s in range(steps):
         M.latentmoe_forward_timed(bufs["dims"], W, dev["x"], bufs["y"], bufs["ids"], bufs["probs"],
                                   bufs["counts"], ev_sets[s], workspace=bufs["ws"])
     torch.cuda.synchronize()
@@ -316,7 +300,62 @@ def main():
     roof["algorithmic_flops"] = fl
     roof["ms"] = round(step_ms[dominant], 4)
     roof["traffic"] = measured_traffic(dominant, cfg.name)
+    layer_bytes = float(sum(b for _, b in models.values()))
+    del dev
+    return dict(ms_step=ms_step, step_ms=step_ms, steps_out=steps_out, roof=roof, C=C, t_wall=t_wall,
+                bufs=bufs, layer_bytes=layer_bytes)
 
+
+def secondary_decode(steps: int, warmup: int) -> dict:
+    """The few-token weight-streaming layer (full-K3 shapes, 64 tokens): step
+    time, tokens/s and the whole layer's algorithmic HBM bytes per step as a
+    fraction of the HBM peak, next to the routed gate/up roofline."""
+    import torch
+
+    cfg = S.CONFIGS["k3full_n64"]
+    fm = measure_forward(cfg, steps, warmup)
+    ms = fm["ms_step"]
+    out = {"workload": cfg.name, "ms_per_step": round(ms, 4),
+           "tokens_per_s": round(cfg.n_tokens / (ms / 1e3), 1),
+           "layer_algorithmic_bytes": fm["layer_bytes"],
+           "layer_hbm_frac": round(fm["layer_bytes"] / (ms / 1e3) / (PEAK_HBM_GBS * 1e9), 4),
+           "roofline": fm["roof"]}
+    del fm
+    torch.cuda.empty_cache()
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="k3full_n8192", choices=sorted(S.CONFIGS))
+    ap.add_argument("--cpu-sample", type=int, default=24, help="tokens for the CPU oracle baseline (0: skip)")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward legs (routed block and whole layer)")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the few-token (64-token, full-K3) forward measured after the prefill workload")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a 1 GiB device copy (FETCH_SIZE / WRITE_SIZE calibration)")
+    args = ap.parse_args()
+    if args.calibrate_copy:
+        copy_calibration()
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the layer would shard tokens or experts; see the design notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mixture_experts_ffn_sigmoid_amd as M
+
+    cfg = S.CONFIGS[args.workload]
+    M.load()
+    fm = measure_forward(cfg, args.steps, args.warmup)
+    ms_step, step_ms, steps_out, roof, C, t_wall, bufs = (fm["ms_step"], fm["step_ms"], fm["steps_out"], fm["roof"],
+                                                          fm["C"], fm["t_wall"], fm["bufs"])
+    peak_tf = PEAK_MFMA_TFLOPS[cfg.dtype]
     flops = cfg.flops()
     tok_s = cfg.n_tokens / (ms_step / 1e3)
     out = {
@@ -349,6 +388,10 @@ def main():
         out["layer_backward"] = layer_backward_leg(cfg, bufs["ids"], bufs["probs"], max(2, args.steps // 4), 1)
     if args.cpu_sample > 0:
         out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_sample)
+    if cfg.name == "k3full_n8192" and not args.no_secondary:
+        del bufs, fm
+        torch.cuda.empty_cache()
+        out["secondary"] = secondary_decode(args.steps, args.warmup)
     print(json.dumps(out), flush=True)
 
 
