@@ -38,6 +38,9 @@
 //   E_STORE   plain store (fp32 or storage dtype), masked to valid rows/cols
 //   E_SITU    SiTU-GLU hidden of the (gate, up) accumulator pair, stored as OutT
 //   E_SLOTS   p-weighted result of sorted pair q written to its own slot row q
+// Runtime option (A_DENSE with E_STORE): split K (ksplit > 1): the grid also
+// runs over K slices of kslice steps, each storing an fp32 partial product
+// (summed afterwards by splitk_reduce_kernel).
 #pragma once
 
 #include "lmoe_common.h"
