@@ -70,6 +70,8 @@ def _forward_parity(cfg, host=None, sample=None):
     # p for the GPU's ids, from the oracle's s
     sel = np.take_along_axis(routes.s, ids.astype(np.int64), axis=1)
     np.testing.assert_allclose(probs, sel / sel.sum(1, keepdims=True), rtol=0, atol=2e-5)
+    if callable(sample):
+        sample = sample(ids)
     rows = np.arange(cfg.n_tokens) if sample is None else np.asarray(sample)
     ref = O.forward(x[rows], W, ids=ids[rows])["y"]
     err = G.rel_err(y[rows], ref)
@@ -247,6 +249,27 @@ def test_forward_parity_k3_prefill():
     cfg = S.CONFIGS["k3full_n8192"]
     r = _forward_parity(cfg, host=None, sample=[0, 4097, 8191])
     assert r["C"] >= 131072 // 896
+
+
+@pytest.mark.slow
+def test_forward_parity_k3_past_2g_elements():
+    """The largest-size case: the full-K3 layer at N = 70000 tokens, where the
+    sorted pair rows of the routed hidden h (N k f_r = 2.29e9 elements) and the
+    slot rows (N k l = 4.01e9) run past 2^31.  The sampled tokens are the last
+    one (its slot rows are the last) and tokens routed to the two last experts
+    (their pairs sit at the end of the sorted order), so the expert GEMMs'
+    row offsets, their epilogues and the combine are checked past that point."""
+    cfg = S.CONFIGS["k3full_n8192"].with_(name="k3full_n70000", n_tokens=70000)
+    N, k, R = cfg.n_tokens, cfg.top_k, cfg.n_routed
+    assert N * k * cfg.ff_routed > 2**31 and N * k * cfg.d_latent > 2**31
+
+    def late_pairs(ids):
+        late = np.flatnonzero((ids >= R - 2).any(axis=1))
+        assert late.size >= 2
+        return [0, int(late[0]), int(late[-1]), N - 1]
+
+    r = _forward_parity(cfg, host=None, sample=late_pairs)
+    assert r["C"] >= N * k // R
 
 
 def _softmax_margin(logits: np.ndarray, k: int) -> np.ndarray:
