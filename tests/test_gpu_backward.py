@@ -153,7 +153,7 @@ def test_routed_backward_empty_batch_zeroes_weight_grads():
 
 
 def _full_size(name, tok_sample, n_experts_sample):
-    cfg = S.CONFIGS[name]
+    cfg = S.CONFIGS[name] if isinstance(name, str) else name
     _say(f"[routed_backward full] {cfg.name}")
     W = O.config_weights(cfg, cache_experts=2)
     ids, probs = _routes(cfg, W)
@@ -162,7 +162,7 @@ def _full_size(name, tok_sample, n_experts_sample):
     del dev
     tol = G.TOL[cfg.dtype]
     # dz / dprobs of sampled tokens: their own pairs only
-    rows = np.asarray(tok_sample)
+    rows = np.asarray(tok_sample(ids) if callable(tok_sample) else tok_sample)
     z, du = _z_du(cfg, rows)
     ref = O.routed_backward(z, ids[rows], probs[rows].astype(np.float64), W.experts, cfg.n_routed,
                             cfg.beta1, cfg.beta2, du, want=[])
@@ -194,6 +194,25 @@ def test_routed_backward_k3_decode_sample():
 @pytest.mark.slow
 def test_routed_backward_k3_prefill_sample():
     _full_size("k3full_n8192", [0, 4097, 8191], 2)
+
+
+@pytest.mark.slow
+def test_routed_backward_k3_past_2g_elements():
+    """The largest size: the full-K3 routed block at N = 70000 tokens, where the
+    per-pair buffers (h and the gate / up pre-activations, N k f_r = 2.29e9
+    elements; the expert outputs, N k l = 4.01e9) pass 2^31.  Sampled: the last
+    token and tokens routed to the two last experts (their pairs sit at the
+    end of the sorted order), and the weight gradients of the first, a middle
+    and the last expert over all their pairs."""
+    cfg = S.CONFIGS["k3full_n8192"].with_(name="k3full_n70000", n_tokens=70000)
+    N, R = cfg.n_tokens, cfg.n_routed
+
+    def late_pairs(ids):
+        late = np.flatnonzero((ids >= R - 2).any(axis=1))
+        return [int(late[0]), int(late[-1]), N - 1]
+
+    _full_size(cfg, late_pairs, 3)
+    torch.cuda.empty_cache()
 
 
 # ------------------------------------------------------------ whole layer
