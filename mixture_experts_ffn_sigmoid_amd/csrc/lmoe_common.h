@@ -63,18 +63,22 @@ __device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 in) {
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
 
+// 1/x from the hardware reciprocal v_rcp_f32 (about 1 ulp; 1/inf = 0).  A
+// correctly rounded reciprocal compiles to a ten-instruction division sequence.
+__device__ __forceinline__ float rcp_fast(float x) { return __builtin_amdgcn_rcpf(x); }
+
 // tanh from one hardware exp and one reciprocal: tanh|x| = (1 - e) / (1 + e),
 // e = exp(-2|x|) in (0, 1], so nothing overflows; absolute error ~1e-7.
 __device__ __forceinline__ float tanh_fast(float x) {
   const float e = __expf(-2.0f * fabsf(x));
-  return copysignf((1.0f - e) * __frcp_rn(1.0f + e), x);
+  return copysignf((1.0f - e) * rcp_fast(1.0f + e), x);
 }
 
 // SiTU-GLU hidden: beta1*tanh(g/beta1)*sigmoid(g) * beta2*tanh(u/beta2), fp32.
 // inv_b1 = 1/beta1, inv_b2 = 1/beta2.
 __device__ __forceinline__ float situ_hidden(float g, float u, float beta1, float beta2,
                                              float inv_b1, float inv_b2) {
-  const float sig = __frcp_rn(1.0f + __expf(-g));  // exp(-g) = inf gives 0
+  const float sig = rcp_fast(1.0f + __expf(-g));  // exp(-g) = inf gives 0
   const float gate = beta1 * tanh_fast(g * inv_b1) * sig;
   const float up = beta2 * tanh_fast(u * inv_b2);
   return gate * up;
