@@ -238,22 +238,30 @@ __global__ __launch_bounds__(256) void pair_grad_kernel(const float* __restrict_
 //   G'(a) = (1 - tanh(a/b1)^2) sigmoid(a) + b1 tanh(a/b1) sigmoid(a) (1 - sigmoid(a)),
 //   U'(a) = 1 - tanh(a/b2)^2.
 // Row q of dgu (leading dimension ld, starting at column col0) holds
-// [dg | du] (f columns each); n = rows * f elements.
+// [dg | du] (f columns each) for row q of the rows x f pre-activations.
+// Workgroups stride over rows and threads over columns (no index division);
+// tanh and sigma from the hardware exp and reciprocal (absolute error ~1e-7).
 template <typename TD>
 __global__ __launch_bounds__(256) void situ_backward_kernel(const float* __restrict__ dh, const float* __restrict__ g,
-                                                            const float* __restrict__ u, int64_t n, int f,
+                                                            const float* __restrict__ u, int64_t rows, int f,
                                                             float beta1, float beta2, TD* __restrict__ dgu,
                                                             int64_t ld, int64_t col0) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
-    const float a = g[i], b = u[i], d = dh[i];
-    const float tg = tanhf(a / beta1), tu = tanhf(b / beta2);
-    const float sg = 1.0f / (1.0f + expf(-a));
-    const float gate = beta1 * tg * sg, up = beta2 * tu;
-    const float dgate = (1.0f - tg * tg) * sg + beta1 * tg * sg * (1.0f - sg);
-    const float dup = 1.0f - tu * tu;
-    const int64_t q = i / f, j = i - q * f;
-    Elem<TD>::store(dgu + q * ld + col0 + j, d * dgate * up);
-    Elem<TD>::store(dgu + q * ld + col0 + f + j, d * gate * dup);
+  const float ib1 = 1.0f / beta1, ib2 = 1.0f / beta2;
+  for (int64_t q = blockIdx.x; q < rows; q += gridDim.x) {
+    const float* gq = g + q * f;
+    const float* uq = u + q * f;
+    const float* dq = dh + q * f;
+    TD* out = dgu + q * ld + col0;
+    for (int j = threadIdx.x; j < f; j += 256) {
+      const float a = gq[j], b = uq[j], d = dq[j];
+      const float tg = tanh_fast(a * ib1), tu = tanh_fast(b * ib2);
+      const float sg = rcp_fast(1.0f + __expf(-a));
+      const float gate = beta1 * tg * sg, up = beta2 * tu;
+      const float dgate = (1.0f - tg * tg) * sg + beta1 * tg * sg * (1.0f - sg);
+      const float dup = 1.0f - tu * tu;
+      Elem<TD>::store(out + j, d * dgate * up);
+      Elem<TD>::store(out + f + j, d * gate * dup);
+    }
   }
 }
 

@@ -682,8 +682,8 @@ lmoe_status routed_gradients(const Plan& p, const lmoe_dims* dm, const void* z, 
     LMOE_TRY((gemm<TI, T, float, A_SORTED, B_SINGLE, E_STORE>(
         grouped(w.dout, l * ei, w.w_oT, l * es, (int64_t)f * l * es, f, l, w.dh, (int64_t)f * 4), tile, st)));
   }
-  situ_backward_kernel<TI><<<blocks(P * f), 256, 0, st>>>(w.dh, w.g, w.up, P * f, f, dm->beta1, dm->beta2,
-                                                          (TI*)w.dgu, 2 * (int64_t)f, 0);
+  situ_backward_kernel<TI><<<(unsigned)std::min<int64_t>(P, 65536), 256, 0, st>>>(
+      w.dh, w.g, w.up, P, f, dm->beta1, dm->beta2, (TI*)w.dgu, 2 * (int64_t)f, 0);
   LMOE_HIP(hipGetLastError());
   // 5. dz rows = [dg | du] [W_g ; W_u] (K = 2f: W_g's rows, then W_u's), summed per token
   float* dzrows = w.o;  // o is consumed
@@ -844,8 +844,8 @@ lmoe_status run_layer_backward(const Plan& p, const lmoe_dims* dm, const lmoe_we
     LMOE_TRY((gemm<T, T, float, A_DENSE, B_SINGLE, E_STORE>(dense(dy, d * es, (int)N, w.shoT, d * es, nsf, d,
                                                                   w.dhs, (int64_t)nsf * 4),
                                                             dense_tile(N, nsf, false), st)));
-    situ_backward_kernel<TI><<<blocks(N * nsf), 256, 0, st>>>(w.dhs, w.ag, w.au, N * nsf, nsf, dm->beta1,
-                                                              dm->beta2, (TI*)w.dcat, kcat, l + rpad);
+    situ_backward_kernel<TI><<<(unsigned)std::min<int64_t>(N, 65536), 256, 0, st>>>(
+        w.dhs, w.ag, w.au, N, nsf, dm->beta1, dm->beta2, (TI*)w.dcat, kcat, l + rpad);
     LMOE_HIP(hipGetLastError());
   }
   // ---- step 3 backward (routed block) -> dz into dcat[:, :l], dprobs
