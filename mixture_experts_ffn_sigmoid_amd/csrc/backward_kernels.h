@@ -273,19 +273,32 @@ __global__ __launch_bounds__(256) void inverse_order_kernel(const int32_t* __res
 }
 
 // dz[n] (row stride ld) = sum over slots j (in slot order) of wts[n k + j] *
-// rows[inv[n k + j]] (wts NULL = ones), one workgroup per token.
+// rows[inv[n k + j]] (wts NULL = ones), one workgroup per token; top_k <= 64,
+// ell a multiple of 4 (16-byte row loads).
 template <typename TD>
 __global__ __launch_bounds__(256) void pair_sum_kernel(const float* __restrict__ rows, const int32_t* __restrict__ inv,
                                                        int top_k, int ell, const float* __restrict__ wts,
                                                        TD* __restrict__ dz, int64_t ld) {
   const int64_t n = blockIdx.x;
-  for (int c = threadIdx.x; c < ell; c += 256) {
-    float acc = 0.f;
+  __shared__ int64_t src[64];  // first element of each slot's row
+  __shared__ float wq[64];
+  if ((int)threadIdx.x < top_k) {
+    src[threadIdx.x] = (int64_t)inv[n * top_k + threadIdx.x] * ell;
+    wq[threadIdx.x] = wts ? wts[n * top_k + threadIdx.x] : 1.0f;
+  }
+  __syncthreads();
+  TD* out = dz + n * ld;
+  for (int c = 4 * (int)threadIdx.x; c < ell; c += 4 * 256) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
     for (int j = 0; j < top_k; ++j) {
-      const float v = rows[(int64_t)inv[n * top_k + j] * ell + c];
-      acc += wts ? wts[n * top_k + j] * v : v;
+      const f32x4 v = *(const f32x4*)(rows + src[j] + c);
+      const float w = wq[j];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] += w * v[q];
     }
-    Elem<TD>::store(dz + n * ld + c, acc);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) Elem<TD>::store(out + c + q, acc[q]);
   }
 }
 
