@@ -219,10 +219,21 @@ __global__ __launch_bounds__(256) void pair_grad_kernel(const float* __restrict_
   TD* drow = dout + qs * ell;
   const float pq = probs[q];
   float acc = 0.f;
-  for (int c = threadIdx.x; c < ell; c += 256) {
-    const float v = dur[c];
-    acc += v * orow[c];
-    Elem<TD>::store(drow + c, pq * v);
+  if (((((uintptr_t)du) | ((uintptr_t)o)) & 15) == 0 && (ell & 3) == 0) {  // 16-byte rows (uniform)
+    for (int c = 4 * (int)threadIdx.x; c < ell; c += 4 * 256) {
+      const f32x4 v = *(const f32x4*)(dur + c), w = *(const f32x4*)(orow + c);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc += v[i] * w[i];
+        Elem<TD>::store(drow + c + i, pq * v[i]);
+      }
+    }
+  } else {
+    for (int c = threadIdx.x; c < ell; c += 256) {
+      const float v = dur[c];
+      acc += v * orow[c];
+      Elem<TD>::store(drow + c, pq * v);
+    }
   }
   __shared__ float red[4];
 #pragma unroll
@@ -273,8 +284,8 @@ __global__ __launch_bounds__(256) void inverse_order_kernel(const int32_t* __res
 }
 
 // dz[n] (row stride ld) = sum over slots j (in slot order) of wts[n k + j] *
-// rows[inv[n k + j]] (wts NULL = ones), one workgroup per token; top_k <= 64,
-// ell a multiple of 4 (16-byte row loads).
+// rows[inv[n k + j]] (wts NULL = ones), one workgroup per token; top_k <= 64.
+// 16-byte row loads where rows and ell allow them.
 template <typename TD>
 __global__ __launch_bounds__(256) void pair_sum_kernel(const float* __restrict__ rows, const int32_t* __restrict__ inv,
                                                        int top_k, int ell, const float* __restrict__ wts,
@@ -288,17 +299,25 @@ __global__ __launch_bounds__(256) void pair_sum_kernel(const float* __restrict__
   }
   __syncthreads();
   TD* out = dz + n * ld;
-  for (int c = 4 * (int)threadIdx.x; c < ell; c += 4 * 256) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if ((((uintptr_t)rows) & 15) == 0 && (ell & 3) == 0) {  // uniform
+    for (int c = 4 * (int)threadIdx.x; c < ell; c += 4 * 256) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
-    for (int j = 0; j < top_k; ++j) {
-      const f32x4 v = *(const f32x4*)(rows + src[j] + c);
-      const float w = wq[j];
+      for (int j = 0; j < top_k; ++j) {
+        const f32x4 v = *(const f32x4*)(rows + src[j] + c);
+        const float w = wq[j];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acc[q] += w * v[q];
+        for (int q = 0; q < 4; ++q) acc[q] += w * v[q];
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) Elem<TD>::store(out + c + q, acc[q]);
     }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) Elem<TD>::store(out + c + q, acc[q]);
+  } else {
+    for (int c = threadIdx.x; c < ell; c += 256) {
+      float acc = 0.f;
+      for (int j = 0; j < top_k; ++j) acc += wq[j] * rows[src[j] + c];
+      Elem<TD>::store(out + c, acc);
+    }
   }
 }
 
