@@ -736,14 +736,14 @@ lmoe_status routed_gradients(const Plan& p, const lmoe_dims* dm, const void* z, 
     return g;
   };
   // Every expert's K is its padded pair count (at most C rounded up to 64).
-  // Up to kWgradKMax, with 16-bit operands and 128-multiple widths, one
-  // workgroup per 128-row strip keeps its A fragments in registers and sweeps
+  // Up to kWgradKMax, with 16-bit operands and 256-multiple widths, one
+  // workgroup per 256-row strip keeps its A fragments in registers and sweeps
   // the columns; otherwise batched GEMM tiles (128 x 128, 64-byte K steps in
   // a 3-stage ring: 48 KB of LDS, three tiles per compute unit).
   if constexpr (sizeof(TI) == 2 && sizeof(T) == 2) {
-    if ((C + 63) / 64 * 64 <= kWgradKMax && l % kWgradTile == 0 && f % kWgradTile == 0) {
+    if ((C + 63) / 64 * 64 <= kWgradKMax && l % kWgradStrip == 0 && f % kWgradStrip == 0) {
       auto strips = [&](const void* a, int M, const void* b, int N, void* out) -> lmoe_status {
-        wgrad_kernel<TI, T><<<(unsigned)((int64_t)R * (M / kWgradTile)), 256, 0, st>>>(
+        wgrad_kernel<TI, T><<<(unsigned)((int64_t)R * (M / kWgradStrip)), kWgradThreads, 0, st>>>(
             (const TI*)a, (const TI*)b, w.kr_off, w.kr_len, M, N, (T*)out);
         LMOE_HIP(hipGetLastError());
         return LMOE_OK;

@@ -4,26 +4,31 @@
 //
 // A_e the row-major [M, K_e] block at element kr_off[e] * M of `a`, B_e the
 // [N, K_e] block at kr_off[e] * N of `b`, K_e = kr_len[e] in {0, 64, 128, 192}
-// (an expert's pairs, zero-padded to a multiple of 64).  M and N are
-// multiples of 128; 16-bit operands, fp32 accumulation.
+// (an expert's pairs, zero-padded to a multiple of 64).  M is a multiple of
+// 256 and N of 128; 16-bit operands, fp32 accumulation.
 //
 // A general GEMM tile spends most of its life waiting for its few K steps'
-// operands.  Here one workgroup (4 waves, 2 x 2) owns an expert's 128-row
+// operands.  Here one workgroup (8 waves, 4 x 2) owns an expert's 256-row
 // strip of M: the strip passes through LDS into registers once (the A
 // fragments of every K step, at most 96 VGPRs per lane), then the workgroup
-// sweeps all N / 128 column tiles.  The next column tile's B operand streams
-// into LDS (LDS-DMA) while the current output tile is staged in LDS and
-// written back as 16-byte row chunks; with 80 KB of LDS two workgroups share
-// a compute unit, so one multiplies while the other stages and stores.
+// sweeps all N / 128 column tiles.  Two LDS buffers alternate for the B tiles:
+// tile t+1 streams in (LDS-DMA) while tile t is multiplied, staged in a third
+// buffer and written back as 16-byte row chunks.  The loads of a CU queue with
+// its stores; a 256-row strip reads each B tile once per 64 KB of output.
 #pragma once
 
 #include "lmoe_common.h"
 
 namespace lmoe {
 
-constexpr int kWgradKMax = 192;  // largest K_e this kernel takes
-constexpr int kWgradTile = 128;  // rows / columns of a tile
-constexpr int kWgradBuf = kWgradTile * kWgradKMax * 2;  // bytes of one operand tile (48 KB)
+constexpr int kWgradKMax = 192;    // largest K_e this kernel takes
+constexpr int kWgradTile = 128;    // columns of an output tile, rows of a B tile
+constexpr int kWgradStrip = 256;   // rows of an A strip and of an output tile
+constexpr int kWgradBuf = kWgradTile * kWgradKMax * 2;     // one B tile (48 KB)
+constexpr int kWgradStage = kWgradStrip * kWgradTile * 2;  // one staged output tile (64 KB)
+constexpr int kWgradLds = 2 * kWgradBuf + kWgradStage;    // 160 KB: one workgroup per CU
+constexpr int kWgradWaves = 8;
+constexpr int kWgradThreads = 64 * kWgradWaves;
 
 typedef __attribute__((address_space(3))) void wg_lds_void_t;
 
@@ -58,55 +63,61 @@ __device__ __forceinline__ void wg_dma(const char* blk, int K, char* buf, int wa
   }
 }
 
-// Staged output tile: 128 rows of 256 bytes, 16-byte chunk c of row r at
+// Staged output tile: 256 rows of 256 bytes, 16-byte chunk c of row r at
 // chunk c ^ (r % 16).
 __device__ __forceinline__ int wg_spos(int row, int chunk) { return row * 256 + ((chunk ^ (row & 15)) << 4); }
 
 template <typename TO, int KG>
 __device__ __forceinline__ void wgrad_strip(const char* a_blk, const char* b_blk, int K, int N, char* out,
                                             int64_t ldo, char* smem) {
-  constexpr int NWAVE = 4, NTHR = 64 * NWAVE;
-  constexpr int KS = 2 * KG;  // MFMA K steps of 16
+  constexpr int NWAVE = kWgradWaves, NTHR = kWgradThreads;
+  constexpr int KS = 2 * KG;              // MFMA K steps of 16
+  constexpr int kDma = KG * (8 / NWAVE);  // DMA instructions per wave per 128-row block
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // waves 2 (rows) x 2 (columns): 64 x 64 of the tile each
+  // waves 4 (rows) x 2 (columns): 64 x 64 of the tile each
   const int wm = wave >> 1, wn = wave & 1, lr = lane & 31, lh = lane >> 5;
   const int NT = N / kWgradTile;
-  char* const B = smem;               // operand tile (the A strip first, then B tiles)
-  char* const S = smem + kWgradBuf;   // staged output tile
-  auto b_tile = [&](int t) { return b_blk + (int64_t)min(t, NT - 1) * kWgradTile * K * 2; };
+  auto bbuf = [&](int t) { return smem + (t & 1) * kWgradBuf; };  // column tile t's B buffer
+  char* const S = smem + 2 * kWgradBuf;                           // staged output tile
+  auto b_tile = [&](int t) { return b_blk + (int64_t)t * kWgradTile * K * 2; };
   const uint32_t lane_off = (uint32_t)((lane >> 2) * K * 2 + (((lane & 3) ^ ((lane >> 4) & 3)) << 4));
-  auto sync_lds = [&]() {  // this wave's LDS accesses are done, then the workgroup barrier
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(wg_lgkm0());
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-  };
 
-  // the A strip through LDS into registers
-  wg_dma<KG, NWAVE>(a_blk, K, B, wave, lane_off);
-  __builtin_amdgcn_s_waitcnt(wg_vmcnt(0));
+  // the A strip's two 128-row blocks into B buffer 1 and the staging buffer
+  // (contiguous), B tile 0 into B buffer 0; then the strip into registers
+  wg_dma<KG, NWAVE>(a_blk, K, bbuf(1), wave, lane_off);
+  wg_dma<KG, NWAVE>(a_blk + (int64_t)kWgradTile * K * 2, K, bbuf(1) + kWgradBuf, wave, lane_off);
+  wg_dma<KG, NWAVE>(b_tile(0), K, bbuf(0), wave, lane_off);
+  __builtin_amdgcn_s_waitcnt(wg_vmcnt(kDma));  // issued after the strip: B tile 0 only
+  asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
   u32x4 fa[KS][2];
+  {
+    const char* Ab = bbuf(1) + (wm >> 1) * kWgradBuf;  // this wave's 64 rows lie in one block
 #pragma unroll
-  for (int s = 0; s < KS; ++s)
+    for (int s = 0; s < KS; ++s)
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      fa[s][i] = *(const u32x4*)(B + wg_pos(s >> 1, wm * 64 + i * 32 + lr, 2 * (s & 1) + lh));
-  sync_lds();
-  wg_dma<KG, NWAVE>(b_tile(0), K, B, wave, lane_off);
+      for (int i = 0; i < 2; ++i)
+        fa[s][i] = *(const u32x4*)(Ab + wg_pos(s >> 1, (wm & 1) * 64 + i * 32 + lr, 2 * (s & 1) + lh));
+  }
 
   // per-lane parts of the staging address: row wm*64 + 4*lh (+ constants),
   // chunk (wn*8 + lr/8) ^ 4*lh (^ constants), byte (lr % 8) * 2
   const int st_base = (wm * 64 + 4 * lh) * 256 + (lr & 7) * 2;
   const int st_chunk = (wn * 8 + (lr >> 3)) ^ (4 * lh);
-  constexpr int kStores = kWgradTile * 256 / 16 / NTHR;  // 16-byte stores per thread per tile
+  constexpr int kStores = kWgradStrip * 256 / 16 / NTHR;  // 16-byte stores per thread per tile
   for (int t = 0; t < NT; ++t) {
-    // B tile t has landed: issued after it are the stores of tile t-1 (none before tile 0)
-    if (t == 0) __builtin_amdgcn_s_waitcnt(wg_vmcnt(0));
-    else __builtin_amdgcn_s_waitcnt(wg_vmcnt(kStores));
+    const char* const B = bbuf(t);
+    // B tile t has landed (issued after it: the stores of tile t-1, none
+    // before tile 0), and every wave is done reading the A strip or the
+    // staged tile t-1 and B tile t-1: B tile t+1 may stream into the other
+    // buffer and tile t may be staged
+    if (t == 0) __builtin_amdgcn_s_waitcnt(wg_vmcnt(0) & wg_lgkm0());
+    else __builtin_amdgcn_s_waitcnt(wg_vmcnt(kStores) & wg_lgkm0());
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+    if (t + 1 < NT) wg_dma<KG, NWAVE>(b_tile(t + 1), K, bbuf(t + 1), wave, lane_off);
     f32x16 acc[2][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -126,10 +137,6 @@ __device__ __forceinline__ void wgrad_strip(const char* a_blk, const char* b_blk
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, fa[s][i]),
                                                              __builtin_bit_cast(f16x8, fb[j]), acc[i][j], 0, 0, 0);
     }
-    // every wave is done with B tile t and with the staged tile t-1: B tile
-    // t+1 streams in while tile t is staged and stored
-    sync_lds();
-    if (t + 1 < NT) wg_dma<KG, NWAVE>(b_tile(t + 1), K, B, wave, lane_off);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -141,7 +148,10 @@ __device__ __forceinline__ void wgrad_strip(const char* a_blk, const char* b_blk
           const int cx = 8 * ((v >> 2) & 1) + (v & 3);
           Elem<TO>::store((TO*)(S + st_base + rc * 256 + ((st_chunk ^ (4 * j) ^ cx) << 4)), acc[i][j][v]);
         }
-    sync_lds();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(wg_lgkm0());
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
     char* otile = out + (int64_t)t * kWgradTile * 2;
 #pragma unroll
     for (int q = 0; q < kStores; ++q) {
@@ -154,20 +164,20 @@ __device__ __forceinline__ void wgrad_strip(const char* a_blk, const char* b_blk
 }
 
 template <typename TI, typename TO>
-__global__ __launch_bounds__(256, 2) void wgrad_kernel(const TI* __restrict__ a, const TI* __restrict__ b,
+__global__ __launch_bounds__(kWgradThreads) void wgrad_kernel(const TI* __restrict__ a, const TI* __restrict__ b,
                                                     const int32_t* __restrict__ kr_off,
                                                     const int32_t* __restrict__ kr_len, int M, int N,
                                                     TO* __restrict__ out) {
   static_assert(sizeof(TI) == 2 && sizeof(TO) == 2, "16-bit operands and output");
-  __shared__ __attribute__((aligned(1024))) char smem[kWgradBuf + kWgradTile * 256];  // 80 KB: two per CU
-  const int strips = M / kWgradTile;
+  __shared__ __attribute__((aligned(1024))) char smem[kWgradLds];
+  const int strips = M / kWgradStrip;
   // the strips of one expert are neighbours on one XCD: they share B_e in its L2
   const int L = xcd_contiguous_id(blockIdx.x, gridDim.x);
   const int e = L / strips, ms = L % strips;
   const int K = kr_len[e];
   const int64_t ldo = (int64_t)N * 2;
-  char* o = (char*)(out + ((int64_t)e * M + (int64_t)ms * kWgradTile) * N);
-  const char* ab = (const char*)(a + (int64_t)kr_off[e] * M + (int64_t)ms * kWgradTile * K);
+  char* o = (char*)(out + ((int64_t)e * M + (int64_t)ms * kWgradStrip) * N);
+  const char* ab = (const char*)(a + (int64_t)kr_off[e] * M + (int64_t)ms * kWgradStrip * K);
   const char* bb = (const char*)(b + (int64_t)kr_off[e] * N);
   switch (K) {
     case 64: wgrad_strip<TO, 2>(ab, bb, K, N, o, ldo, smem); break;
@@ -176,7 +186,7 @@ __global__ __launch_bounds__(256, 2) void wgrad_kernel(const TI* __restrict__ a,
     default: {  // no pairs: a zero gradient (K above the maximum never reaches here)
       const u32x4 z = {0u, 0u, 0u, 0u};
       const int chunks = N / 8;  // 16-byte chunks per row
-      for (int id = threadIdx.x; id < kWgradTile * chunks; id += 256)
+      for (int id = threadIdx.x; id < kWgradStrip * chunks; id += kWgradThreads)
         *(u32x4*)(o + (int64_t)(id / chunks) * ldo + (id % chunks) * 16) = z;
     }
   }

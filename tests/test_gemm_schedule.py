@@ -13,8 +13,8 @@ stages; a prologue issues virtual steps -SB..-1 (A tile s + SA when >= 0, B
 tile s + SB); step kt waits with vmcnt(kNewer) for tile kt + 1 and then issues
 A tile kt + SA and B tile kt + SB into the stages tile kt released (B before A
 when SB == SA, after it when SB > SA); tiles past the end reload tile KT - 1.
-wgrad_kernel (csrc/wgrad_kernel.h): A strip, then per column tile t: wait for
-B(t), multiply, issue B(t+1), 8 stores of tile t.
+wgrad_kernel (csrc/wgrad_kernel.h): the A strip and B(0), then per column tile
+t: wait for B(t), issue B(t+1) into the other buffer, multiply, stage, 8 stores.
 """
 import pytest
 
@@ -79,24 +79,38 @@ def test_a_wait_one_operation_too_shallow_is_caught(SA, SB):
         gemm_schedule(SA, SB, 16, 2, 4, wait_delta=1)
 
 
-def wgrad_schedule(KG, NT, wait_delta=0, stores=8, nwave=4):
-    """Replays wgrad_kernel's issue order (per wave: the A strip, B tile 0;
-    per column tile t: wait, multiply, B tile t+1, the 8 stores of tile t)."""
-    dma = KG * (8 // nwave)  # DMA instructions per operand tile per wave
-    issued, last = [], {}
+def wgrad_schedule(KG, NT, wait_delta=0, stores=8, nwave=8):
+    """Replays wgrad_kernel's issue order per wave: the A strip's two 128-row
+    blocks (into B buffer 1 and the staging buffer), B tile 0 (into B buffer
+    0), a wait for the strip; per column tile t: wait for B(t), B tile t+1 into
+    buffer (t+1) % 2, multiply from buffer t % 2, stage, the stores of tile t.
+    Also checks that no DMA still in flight targets a buffer being read or
+    staged into."""
+    dma = KG * (8 // nwave)  # DMA instructions per 128-row block per wave
+    issued, last = [], {}    # issued: (tag, target buffer or None)
 
-    def issue(tag, n):
-        issued.extend([tag] * n)
+    def issue(tag, n, buf=None):
+        issued.extend([(tag, buf)] * n)
         last[tag] = len(issued) - 1
 
-    issue(("A", 0), dma)
-    assert last[("A", 0)] < len(issued) - 0  # vmcnt(0) before the strip is read
-    issue(("B", 0), dma)
+    def in_flight(n):  # what may still be outstanding after vmcnt(n)
+        return issued[len(issued) - n:] if n > 0 else []
+
+    issue(("A", 0), dma, 1)
+    issue(("A", 1), dma, "S")
+    issue(("B", 0), dma, 0)
+    n = dma + wait_delta
+    assert last[("A", 1)] < len(issued) - n, (KG, NT)  # the strip is read
+    assert all(b not in (1, "S") for _, b in in_flight(n))
     for t in range(NT):
-        wait = (0 if t == 0 else stores) + wait_delta
-        assert last[("B", t)] < len(issued) - wait, (KG, NT, t)
+        n = (0 if t == 0 else stores) + wait_delta
+        assert last[("B", t)] < len(issued) - n, (KG, NT, t)
+        flying = in_flight(n)
         if t + 1 < NT:
-            issue(("B", t + 1), dma)
+            issue(("B", t + 1), dma, (t + 1) % 2)
+            flying = flying + issued[-dma:]
+        # the MFMAs read buffer t % 2 and the staging writes "S"
+        assert all(b not in (t % 2, "S") for _, b in flying), (KG, NT, t)
         issue(("S", t), stores)
 
 
