@@ -32,6 +32,11 @@
  *    latentmoe_workspace_bytes(dims, entry) bytes; the library allocates no
  *    device memory and keeps no state between calls.  Calls that share a
  *    workspace must be ordered on one stream.
+ *  - Matrices (x, y, z, the padded tensor, u, du, dz, dy, dx and every weight
+ *    and weight-gradient matrix) and the workspace must be 16-byte aligned, as
+ *    hipMalloc and torch allocations are: they are moved 16 bytes at a time.
+ *    A misaligned one is INVALID_ARGUMENT.  Vectors (ids, probs, counts, bias,
+ *    logits, ...) need only their element alignment.
  *  - Errors: a status code, never an abort.  Arguments are validated before
  *    anything is enqueued; on any error the outputs are unspecified.
  *    latentmoe_last_error() returns a thread-local description of the last

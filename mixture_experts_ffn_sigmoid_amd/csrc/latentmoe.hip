@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 #include <mutex>
 
 #include "latentmoe.h"
@@ -66,6 +67,17 @@ int routed_tile_m(int64_t pairs, int R) {
   const int64_t mean = pairs / R;
   return mean < 48 ? 64 : mean < 96 ? 128 : 192;
 }
+
+// Matrices and workspace buffers are moved 16 bytes at a time (LDS-DMA
+// operand tiles, 16-byte epilogue and weight-gradient stores), so every
+// matrix pointer and the workspace must be 16-byte aligned (hipMalloc and
+// torch allocations are).  NULL passes: it is checked on its own.
+bool misaligned(std::initializer_list<const void*> ptrs) {
+  for (const void* q : ptrs)
+    if (((uintptr_t)q) & 15) return true;
+  return false;
+}
+constexpr const char* kAlignMsg = "matrix pointers and the workspace must be 16-byte aligned";
 
 lmoe_status check_dims(const lmoe_dims* dm, Plan* p) {
   if (!dm) return fail(LMOE_ERR_INVALID_ARGUMENT, "dims is NULL");
@@ -1096,6 +1108,7 @@ lmoe_status latentmoe_route(const lmoe_dims* dims, const void* x, const void* w_
   LMOE_TRY(check_dims(dims, &p));
   if (p.N == 0) return LMOE_OK;
   if (!x || !w_router || !ids || !probs) return fail(LMOE_ERR_INVALID_ARGUMENT, "NULL tensor");
+  if (misaligned({x, w_router, workspace})) return fail(LMOE_ERR_INVALID_ARGUMENT, kAlignMsg);
   RouteWs w{};
   if (!logits) {
     const size_t need = carve_route(p, nullptr, &w);
@@ -1116,6 +1129,7 @@ lmoe_status latentmoe_route_softmax(const lmoe_dims* dims, const void* x, const 
   LMOE_TRY(check_dims(dims, &p));
   if (p.N == 0) return LMOE_OK;
   if (!x || !w_router || !ids || !probs) return fail(LMOE_ERR_INVALID_ARGUMENT, "NULL tensor");
+  if (misaligned({x, w_router, workspace})) return fail(LMOE_ERR_INVALID_ARGUMENT, kAlignMsg);
   RouteWs w{};
   if (!logits) {
     const size_t need = carve_route(p, nullptr, &w);
@@ -1169,6 +1183,7 @@ lmoe_status latentmoe_dispatch(const lmoe_dims* dims, const int32_t* ids, const 
     return fail(LMOE_ERR_INVALID_ARGUMENT, "NULL argument");
   if (padded && !z) return fail(LMOE_ERR_INVALID_ARGUMENT, "padded output needs z");
   if (capacity < 0) return fail(LMOE_ERR_INVALID_ARGUMENT, "capacity < 0");
+  if (misaligned({z, padded, workspace})) return fail(LMOE_ERR_INVALID_ARGUMENT, kAlignMsg);
   hipStream_t st = launch_stream(stream);
   *C_out = 0;
   if (p.N == 0) {
@@ -1215,6 +1230,7 @@ lmoe_status latentmoe_experts(const lmoe_dims* dims, const void* padded, int64_t
   if (!padded || !counts || !offsets || !order || !probs || !w_g || !w_u || !w_o || !u)
     return fail(LMOE_ERR_INVALID_ARGUMENT, "NULL tensor");
   if (C < 1 || C > p.N) return fail(LMOE_ERR_INVALID_ARGUMENT, "C must be in [1, N]");
+  if (misaligned({padded, w_g, w_u, w_o, u, workspace})) return fail(LMOE_ERR_INVALID_ARGUMENT, kAlignMsg);
   ExpertsWs w{};
   const size_t need = carve_experts(p, nullptr, &w);
   if (!workspace || workspace_bytes < need)
@@ -1254,6 +1270,9 @@ lmoe_status forward_impl(const lmoe_dims* dims, const lmoe_weights* weights, con
     return fail(LMOE_ERR_INVALID_ARGUMENT, "NULL weight");
   if (p.ns > 0 && (!W->sh_g || !W->sh_u || !W->sh_o))
     return fail(LMOE_ERR_INVALID_ARGUMENT, "NULL shared expert weight");
+  if (misaligned({x, y, W->w_down, W->w_router, W->w_g, W->w_u, W->w_o, W->sh_g, W->sh_u, W->sh_o, W->w_up,
+                  workspace}))
+    return fail(LMOE_ERR_INVALID_ARGUMENT, kAlignMsg);
   ForwardWs w{};
   const size_t need = carve_forward(p, nullptr, &w);
   if (!workspace || workspace_bytes < need)
@@ -1305,6 +1324,8 @@ lmoe_status latentmoe_routed_backward(const lmoe_dims* dims, const void* z, cons
   if (!w_g || !w_u || !w_o || !dw_g || !dw_u || !dw_o) return fail(LMOE_ERR_INVALID_ARGUMENT, "NULL weight");
   if (p.N > 0 && (!z || !ids || !probs || !du || !dz || !dprobs))
     return fail(LMOE_ERR_INVALID_ARGUMENT, "NULL tensor");
+  if (misaligned({z, w_g, w_u, w_o, du, dz, dw_g, dw_u, dw_o, workspace}))
+    return fail(LMOE_ERR_INVALID_ARGUMENT, kAlignMsg);
   RoutedBwdWs w{};
   const size_t need = carve_routed_backward(p, nullptr, &w);
   if (!workspace || workspace_bytes < need)
@@ -1342,6 +1363,9 @@ lmoe_status latentmoe_backward(const lmoe_dims* dims, const lmoe_weights* weight
   if (p.ns > 0 && (!W->sh_g || !W->sh_u || !W->sh_o || !G->sh_g || !G->sh_u || !G->sh_o))
     return fail(LMOE_ERR_INVALID_ARGUMENT, "NULL shared expert weight or gradient");
   if (p.N > 0 && (!x || !ids || !probs || !dy || !dx)) return fail(LMOE_ERR_INVALID_ARGUMENT, "NULL tensor");
+  if (misaligned({x, dy, dx, W->w_down, W->w_router, W->w_g, W->w_u, W->w_o, W->sh_g, W->sh_u, W->sh_o, W->w_up,
+                  G->w_down, G->w_router, G->w_g, G->w_u, G->w_o, G->sh_g, G->sh_u, G->sh_o, G->w_up, workspace}))
+    return fail(LMOE_ERR_INVALID_ARGUMENT, kAlignMsg);
   LayerBwdWs w{};
   const size_t need = carve_layer_backward(p, nullptr, &w);
   if (!workspace || workspace_bytes < need)

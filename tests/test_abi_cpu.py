@@ -134,3 +134,31 @@ def test_layer_backward_argument_errors():
     assert lib.latentmoe_backward(ctypes.byref(dims), ctypes.byref(W), fake, None, fake, fake, fake,
                                   ctypes.byref(G), fake, 1 << 40, None) == 1
     assert M.workspace_bytes(dims, M.ENTRY_BACKWARD) > M.workspace_bytes(dims, M.ENTRY_ROUTED_BACKWARD)
+
+
+def test_misaligned_matrices_are_rejected():
+    """Matrices and the workspace are moved 16 bytes at a time: a pointer off
+    a 16-byte boundary is INVALID_ARGUMENT, found before any HIP call."""
+    lib = M.load()
+    dims = M.dims_of(S.CONFIGS["toy_n128"])
+    fake, off = 4096, 4096 + 8
+    W = M.Weights(*([fake] * 11))
+    C = ctypes.c_int64(-1)
+    # x, then the workspace, of the forward
+    assert lib.latentmoe_forward(ctypes.byref(dims), ctypes.byref(W), off, fake, fake, fake, fake,
+                                 ctypes.byref(C), fake, 1 << 40, None) == 1
+    assert b"16-byte" in lib.latentmoe_last_error()
+    assert lib.latentmoe_forward(ctypes.byref(dims), ctypes.byref(W), fake, fake, fake, fake, fake,
+                                 ctypes.byref(C), off, 1 << 40, None) == 1
+    # a weight matrix (W_up)
+    Wb = M.Weights(*([fake] * 10 + [off]))
+    assert lib.latentmoe_forward(ctypes.byref(dims), ctypes.byref(Wb), fake, fake, fake, fake, fake,
+                                 ctypes.byref(C), fake, 1 << 40, None) == 1
+    # the upstream gradient of the routed backward
+    args = [fake] * 12
+    args[6] = fake + 4
+    assert lib.latentmoe_routed_backward(ctypes.byref(dims), *args, fake, 1 << 40, None) == 1
+    assert b"16-byte" in lib.latentmoe_last_error()
+    # the router's x
+    assert lib.latentmoe_route(ctypes.byref(dims), off, fake, None, fake, fake, None, fake, 1 << 40, None) == 1
+    assert b"16-byte" in lib.latentmoe_last_error()
