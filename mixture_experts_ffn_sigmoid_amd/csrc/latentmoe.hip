@@ -1187,8 +1187,10 @@ lmoe_status latentmoe_dispatch(const lmoe_dims* dims, const int32_t* ids, const 
   hipStream_t st = launch_stream(stream);
   *C_out = 0;
   if (p.N == 0) {
-    LMOE_HIP(hipMemsetAsync(counts, 0, (size_t)p.R * 4, st));
-    LMOE_HIP(hipMemsetAsync(offsets, 0, (size_t)p.R * 4, st));
+    for (int32_t* v : {counts, offsets}) {  // a fill kernel, no memset node if the caller captures
+      zero_words_kernel<<<(unsigned)((p.R + 255) / 256), 256, 0, st>>>((uint32_t*)v, p.R);
+      LMOE_HIP(hipGetLastError());
+    }
     LMOE_HIP(hipStreamSynchronize(st));
     return LMOE_OK;
   }

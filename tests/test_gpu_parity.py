@@ -140,6 +140,19 @@ def _ids_case(rng, N, R, k, skew=False):
     return ids.astype(np.int32)
 
 
+def test_dispatch_empty_batch():
+    """N = 0: C = 0, and counts and offsets come back all zero."""
+    R = 16
+    dims = M.make_dims(0, 64, 64, R, 2, 0, 64, 0, "bf16")
+    counts = torch.full((R,), 7, dtype=torch.int32, device="cuda")
+    offsets = torch.full((R,), 7, dtype=torch.int32, device="cuda")
+    none = torch.empty(0, dtype=torch.int32, device="cuda")
+    C = M.latentmoe_dispatch(dims, none, None, counts, offsets, none)
+    torch.cuda.synchronize()
+    assert C == 0
+    assert (counts == 0).all() and (offsets == 0).all()
+
+
 @pytest.mark.parametrize("case", [
     dict(N=128, R=16, k=2, l=128, dt="f32"),
     dict(N=4096, R=16, k=2, l=384, dt="bf16"),
