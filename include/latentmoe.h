@@ -174,7 +174,9 @@ lmoe_status latentmoe_experts(const lmoe_dims* dims, const void* padded, int64_t
  * Side outputs (the pages' route bookkeeping): ids [N, k] int32 and
  * probs [N, k] fp32 as from latentmoe_route, counts [R] int32 pairs per
  * expert.  If C_host is not NULL the call waits on `stream` and writes
- * C = max counts there; with C_host NULL the call is fully asynchronous.
+ * C = max counts there; with C_host NULL the call is fully asynchronous: it
+ * only enqueues kernels (and, below 2048 tokens, an event fork and join with
+ * a second stream), so a caller may capture it in a HIP graph.
  * The routed experts read their rows straight from z through the sorted
  * pair order (the padded tensor is not materialised), skip empty experts and
  * padding rows, and the scatter-add is deterministic (each pair writes its own
