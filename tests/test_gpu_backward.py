@@ -97,11 +97,13 @@ def _cfgs():
         base["toy_n128"].with_(name="toy_n3_sparse", n_tokens=3),
         S.LayerConfig("kR_bf16", 70, 128, 64, 6, 6, 3, 128, 64, "bf16", seed=8, bias="uniform"),
         S.LayerConfig("wide_k_bf16", 333, 256, 128, 40, 9, 1, 192, 256, "bf16", seed=9, bias="uniform"),
-        # 128-multiple widths with every padded pair count 0/64/128/192 (largest 182):
+        # 256-multiple widths with every padded pair count 0/64/128/192 (largest 182):
         # the strip weight-gradient kernel; 420 tokens push one expert to 194
-        # pairs and the batched GEMM path instead
+        # pairs and the batched GEMM path instead; l = 512 gives dW_o two
+        # 256-row strips and dW_g, dW_u four column tiles (same routes)
         _STRIP,
         _STRIP.with_(name="strip_over_bf16", n_tokens=420),
+        _STRIP.with_(name="strip_wide_bf16", d_latent=512),
     ]
 
 
