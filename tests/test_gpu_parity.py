@@ -278,6 +278,47 @@ def test_experts_entry(name):
     assert err <= G.TOL[cfg.dtype]
 
 
+@pytest.mark.slow
+def test_experts_entry_k3_prefill_sample():
+    """The padded entry points at the full-K3 prefill size: dispatch builds the
+    pages' [R, C, l] layout (about 1.2 GB) from a seeded z, and the padded
+    grouped GEMMs give u, checked on sampled tokens against the oracle's
+    sparse routed sum (tokens are independent given the routes)."""
+    cfg = S.CONFIGS["k3full_n8192"]
+    _say(f"[experts full] {cfg.name}")
+    N, R, k, l = cfg.n_tokens, cfg.n_routed, cfg.top_k, cfg.d_latent
+    W = O.config_weights(cfg, cache_experts=2)
+    routes = O.route(O.config_x(cfg), W.w_router, W.bias, k)
+    ids = routes.ids.astype(np.int32)
+    p = routes.p.astype(np.float32)
+    dims = M.dims_of(cfg)
+    z = S.gen.device_tensor(cfg, "z")
+    dev = {n: S.gen.device_tensor(cfg, n) for n in ("w_g", "w_u", "w_o")}
+    d_ids = torch.from_numpy(ids).cuda()
+    counts = torch.empty(R, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(R, dtype=torch.int32, device="cuda")
+    order = torch.empty(N * k, dtype=torch.int32, device="cuda")
+    ws = torch.empty(max(M.workspace_bytes(dims, M.ENTRY_DISPATCH), M.workspace_bytes(dims, M.ENTRY_EXPERTS)),
+                     dtype=torch.uint8, device="cuda")
+    C = M.latentmoe_dispatch(dims, d_ids, None, counts, offsets, order, workspace=ws)
+    padded = torch.empty((R, C, l), dtype=G.torch_dtype(cfg.dtype), device="cuda")
+    M.latentmoe_dispatch(dims, d_ids, z, counts, offsets, order, padded, C, workspace=ws)
+    u = torch.empty((N, l), dtype=torch.float32, device="cuda")
+    M.latentmoe_experts(dims, padded, C, counts, offsets, order, torch.from_numpy(p).cuda(), dev["w_g"],
+                        dev["w_u"], dev["w_o"], u, workspace=ws)
+    torch.cuda.synchronize()
+    assert C == int(np.bincount(ids.reshape(-1), minlength=R).max())
+    rows = np.array([0, 4097, N - 1])
+    z_rows = np.stack([S.to_f64(S.host_tensor(cfg, "z", int(r) * l, l), cfg.dtype) for r in rows])
+    ref = O.routed_sparse(z_rows, routes.ids[rows], p[rows].astype(np.float64), W.experts, R, cfg.beta1,
+                          cfg.beta2)
+    err = G.rel_err(G.download_f64(u[torch.as_tensor(rows)]), ref)
+    _say(f"   C={C} err={err:.3e}")
+    assert err <= G.TOL[cfg.dtype]
+    del padded, dev, ws
+    torch.cuda.empty_cache()
+
+
 def test_device_generator_matches_host():
     for name, tensors in [("toy_n128", ["x", "w_g"]), ("b05skew_n4096", ["w_router", "sh_o"]),
                           ("k3full_n64", ["bias", "w_up"])]:
