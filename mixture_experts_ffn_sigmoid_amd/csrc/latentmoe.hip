@@ -365,9 +365,12 @@ lmoe_status launch_gemm(GemmArgs a, hipStream_t st) {
 //     stream their weights (B) from HBM; the B ring is one stage deeper than
 //     the ring of the (L2-resident) A rows
 //   V  64 x 256, 4 waves, 2/3, 128: the same for a handful of rows per expert
+//   V2 64 x 256, 4 waves, 2/3, 64 (56 KB, two workgroups per CU): the routed
+//     down projection with a handful of rows per expert, whose tiles have few
+//     K steps: one workgroup's ring fill overlaps the other's streaming
 //   M2 128 x 128, 4 waves, 3/3, 64 (48 KB, three workgroups per CU): short-K
 //     products whose time goes into storing the output tile
-enum Tile { TILE_S = 0, TILE_M = 1, TILE_L = 2, TILE_W = 3, TILE_V = 4, TILE_M2 = 5 };
+enum Tile { TILE_S = 0, TILE_M = 1, TILE_L = 2, TILE_W = 3, TILE_V = 4, TILE_M2 = 5, TILE_V2 = 6 };
 
 template <typename TA, typename TB, typename OutT, int AM, int BMD, int EM, int BM, int BN, int WGM,
           int WGN, int SA, int SB, int KB = 64>
@@ -422,6 +425,7 @@ lmoe_status gemm(GemmArgs a, Tile t, hipStream_t st) {
   } else {
     switch (t) {
       case TILE_V: return gemm_cfg<TA, TB, OutT, AM, BMD, EM, 64, 256, 1, 4, 2, 3, 128>(a, st);
+      case TILE_V2: return gemm_cfg<TA, TB, OutT, AM, BMD, EM, 64, 256, 1, 4, 2, 3, 64>(a, st);
       case TILE_M: return gemm_cfg<TA, TB, OutT, AM, BMD, EM, 128, 128, 2, 2, 3, 3, 128>(a, st);
       default: return gemm_cfg<TA, TB, OutT, AM, BMD, EM, 192, 256, 2, 4, 2, 3, 128>(a, st);
     }
@@ -551,7 +555,7 @@ lmoe_status run_experts(const Plan& p, const lmoe_dims* dm, const void* a_src, i
   b.out = slots;
   b.ldo = (int64_t)p.l * sizeof(TH);
   b.probs = probs;
-  return gemm<TH, TW, TH, A_SORTED, B_SINGLE, E_SLOTS>(b, tile, st);
+  return gemm<TH, TW, TH, A_SORTED, B_SINGLE, E_SLOTS>(b, tile == TILE_V ? TILE_V2 : tile, st);
 }
 
 // Batched transpose out[b][c][col0 + r] = in[b][r][c] (16-byte accesses for
