@@ -178,7 +178,9 @@ KERNEL_SOURCES = ("mixture_experts_ffn_sigmoid_amd/csrc/gemm_kernel.h",
                   "mixture_experts_ffn_sigmoid_amd/csrc/merge_kernels.h",
                   "mixture_experts_ffn_sigmoid_amd/csrc/backward_kernels.h",
                   "mixture_experts_ffn_sigmoid_amd/csrc/wgrad_kernel.h",
-                  "mixture_experts_ffn_sigmoid_amd/csrc/latentmoe.hip")
+                  "mixture_experts_ffn_sigmoid_amd/csrc/lmoe_host.h",
+                  "mixture_experts_ffn_sigmoid_amd/csrc/forward.hip",
+                  "mixture_experts_ffn_sigmoid_amd/csrc/backward.hip")
 
 
 def kernel_source_hash() -> str:

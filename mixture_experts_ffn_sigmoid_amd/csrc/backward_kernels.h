@@ -5,6 +5,9 @@
 #include "lmoe_common.h"
 
 namespace lmoe {
+// Internal linkage: every translation unit that launches these kernels
+// carries its own copy.
+namespace {
 
 // Zero n 4-byte words.
 __global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* __restrict__ p, int64_t n) {
@@ -436,4 +439,5 @@ __global__ void set_ints_kernel(int32_t* __restrict__ p, int32_t a, int32_t b, i
   }
 }
 
+}  // namespace
 }  // namespace lmoe

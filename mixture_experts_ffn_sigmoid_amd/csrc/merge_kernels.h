@@ -5,6 +5,9 @@
 #include "lmoe_common.h"
 
 namespace lmoe {
+// Internal linkage: every translation unit that launches these kernels
+// carries its own copy.
+namespace {
 
 constexpr int kMaxLatent = 8192;  // 8 float4 per thread of a 256-thread workgroup
 
@@ -81,4 +84,5 @@ __global__ __launch_bounds__(256) void combine_rmsnorm_kernel(const TS* __restri
   }
 }
 
+}  // namespace
 }  // namespace lmoe

@@ -5,6 +5,9 @@
 #include "lmoe_common.h"
 
 namespace lmoe {
+// Internal linkage: every translation unit that launches these kernels
+// carries its own copy.
+namespace {
 
 constexpr int kMaxRouted = 4096;
 constexpr int kMaxTopK = 64;
@@ -339,4 +342,5 @@ __global__ __launch_bounds__(256) void padded_gather_kernel(const T* __restrict_
   }
 }
 
+}  // namespace
 }  // namespace lmoe
