@@ -25,56 +25,100 @@ PEAK_HBM_GBS = 8000.0
 
 
 def step_models(cfg, counts):
-    """Algorithmic FLOPs and HBM bytes of each timed step (2 FLOP per multiply-add;
-    each needed weight read once, only experts with pairs; activations in/out
-    once at their stored width).  Returns {step: (flops, bytes)}."""
+    """Per timed step: (algorithmic FLOPs, algorithmic HBM bytes, design HBM bytes).
+
+    FLOPs: 2 per multiply-add; the routed work counts the N*k token-expert
+    pairs (no padding).  Algorithmic bytes: the weights the step needs, each
+    read once (routed experts: only those with pairs), plus the layer's input
+    x (read by each step that uses it) and output y at the storage width, the
+    latent z once at the intermediate width (written by the latent step, read
+    by the routed gate/up), and the router's ids and p.  Design bytes: what
+    this implementation moves by design on top of that: the per-pair gather
+    of z rows, the routed hidden h, the p-weighted slot rows, the shared
+    hidden, RMSNorm(u) and the router logits (fp16 intermediates with bf16
+    storage, fp32 with fp32 storage).  Returns {step: (flops, alg, design)}."""
     N, d, l, R, k = cfg.n_tokens, cfg.d_model, cfg.d_latent, cfg.n_routed, cfg.top_k
     fr, fs, ns = cfg.ff_routed, cfg.ff_shared, cfg.n_shared
-    es = 2 if cfg.dtype == "bf16" else 4
+    es = 2 if cfg.dtype == "bf16" else 4  # storage
+    ei = es  # intermediates: fp16 (bf16 storage) or fp32
     P = N * k
     U = int((counts > 0).sum())
+    w_gu, w_o = es * 2 * U * fr * l, es * U * l * fr
     return {
-        "latent_gemm": (2.0 * N * d * l, es * (N * d + l * d + N * l)),
-        "router": (2.0 * N * d * R, es * (N * d + R * d) + 4 * N * R + 8 * N * k),
-        "dispatch": (0.0, 4 * P * 2 + 8 * R),
-        "shared_gateup": (4.0 * N * d * fs * ns, es * (N * d + 2 * ns * fs * d + N * ns * fs)),
-        "routed_gateup": (4.0 * P * l * fr, es * (2 * U * fr * l + P * l + P * fr)),
-        "routed_down": (2.0 * P * fr * l, es * (U * l * fr + P * fr) + 4 * P * l),
-        "combine_rmsnorm": (0.0, 4 * P * l + es * N * l),
-        "merge_gemm": (2.0 * N * (ns * fs + l) * d, es * (N * (ns * fs + l) + d * (ns * fs + l) + N * d)),
+        "latent_gemm": (2.0 * N * d * l, es * (N * d + l * d) + ei * N * l, es * (N * d + l * d) + ei * N * l),
+        "router": (2.0 * N * d * R, es * (N * d + R * d) + 8 * N * k, es * (N * d + R * d) + 8 * N * k + 8 * N * R),
+        "dispatch": (0.0, 8 * P, 8 * P + 8 * R),
+        "shared_gateup": (4.0 * N * d * fs * ns, es * (N * d + 2 * ns * fs * d),
+                          es * (N * d + 2 * ns * fs * d) + ei * N * ns * fs),
+        "routed_gateup": (4.0 * P * l * fr, w_gu + ei * N * l, w_gu + ei * (P * l + P * fr)),
+        "routed_down": (2.0 * P * fr * l, w_o, w_o + ei * (P * fr + P * l)),
+        "combine_rmsnorm": (0.0, 0, ei * (P * l + N * l)),
+        "merge_gemm": (2.0 * N * (ns * fs + l) * d, es * (d * (ns * fs + l) + N * d),
+                       es * (d * (ns * fs + l) + N * d) + ei * N * (ns * fs + l)),
     }
 
 
-def cpu_baseline(cfg, n_sample: int):
+def layer_algorithmic_bytes(cfg, counts) -> float:
+    """The whole layer's algorithmic HBM bytes: every needed weight once
+    (routed experts with pairs only), x read once and y written once."""
+    N, d, l, R = cfg.n_tokens, cfg.d_model, cfg.d_latent, cfg.n_routed
+    fr, fs, ns = cfg.ff_routed, cfg.ff_shared, cfg.n_shared
+    es = 2 if cfg.dtype == "bf16" else 4
+    U = int((counts > 0).sum())
+    weights = l * d + R * d + 3 * U * fr * l + 3 * ns * fs * d + d * l
+    return float(es * (weights + 2 * N * d))
+
+
+def host_cpu() -> dict:
+    """Cores this process may run on (sched_getaffinity) and the CPU model."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"affinity_cores": len(os.sched_getaffinity(0)), "cpu_model": model}
+
+
+def cpu_baseline(cfg, n_sample: int, threads: int | None = None):
     """The oracle (test infrastructure, untuned) on the first n_sample tokens of
-    the workload, on this host's cores.  Weights the sample needs are
-    generated beforehand (untimed); the timed region is the oracle forward."""
+    the workload, on this host's cores (BLAS threads = `threads`, default all
+    cores of the affinity mask).  Weights the sample needs are generated
+    beforehand (untimed); the timed region is the oracle forward."""
     import numpy as np
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     import oracle as O
 
+    cpu = host_cpu()
+    threads = threads or cpu["affinity_cores"]
+    n_sample = min(n_sample, cfg.n_tokens)
     W = O.config_weights(cfg, cache_experts=0)
     x = O.config_x(cfg, rows=np.arange(n_sample))
     routes = O.route(x, W.w_router, W.bias, cfg.top_k)
     need = sorted(set(routes.ids.reshape(-1).tolist()))
     per = cfg.ff_routed * cfg.d_latent
-    stored = {e: tuple(S.host_tensor(cfg, n, e * per, per) for n in ("w_g", "w_u", "w_o")) for e in need}
     fr, l = cfg.ff_routed, cfg.d_latent
+    stored = {e: tuple(S.to_f64(S.host_tensor(cfg, n, e * per, per), cfg.dtype) for n in ("w_g", "w_u", "w_o"))
+              for e in need}
 
     def experts(e):  # the oracle reads stored (bf16 / fp32) weights as exact fp64
         g, u, o = stored[e]
-        return (S.to_f64(g, cfg.dtype).reshape(fr, l), S.to_f64(u, cfg.dtype).reshape(fr, l),
-                S.to_f64(o, cfg.dtype).reshape(l, fr))
+        return g.reshape(fr, l), u.reshape(fr, l), o.reshape(l, fr)
 
     W.experts = experts
-    t0 = time.perf_counter()
-    O.forward(x, W)
-    dt = time.perf_counter() - t0
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    return {"value": n_sample / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {n_sample} tokens of {cfg.name} (all five steps, fp64 numpy; "
-                      f"{len(need)} routed experts touched); {dt:.1f} s"}
+    with threadpool_limits(limits=threads, user_api="blas"):
+        used = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] + [1])
+        t0 = time.perf_counter()
+        O.forward(x, W)
+        dt = time.perf_counter() - t0
+    return {"value": round(n_sample / dt, 3), "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": f"first {n_sample} of {cfg.n_tokens} tokens of {cfg.name} (all five steps, fp64 numpy, "
+                      f"{len(need)} routed experts touched, BLAS threads {used}); {dt:.2f} s",
+            "seconds": round(dt, 3), "gflops": round(cfg.flops() * n_sample / cfg.n_tokens / dt / 1e9, 2), **cpu}
 
 
 def backward_leg(cfg, ids, probs, steps: int, warmup: int):
@@ -281,31 +325,38 @@ def measure_forward(cfg, steps: int, warmup: int) -> dict:
     counts = bufs["counts"].cpu().numpy()
     C = int(counts.max())
     models = step_models(cfg, counts)
-    peak_tf = PEAK_MFMA_TFLOPS[cfg.dtype]
     steps_out = {}
     for name, ms in step_ms.items():
-        fl, by = models[name]
+        fl, alg, design = models[name]
         steps_out[name] = {"ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1),
-                           "gbs": round(by / ms / 1e6, 1)}
+                           "gbs": round(alg / ms / 1e6, 1), "design_gbs": round(design / ms / 1e6, 1)}
     dominant = max(step_ms, key=step_ms.get)
-    fl, by = models[dominant]
-    t_dom = step_ms[dominant] / 1e3
-    mfma_bound = fl / (peak_tf * 1e12) >= by / (PEAK_HBM_GBS * 1e9)
-    if mfma_bound:
-        roof = {"kernel": dominant, "bound": "mfma", "achieved": round(fl / t_dom / 1e12, 1),
-                "peak": peak_tf, "unit": "TFLOP/s"}
-    else:
-        roof = {"kernel": dominant, "bound": "hbm", "achieved": round(by / t_dom / 1e9, 1),
-                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
-    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["algorithmic_bytes"] = by
-    roof["algorithmic_flops"] = fl
-    roof["ms"] = round(step_ms[dominant], 4)
-    roof["traffic"] = measured_traffic(dominant, cfg.name)
-    layer_bytes = float(sum(b for _, b in models.values()))
+    roof = roofline(cfg, dominant, models[dominant], step_ms[dominant])
+    layer_bytes = layer_algorithmic_bytes(cfg, counts)
     del dev
     return dict(ms_step=ms_step, step_ms=step_ms, steps_out=steps_out, roof=roof, C=C, t_wall=t_wall,
-                bufs=bufs, layer_bytes=layer_bytes)
+                bufs=bufs, layer_bytes=layer_bytes, counts=counts)
+
+
+def roofline(cfg, step: str, model, ms: float) -> dict:
+    """Roofline entry of one timed step: MFMA-bound when its FLOPs need more
+    time at the MFMA peak than its algorithmic bytes at the HBM peak."""
+    fl, alg, design = model
+    peak_tf = PEAK_MFMA_TFLOPS[cfg.dtype]
+    t = ms / 1e3
+    if fl / (peak_tf * 1e12) >= alg / (PEAK_HBM_GBS * 1e9):
+        roof = {"kernel": step, "bound": "mfma", "achieved": round(fl / t / 1e12, 1), "peak": peak_tf,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"kernel": step, "bound": "hbm", "achieved": round(alg / t / 1e9, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["algorithmic_bytes"] = alg
+    roof["design_bytes"] = design
+    roof["algorithmic_flops"] = fl
+    roof["ms"] = round(ms, 4)
+    roof["traffic"] = measured_traffic(step, cfg.name)
+    return roof
 
 
 def secondary_decode(steps: int, warmup: int) -> dict:
@@ -327,6 +378,35 @@ def secondary_decode(steps: int, warmup: int) -> dict:
     return out
 
 
+def small_workloads(names, steps: int, warmup: int, cpu: bool) -> dict:
+    """The other configured layers (toy fp32, 0.5b, skewed 0.5b): GPU step
+    time, tokens/s, TFLOP/s and the fraction of the matching MFMA peak (fp32
+    for the toy layer), the roofline of the slowest step, the padded-capacity
+    waste R*C / pairs, and the oracle's CPU time on the whole workload (all
+    cores; for the toy and 0.5b layers also one thread)."""
+    import torch
+
+    out = {}
+    for name in names:
+        cfg = S.CONFIGS[name]
+        fm = measure_forward(cfg, max(steps, 50), warmup)
+        ms = fm["ms_step"]
+        peak = PEAK_MFMA_TFLOPS[cfg.dtype]
+        tf = cfg.flops() / (ms / 1e3) / 1e12
+        e = {"ms_per_step": round(ms, 5), "tokens_per_s": round(cfg.n_tokens / (ms / 1e3), 1),
+             "tflops": round(tf, 2), "mfma_frac": round(tf / peak, 4), "peak_tflops": peak, "dtype": cfg.dtype,
+             "capacity": fm["C"], "padded_over_pairs": round(cfg.n_routed * fm["C"] / cfg.pairs, 3),
+             "roofline": fm["roof"], "steps_breakdown": fm["steps_out"]}
+        del fm
+        torch.cuda.empty_cache()
+        if cpu:
+            e["cpu_oracle"] = cpu_baseline(cfg, cfg.n_tokens)
+            if name in ("toy_n128", "b05_n4096"):
+                e["cpu_oracle_1thread"] = cpu_baseline(cfg, cfg.n_tokens, threads=1)
+        out[name] = e
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -337,6 +417,8 @@ def main():
     ap.add_argument("--no-backward", action="store_true", help="skip the backward legs (routed block and whole layer)")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the few-token (64-token, full-K3) forward measured after the prefill workload")
+    ap.add_argument("--no-small", action="store_true",
+                    help="skip the toy / 0.5b / skewed 0.5b layers measured after the prefill workload")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (FETCH_SIZE / WRITE_SIZE calibration)")
     args = ap.parse_args()
@@ -394,6 +476,9 @@ def main():
         del bufs, fm
         torch.cuda.empty_cache()
         out["secondary"] = secondary_decode(args.steps, args.warmup)
+    if cfg.name == "k3full_n8192" and not args.no_small:
+        out["workloads"] = small_workloads(("toy_n128", "b05_n4096", "b05skew_n4096"), args.steps, args.warmup,
+                                           args.cpu_sample > 0)
     print(json.dumps(out), flush=True)
 
 

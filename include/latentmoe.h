@@ -20,18 +20,28 @@
  *  - Storage type: dims->dtype selects fp32 (LMOE_F32) or bf16 (LMOE_BF16) for
  *    x, every weight matrix, the padded tensor and y.  bias, rms_w, probs,
  *    logits and u are always fp32.  Accumulation is always fp32.  In bf16 mode
- *    the intermediates that feed a second matrix product -- z, the SiTU hidden
- *    h and RMSNorm(u) -- are held in fp16 (11-bit significand), and the bf16
- *    weights they meet are widened to fp16 (exact for |w| >= 2^-14).  fp16's
- *    range is safe for them: |h| < beta1*beta2 by the SiTU bound, |RMSNorm(u)|
- *    <= sqrt(l) * max|rms_w|, and z = W_down x stays far below 65504 for
- *    unit-scale (pre-normed) x.
+ *    the intermediates that feed a second matrix product or a sum -- z, the
+ *    SiTU hidden h, the p-weighted expert outputs (one row per (token, slot)
+ *    pair, summed per token in slot order) and RMSNorm(u) -- are held in fp16
+ *    (11-bit significand), and the bf16 weights they meet are widened to fp16
+ *    (exact for |w| >= 2^-14).  Range: |h| < beta1*beta2 by the SiTU bound
+ *    (bf16 storage requires beta1*beta2 < 65504), |RMSNorm(u)| <= sqrt(l) *
+ *    max|rms_w|, and z = W_down x and p E(z) stay far below 65504 for
+ *    unit-scale (pre-normed) x and N(0, 1/fan_in) weights.  The forward checks
+ *    z, the p-weighted outputs and RMSNorm(u) as it stores them: a value that
+ *    would round to inf in fp16 (or is NaN) raises a flag in the workspace,
+ *    reported as LMOE_ERR_RANGE by the synchronous forward and by
+ *    latentmoe_forward_check.  The backward's fp16 intermediates are not
+ *    checked.
  *  - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL = the
  *    default stream) and is asynchronous unless an entry point says otherwise.
  *  - `workspace` is caller-owned device scratch of at least
  *    latentmoe_workspace_bytes(dims, entry) bytes; the library allocates no
- *    device memory and keeps no state between calls.  Calls that share a
- *    workspace must be ordered on one stream.
+ *    device memory.  Calls that share a workspace must be ordered on one
+ *    stream.  The one state kept between calls: latentmoe_forward's
+ *    overlapped path (N <= 2048, n_shared > 0) creates, on first use by a
+ *    host thread on a device, a second non-blocking stream of default
+ *    priority for that thread and device, kept until the process ends.
  *  - Matrices (x, y, z, the padded tensor, u, du, dz, dy, dx and every weight
  *    and weight-gradient matrix) and the workspace must be 16-byte aligned, as
  *    hipMalloc and torch allocations are: they are moved 16 bytes at a time.
@@ -60,7 +70,9 @@ typedef enum {
   LMOE_ERR_UNSUPPORTED = 2,      /* a shape outside the limits listed above */
   LMOE_ERR_CAPACITY = 3,         /* padded buffer too small for C (C is still reported) */
   LMOE_ERR_WORKSPACE = 4,        /* workspace smaller than latentmoe_workspace_bytes() */
-  LMOE_ERR_HIP = 5               /* a HIP runtime call or launch failed */
+  LMOE_ERR_HIP = 5,              /* a HIP runtime call or launch failed */
+  LMOE_ERR_RANGE = 6             /* bf16 storage: an fp16 intermediate of the forward left fp16's
+                                    range (see the conventions above); outputs unspecified */
 } lmoe_status;
 
 typedef enum { LMOE_F32 = 0, LMOE_BF16 = 1 } lmoe_dtype;
@@ -163,7 +175,11 @@ lmoe_status latentmoe_dispatch(const lmoe_dims* dims, const int32_t* ids, const 
  * padded [R, C, l] as written by latentmoe_dispatch, counts/offsets/order as
  * returned by it, probs [N, k] fp32 (the router's p), w_g/w_u [R, f_r, l],
  * w_o [R, l, f_r].  Padding rows are never read.  Output u [N, l] fp32,
- * overwritten.  Asynchronous. */
+ * overwritten.  Asynchronous.
+ * C is the row stride the padded buffer was laid out with, 1 <= C <= N.  The
+ * pages take C = max counts; with a smaller C the buffer holds only each
+ * expert's first C pairs, and its later pairs are dropped: they add nothing
+ * to u.  No read leaves the R * C * l elements of `padded`. */
 lmoe_status latentmoe_experts(const lmoe_dims* dims, const void* padded, int64_t C,
                               const int32_t* counts, const int32_t* offsets, const int32_t* order,
                               const float* probs, const void* w_g, const void* w_u,
@@ -173,21 +189,34 @@ lmoe_status latentmoe_experts(const lmoe_dims* dims, const void* padded, int64_t
 /* The whole layer, steps 1-5.  x [N, d] in, y [N, d] out (storage dtype).
  * Side outputs (the pages' route bookkeeping): ids [N, k] int32 and
  * probs [N, k] fp32 as from latentmoe_route, counts [R] int32 pairs per
- * expert.  If C_host is not NULL the call waits on `stream` and writes
- * C = max counts there; with C_host NULL the call is fully asynchronous: it
+ * expert.  If C_host is not NULL the call waits on `stream`, writes
+ * C = max counts there and returns LMOE_ERR_RANGE if an fp16 intermediate
+ * left fp16's range; with C_host NULL the call is fully asynchronous: it
  * only enqueues kernels (and, below 2048 tokens, an event fork and join with
- * a second stream), so a caller may capture it in a HIP graph.
+ * a second stream), so a caller may capture it in a HIP graph, and
+ * latentmoe_forward_check reads the range flag afterwards.
  * The routed experts read their rows straight from z through the sorted
  * pair order (the padded tensor is not materialised), skip empty experts and
  * padding rows, and the scatter-add is deterministic (each pair writes its own
  * slot; slots are summed in slot order).  For N <= 2048 the shared experts'
- * gate/up GEMM runs on a second, library-owned stream of the current device,
- * forked from and joined back into `stream` with events (capturable as a
- * fork/join in a HIP graph); all other work is on `stream`. */
+ * gate/up GEMM runs on a second, library-owned stream (one per calling host
+ * thread and device), forked from and joined back into `stream` with events
+ * (capturable as a fork/join in a HIP graph); all other work is on
+ * `stream`. */
 lmoe_status latentmoe_forward(const lmoe_dims* dims, const lmoe_weights* weights, const void* x,
                               void* y, int32_t* ids, float* probs, int32_t* counts,
                               int64_t* C_host, void* workspace, size_t workspace_bytes,
                               void* stream);
+
+/* Range status of the last latentmoe_forward (or latentmoe_forward_timed)
+ * enqueued with this workspace and dims: waits on `stream`, then returns
+ * LMOE_ERR_RANGE if an fp16 intermediate of that forward left fp16's range
+ * (its y is then unspecified), LMOE_OK otherwise.  For callers of the
+ * asynchronous form (C_host NULL), e.g. after replaying a captured forward.
+ * Errors: INVALID_ARGUMENT for bad dims, WORKSPACE for a missing or short
+ * workspace. */
+lmoe_status latentmoe_forward_check(const lmoe_dims* dims, const void* workspace, size_t workspace_bytes,
+                                    void* stream);
 
 /* Backward of the routed-expert block u = sum_j p_j E_{ids_j}(z) (chapter
  * step 3 and the sparse-execution section, differentiated; the pages train

@@ -14,14 +14,14 @@ LIB_PATH = os.path.join(PKG, "liblatentmoe.so")
 
 LMOE_F32, LMOE_BF16 = 0, 1
 ENTRY_ROUTE, ENTRY_DISPATCH, ENTRY_EXPERTS, ENTRY_FORWARD, ENTRY_ROUTED_BACKWARD, ENTRY_BACKWARD = 0, 1, 2, 3, 4, 5
-STATUS = {0: "OK", 1: "INVALID_ARGUMENT", 2: "UNSUPPORTED", 3: "CAPACITY", 4: "WORKSPACE", 5: "HIP"}
+STATUS = {0: "OK", 1: "INVALID_ARGUMENT", 2: "UNSUPPORTED", 3: "CAPACITY", 4: "WORKSPACE", 5: "HIP", 6: "RANGE"}
 
 # every symbol include/latentmoe.h declares
 EXPORTS = (
     "latentmoe_workspace_bytes", "latentmoe_status_string", "latentmoe_last_error",
     "latentmoe_route", "latentmoe_dispatch", "latentmoe_experts", "latentmoe_forward",
     "latentmoe_forward_timed", "latentmoe_route_softmax", "latentmoe_router_losses_workspace_bytes",
-    "latentmoe_router_losses", "latentmoe_routed_backward", "latentmoe_backward",
+    "latentmoe_router_losses", "latentmoe_routed_backward", "latentmoe_backward", "latentmoe_forward_check",
 )
 GRAD_NAMES = ("w_down", "w_router", "w_g", "w_u", "w_o", "sh_g", "sh_u", "sh_o", "rms_w", "w_up")
 TIMING_EVENTS = 9
@@ -79,6 +79,7 @@ def load() -> ctypes.CDLL:
     lib.latentmoe_forward_timed.argtypes = [D, ctypes.POINTER(Weights), vp, vp, vp, vp, vp, vp, st, vp,
                                             ctypes.POINTER(vp), i32]
     lib.latentmoe_route_softmax.argtypes = [D, vp, vp, vp, vp, vp, vp, st, vp]
+    lib.latentmoe_forward_check.argtypes = [D, vp, st, vp]
     lib.latentmoe_router_losses_workspace_bytes.argtypes = [D]
     lib.latentmoe_router_losses_workspace_bytes.restype = st
     lib.latentmoe_router_losses.argtypes = [D, vp, vp, vp, vp, st, vp]
@@ -87,7 +88,7 @@ def load() -> ctypes.CDLL:
                                        st, vp]
     for fn in ("latentmoe_route", "latentmoe_dispatch", "latentmoe_experts", "latentmoe_forward",
                "latentmoe_forward_timed", "latentmoe_route_softmax", "latentmoe_router_losses",
-               "latentmoe_routed_backward", "latentmoe_backward"):
+               "latentmoe_routed_backward", "latentmoe_backward", "latentmoe_forward_check"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -229,3 +230,12 @@ def latentmoe_forward_timed(dims, weights, x, y, ids, probs, counts, events, wor
                                          ptr(probs), ptr(counts), ptr(ws),
                                          0 if ws is None else ws.numel() * ws.element_size(),
                                          stream_handle(stream), handles, len(events)))
+
+
+def latentmoe_forward_check(dims, workspace, stream=None):
+    """Raises LatentMoEError (status RANGE) if the last forward enqueued with
+    this workspace left fp16's range in an intermediate."""
+    ws = workspace
+    check(load().latentmoe_forward_check(ctypes.byref(dims), ptr(ws),
+                                         0 if ws is None else ws.numel() * ws.element_size(),
+                                         stream_handle(stream)))

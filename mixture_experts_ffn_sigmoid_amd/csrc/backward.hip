@@ -275,7 +275,7 @@ lmoe_status run_layer_backward(const Plan& p, const lmoe_dims* dm, const lmoe_we
   pair_sum_kernel<float><<<(unsigned)N, 256, 0, st>>>(rw.o, rw.inv, p.k, l, probs, w.u, l);
   LMOE_HIP(hipGetLastError());
   combine_rmsnorm_kernel<float, TI><<<(unsigned)N, 256, 0, st>>>(w.u, 1, l, nullptr, W->rms_w, dm->rms_eps,
-                                                                 (TI*)w.rn, l);
+                                                                 (TI*)w.rn, l, nullptr);
   LMOE_HIP(hipGetLastError());
   if (nsf > 0) {
     LMOE_TRY((gemm<T, T, float, A_DENSE, B_SINGLE, E_STORE>(

@@ -49,7 +49,7 @@ lmoe_status run_experts(const Plan& p, const lmoe_dims* dm, const void* a_src, i
                         const int32_t* counts, const int32_t* offsets, const int32_t* order,
                         const float* probs, const void* w_g, const void* w_u, const void* w_o,
                         int32_t* tile_list, int32_t* meta, char* h, char* slots, hipStream_t st,
-                        Mark* mark = nullptr) {
+                        int32_t* range_flag, Mark* mark = nullptr) {
   tile_list_kernel<<<1, 1024, 0, st>>>(counts, p.R, p.tile_m, tile_list, meta);
   LMOE_HIP(hipGetLastError());
   const Tile tile = p.tile_m == 64 ? TILE_V : p.tile_m == 128 ? TILE_M : TILE_W;
@@ -95,6 +95,8 @@ lmoe_status run_experts(const Plan& p, const lmoe_dims* dm, const void* a_src, i
   b.out = slots;
   b.ldo = (int64_t)p.l * sizeof(TH);
   b.probs = probs;
+  b.cap = AM == A_PADDED ? cap : 0;  // pairs past the padded capacity are dropped
+  b.range_flag = range_flag;
   return gemm<TH, TW, TH, A_SORTED, B_SINGLE, E_SLOTS>(b, tile == TILE_V ? TILE_V2 : tile, st);
 }
 
@@ -130,6 +132,10 @@ lmoe_status run_forward(const Plan& p, const lmoe_dims* dm, const lmoe_weights* 
     return LMOE_OK;
   };
   LMOE_TRY(mark());
+  // meta: C, tile count, bad ids, range flag -- all cleared (a fill kernel,
+  // not a memset node, so a captured forward replays correctly)
+  set_ints_kernel<<<1, 64, 0, st>>>(w.meta, 0, 0, 0, 0);
+  LMOE_HIP(hipGetLastError());
   // The shared experts depend on x only.  For small batches (whose GEMMs
   // leave most CUs idle) and without timing marks they run on a second
   // stream, next to steps 1-3 and the routed experts; the merge GEMM waits
@@ -167,6 +173,7 @@ lmoe_status run_forward(const Plan& p, const lmoe_dims* dm, const lmoe_weights* 
   a.ldo = (int64_t)p.l * p.es;
   a.part = w.part;
   a.part_bytes = w.part_bytes;
+  a.range_flag = w.meta + kMetaRange;
   LMOE_TRY((gemm<T, T, TI, A_DENSE, B_SINGLE, E_STORE>(a, dense_tile(p.N, p.l, false), st)));
   LMOE_TRY(mark());
   // 2. routing
@@ -181,12 +188,12 @@ lmoe_status run_forward(const Plan& p, const lmoe_dims* dm, const lmoe_weights* 
   // 3b. routed experts straight from z -> slots
   LMOE_TRY((run_experts<TI, T, TI, A_GATHER>(p, dm, w.z, 0, counts, w.offsets, w.order, probs, W->w_g,
                                      W->w_u, W->w_o, w.tile_list, w.meta, w.h, w.slots, st,
-                                     ev ? &mark : nullptr)));
+                                     w.meta + kMetaRange, ev ? &mark : nullptr)));
   LMOE_TRY(mark());
   // 5a. u = sum of slots, RMSNorm -> hcat[:, n_s f_s:]
   combine_rmsnorm_kernel<TI, TI><<<(unsigned)p.N, 256, 0, st>>>(
       (const TI*)w.slots, p.k, p.l, nullptr, W->rms_w, dm->rms_eps,
-      (TI*)(w.hcat + (int64_t)p.ns * p.fs * p.es), p.ldh);
+      (TI*)(w.hcat + (int64_t)p.ns * p.fs * p.es), p.ldh, w.meta + kMetaRange);
   LMOE_HIP(hipGetLastError());
   LMOE_TRY(mark());
   if (overlap) LMOE_HIP(hipStreamWaitEvent(st, evs.join, 0));
@@ -229,6 +236,7 @@ const char* latentmoe_status_string(lmoe_status s) {
     case LMOE_ERR_CAPACITY: return "padded capacity smaller than C";
     case LMOE_ERR_WORKSPACE: return "workspace too small";
     case LMOE_ERR_HIP: return "HIP runtime error";
+    case LMOE_ERR_RANGE: return "an fp16 intermediate left fp16's range";
   }
   return "unknown status";
 }
@@ -407,16 +415,16 @@ lmoe_status latentmoe_experts(const lmoe_dims* dims, const void* padded, int64_t
   hipStream_t st = launch_stream(stream);
   if (p.bf16)
     LMOE_TRY((run_experts<bf16_t, bf16_t, f16_t, A_PADDED>(p, dims, padded, C, counts, offsets, order, probs, w_g,
-                                            w_u, w_o, w.tile_list, w.meta, w.h, w.slots, st)));
+                                            w_u, w_o, w.tile_list, w.meta, w.h, w.slots, st, nullptr)));
   else
     LMOE_TRY((run_experts<float, float, float, A_PADDED>(p, dims, padded, C, counts, offsets, order, probs, w_g, w_u,
-                                           w_o, w.tile_list, w.meta, w.h, w.slots, st)));
+                                           w_o, w.tile_list, w.meta, w.h, w.slots, st, nullptr)));
   if (p.bf16)
     combine_rmsnorm_kernel<f16_t, f16_t><<<(unsigned)p.N, 256, 0, st>>>(
-        (const f16_t*)w.slots, p.k, p.l, u, nullptr, 0.f, nullptr, 0);
+        (const f16_t*)w.slots, p.k, p.l, u, nullptr, 0.f, nullptr, 0, nullptr);
   else
     combine_rmsnorm_kernel<float, float><<<(unsigned)p.N, 256, 0, st>>>(
-        (const float*)w.slots, p.k, p.l, u, nullptr, 0.f, nullptr, 0);
+        (const float*)w.slots, p.k, p.l, u, nullptr, 0.f, nullptr, 0, nullptr);
   LMOE_HIP(hipGetLastError());
   return LMOE_OK;
 }
@@ -450,10 +458,13 @@ lmoe_status forward_impl(const lmoe_dims* dims, const lmoe_weights* weights, con
   if (p.bf16) LMOE_TRY((run_forward<bf16_t, f16_t>(p, dims, W, x, y, ids, probs, counts, w, st, ev)));
   else LMOE_TRY((run_forward<float, float>(p, dims, W, x, y, ids, probs, counts, w, st, ev)));
   if (C_host) {
-    int32_t C = 0;
-    LMOE_HIP(hipMemcpyAsync(&C, w.meta, sizeof(int32_t), hipMemcpyDeviceToHost, st));
+    int32_t meta[4] = {0, 0, 0, 0};
+    LMOE_HIP(hipMemcpyAsync(meta, w.meta, sizeof(meta), hipMemcpyDeviceToHost, st));
     LMOE_HIP(hipStreamSynchronize(st));
-    *C_host = C;
+    *C_host = meta[kMetaC];
+    if (meta[kMetaRange])
+      return fail(LMOE_ERR_RANGE, "an fp16 intermediate (z, a p-weighted expert output or RMSNorm(u)) "
+                                  "left fp16's range; y is unspecified");
   }
   return LMOE_OK;
 }
@@ -480,6 +491,26 @@ lmoe_status latentmoe_forward_timed(const lmoe_dims* dims, const lmoe_weights* w
     if (!events[i]) return fail(LMOE_ERR_INVALID_ARGUMENT, "NULL event");
   return forward_impl(dims, weights, x, y, ids, probs, counts, nullptr, workspace, workspace_bytes,
                       stream, (hipEvent_t*)events);
+}
+
+lmoe_status latentmoe_forward_check(const lmoe_dims* dims, const void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  Plan p;
+  LMOE_TRY(check_dims(dims, &p));
+  if (p.N == 0) return LMOE_OK;
+  ForwardWs w{};
+  const size_t need = carve_forward(p, nullptr, &w);
+  if (!workspace || workspace_bytes < need)
+    return fail(LMOE_ERR_WORKSPACE, "forward needs %zu workspace bytes", need);
+  carve_forward(p, (char*)workspace, &w);
+  hipStream_t st = launch_stream(stream);
+  int32_t flag = 0;
+  LMOE_HIP(hipMemcpyAsync(&flag, w.meta + kMetaRange, sizeof(flag), hipMemcpyDeviceToHost, st));
+  LMOE_HIP(hipStreamSynchronize(st));
+  if (flag)
+    return fail(LMOE_ERR_RANGE, "an fp16 intermediate (z, a p-weighted expert output or RMSNorm(u)) "
+                                "left fp16's range; y is unspecified");
+  return LMOE_OK;
 }
 
 }  // extern "C"

@@ -70,7 +70,7 @@ struct GemmArgs {
   int64_t lda;  // bytes
   const int32_t* order;
   int top_k;
-  int64_t cap;  // A_PADDED: rows per expert
+  int64_t cap;  // A_PADDED: rows per expert; E_SLOTS: pairs kept per expert (0: all)
   // grouped tiles
   const int32_t* tile_list;  // (expert, m0) pairs
   const int32_t* tile_count;
@@ -106,7 +106,13 @@ struct GemmArgs {
   int64_t ldo;  // bytes (E_SLOTS: fp32 elements per slot row * 4)
   const float* probs;
   float beta1, beta2;
+  // E_STORE / E_SLOTS with fp16 output: set to 1 when a stored value leaves
+  // fp16's range (|v| >= 65520 rounds to inf) or is NaN (NULL: no check)
+  int32_t* range_flag;
 };
+
+// A value whose fp16 rounding is not finite.
+__device__ __forceinline__ bool f16_out_of_range(float v) { return !(fabsf(v) < 65520.0f); }
 
 // s_waitcnt immediate that waits until at most n vector-memory operations of
 // this wave are outstanding (gfx9 encoding; expcnt / lgkmcnt left at "no wait").
@@ -240,14 +246,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
   const int64_t k0b = (int64_t)kt0 * ROWB;
   // E_SLOTS: slot row q and weight p_q of every tile row, fetched now (their
   // latency hides behind the main loop) into LDS outside the operand ring;
-  // the main loop's barriers publish them to every wave.
+  // the main loop's barriers publish them to every wave.  With cap > 0 the
+  // pairs at positions >= cap of their expert are dropped: weight 0.
   __shared__ int slot_row[EMODE == E_SLOTS ? BM : 1];
   __shared__ float slot_p[EMODE == E_SLOTS ? BM : 1];
   if constexpr (EMODE == E_SLOTS) {
     for (int r = tid; r < BM; r += 64 * NW) {
       const int q = r < rows_valid ? args.order[off + m0 + r] : 0;
+      const bool kept = r < rows_valid && (args.cap == 0 || m0 + r < args.cap);
       slot_row[r] = q;
-      slot_p[r] = r < rows_valid ? args.probs[q] : 0.f;
+      slot_p[r] = kept ? args.probs[q] : 0.f;
     }
   }
 
@@ -268,7 +276,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
   const char* a_base;
   uint32_t a_off[A_W];
   if constexpr (AMODE == A_GATHER) a_base = args.a;
-  else if constexpr (AMODE == A_PADDED) a_base = args.a + ((int64_t)e * args.cap + m0) * args.lda;
+  else if constexpr (AMODE == A_PADDED) a_base = args.a + (int64_t)e * args.cap * args.lda;
   else if constexpr (AMODE == A_SORTED) a_base = args.a + (off + m0) * args.lda;
   else a_base = args.a + (int64_t)kbeg * args.M * (int64_t)sizeof(TA) + (int64_t)m0 * lda + k0b;
 #pragma unroll
@@ -276,6 +284,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
     const int rr = min((wave * A_W + ii) * RPI + lane / NCH, rows_valid - 1);
     int64_t row = rr;
     if constexpr (AMODE == A_GATHER) row = args.order[off + m0 + rr] / args.top_k;
+    // the padded buffer holds an expert's first cap pairs: later pairs
+    // (dropped, weighted 0 by the down projection) reread row cap - 1
+    if constexpr (AMODE == A_PADDED) row = min(m0 + rr, (int)args.cap - 1);
     a_off[ii] = (uint32_t)(row * lda) + lane_chunk(wave * A_W + ii);
   }
   // B_KMAJOR stage: KE = KB / 2 K-rows of BN values (ROWK bytes, NCR 16-byte
@@ -609,6 +620,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
     else return GROUPED ? off + m0 + r : (int64_t)(m0 + r);
   };
 
+  constexpr bool kRangeCheck = EMODE != E_SITU && __is_same(OutT, f16_t);
+  bool out_of_range = false;
   if constexpr (kStaged) {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();  // every wave is done reading the ring
@@ -631,6 +644,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
           const int rl = i * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
           float val = value(i, j, v);
           if constexpr (EMODE == E_SLOTS) val *= ps[v];
+          if constexpr (kRangeCheck) out_of_range |= f16_out_of_range(val);
           Elem<OutT>::store((OutT*)(E + pos(rl, cb >> 4) + (cb & 15)), val);
         }
       }
@@ -663,11 +677,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
           if (r >= rows_valid) continue;
           float val = value(i, j, v);
           if constexpr (EMODE == E_SLOTS) val *= slot_p[r];
+          if constexpr (kRangeCheck) out_of_range |= f16_out_of_range(val);
           Elem<OutT>::store((OutT*)(outp + out_row(r) * args.ldo) + col, val);
         }
       }
     }
   }
+  // rows past the valid range hold finite (clamped-row) values, so a flag
+  // raised by them is raised by a valid row too
+  if constexpr (kRangeCheck)
+    if (out_of_range && args.range_flag) *args.range_flag = 1;  // any lane: every writer stores 1
 }
 
 // Sum of the K slices' fp32 partial products in slice order, stored as OutT:
@@ -676,7 +695,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
 // loads issued four at a time.
 template <typename OutT>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int S, int M, int N,
-                                                            char* __restrict__ out, int64_t ldo) {
+                                                            char* __restrict__ out, int64_t ldo,
+                                                            int32_t* __restrict__ range_flag) {
+  constexpr bool kRangeCheck = __is_same(OutT, f16_t);
+  bool out_of_range = false;
   const int64_t MN = (int64_t)M * N;
   const bool vec = (N & 3) == 0;
   for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; i < MN; i += (int64_t)gridDim.x * 1024) {
@@ -697,15 +719,20 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
         for (int q = 0; q < 4; ++q) acc[q] += a[q];
       }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) Elem<OutT>::store(dst + q, acc[q]);
+      for (int q = 0; q < 4; ++q) {
+        if constexpr (kRangeCheck) out_of_range |= f16_out_of_range(acc[q]);
+        Elem<OutT>::store(dst + q, acc[q]);
+      }
     } else {
       for (int64_t j = i; j < i + 4 && j < MN; ++j) {
         float acc = 0.f;
         for (int sl = 0; sl < S; ++sl) acc += part[sl * MN + j];
+        if constexpr (kRangeCheck) out_of_range |= f16_out_of_range(acc);
         Elem<OutT>::store((OutT*)(out + (j / N) * ldo) + j % N, acc);
       }
     }
   }
+  if (out_of_range && range_flag) *range_flag = 1;
 }
 
 }  // namespace lmoe

@@ -102,6 +102,9 @@ lmoe_status check_dims(const lmoe_dims* dm, Plan* p) {
   if (!(dm->rms_eps >= 0.f)) return fail(LMOE_ERR_INVALID_ARGUMENT, "rms_eps < 0");
   if (dm->dtype != LMOE_F32 && dm->dtype != LMOE_BF16)
     return fail(LMOE_ERR_INVALID_ARGUMENT, "unknown dtype %d", dm->dtype);
+  // bf16 storage keeps the SiTU hidden in fp16: its bound beta1 * beta2 must fit
+  if (dm->dtype == LMOE_BF16 && !((double)dm->beta1 * (double)dm->beta2 < 65504.0))
+    return fail(LMOE_ERR_UNSUPPORTED, "beta1 * beta2 must stay below 65504 with bf16 storage");
   if (dm->d_model % 64 || dm->d_latent % 64 || dm->ff_routed % 64 ||
       (dm->n_shared > 0 && dm->ff_shared % 64))
     return fail(LMOE_ERR_UNSUPPORTED, "d, l, f_r, f_s must be multiples of 64");
@@ -336,18 +339,24 @@ size_t carve_layer_backward(const Plan& p, char* b, LayerBwdWs* w) {
   return c.off;
 }
 
+// Words of a workspace's meta block: C (dispatch), the grouped tile count,
+// the count of expert ids outside [0, R), and the range flag (set when an
+// fp16 intermediate of the forward left fp16's range).
+constexpr int kMetaC = 0, kMetaTiles = 1, kMetaBadIds = 2, kMetaRange = 3;
+
 // Largest batch whose shared-expert GEMM runs on the second stream.
 constexpr int64_t kOverlapMaxTokens = 2048;
 
-// A second stream per device on which the shared-expert GEMM overlaps the
-// routed experts (default priority, non-blocking, created once per device).
+// A second stream on which the shared-expert GEMM overlaps the routed
+// experts: default priority, non-blocking, created on first use for each
+// (host thread, device) and kept until the process ends.  Per thread, so
+// that one thread capturing a forward into a graph never captures (or
+// breaks) another thread's forward on the same device.
 lmoe_status side_stream(hipStream_t* out) {
-  static std::mutex mu;
-  static hipStream_t streams[64] = {};
+  thread_local hipStream_t streams[64] = {};
   int dev = 0;
   LMOE_HIP(hipGetDevice(&dev));
   if (dev < 0 || dev >= 64) return fail(LMOE_ERR_UNSUPPORTED, "device index %d", dev);
-  std::lock_guard<std::mutex> lock(mu);
   if (!streams[dev]) LMOE_HIP(hipStreamCreateWithFlags(&streams[dev], hipStreamNonBlocking));
   *out = streams[dev];
   return LMOE_OK;
@@ -419,7 +428,7 @@ lmoe_status gemm(GemmArgs a, Tile t, hipStream_t st) {
       if (ps != LMOE_OK) return ps;
       const int64_t mn = (int64_t)a.M * a.N;
       splitk_reduce_kernel<OutT><<<(unsigned)std::min<int64_t>((mn + 1023) / 1024, 2048), 256, 0, st>>>(
-          (const float*)a.part, S, a.M, a.N, a.out, a.ldo);
+          (const float*)a.part, S, a.M, a.N, a.out, a.ldo, a.range_flag);
       LMOE_HIP(hipGetLastError());
       return LMOE_OK;
     }

@@ -30,12 +30,13 @@ __device__ __forceinline__ f32x4 load4(const TS* p) {
 //   u[c] = sum_{j < k} slots[(n k + j) l + c]      (slot order)
 //   u_out[n, c] = u[c]                               (if u_out)
 //   dst[n, c]   = T(w[c] u[c] / sqrt(mean(u^2) + eps)) (if dst; w = 1 when rms_w is NULL)
+// With fp16 dst, *range_flag = 1 when a stored value is not finite in fp16.
 template <typename TS, typename T>
 __global__ __launch_bounds__(256) void combine_rmsnorm_kernel(const TS* __restrict__ slots, int k,
                                                               int ell, float* __restrict__ u_out,
                                                               const float* __restrict__ rms_w,
                                                               float eps, T* __restrict__ dst,
-                                                              int64_t ld_dst) {
+                                                              int64_t ld_dst, int32_t* __restrict__ range_flag) {
   constexpr int kVec = kMaxLatent / 1024;
   __shared__ float red[4];
   const int64_t n = blockIdx.x;
@@ -71,6 +72,7 @@ __global__ __launch_bounds__(256) void combine_rmsnorm_kernel(const TS* __restri
   __syncthreads();
   const float total = (red[0] + red[1]) + (red[2] + red[3]);
   const float r = 1.0f / sqrtf(total / (float)ell + eps);
+  bool out_of_range = false;
 #pragma unroll
   for (int i = 0; i < kVec; ++i) {
     const int c = 4 * t + 1024 * i;
@@ -78,10 +80,13 @@ __global__ __launch_bounds__(256) void combine_rmsnorm_kernel(const TS* __restri
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const float w = rms_w ? rms_w[c + q] : 1.f;
-        Elem<T>::store(dst + n * ld_dst + c + q, u[i][q] * r * w);
+        const float v = u[i][q] * r * w;
+        if constexpr (__is_same(T, f16_t)) out_of_range |= !(fabsf(v) < 65520.0f);
+        Elem<T>::store(dst + n * ld_dst + c + q, v);
       }
     }
   }
+  if (out_of_range && range_flag) *range_flag = 1;
 }
 
 }  // namespace

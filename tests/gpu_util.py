@@ -2,11 +2,14 @@
 compare with the oracle under the near-tie routing rule."""
 from __future__ import annotations
 
+import dataclasses
+
 import numpy as np
 import torch
 
 import lmoe_synth as S
 import mixture_experts_ffn_sigmoid_amd as M
+import oracle as O
 
 MARGIN = 1e-4  # routing sets must match exactly where the top-k margin exceeds this
 
@@ -92,3 +95,102 @@ def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
 
 
 TOL = {"f32": 1e-4, "bf16": 2e-2}
+# u = sum_j p_j E_j(z) in fp32, from the routed experts alone.  With bf16
+# storage two fp16 roundings sit on its path (the hidden h and each
+# p-weighted slot), each about 2^-12 relative rms per term; the largest of
+# ~10^6-10^7 elements lies within ~6 sigma, so max|du| / rms(u) stays near
+# 2 * 6 * 2^-12 = 3e-3 (measured 2e-3).  The bar is 5e-3; the fp32 bar is y's.
+TOL_U = {"f32": 1e-4, "bf16": 5e-3}
+
+
+# ------------------------------------------------ oracle inputs at full size
+class DeviceExperts:
+    """Routed expert weights for the oracle, taken from the device copy of the
+    seeded inputs (written by the seeded generator, which a GPU test shows is
+    bit-identical to the host generator; ``check_device_copy`` compares the
+    copies a test uses as well).  Each block of experts is cast to fp64 on the
+    device (bf16 and fp32 convert exactly) and copied to the host when the
+    oracle first asks for one of them; the oracle walks experts in ascending
+    order.  This replaces regenerating every full-K3 expert on the host
+    (about 0.75 s each)."""
+
+    def __init__(self, cfg, dev: dict, block: int = 8):
+        R, l, f = cfg.n_routed, cfg.d_latent, cfg.ff_routed
+        self.w = (dev["w_g"].reshape(R, f, l), dev["w_u"].reshape(R, f, l), dev["w_o"].reshape(R, l, f))
+        self.R, self.block = R, block
+        self.lo, self.hi, self.cache = 0, 0, None
+
+    def __call__(self, e: int):
+        if not self.lo <= e < self.hi:
+            self.lo, self.hi = e, min(e + self.block, self.R)
+            self.cache = [w[self.lo:self.hi].double().cpu().numpy() for w in self.w]
+        i = e - self.lo
+        return self.cache[0][i], self.cache[1][i], self.cache[2][i]
+
+
+def check_device_copy(cfg, dev: dict, experts) -> None:
+    """The device copies of the routed weights of `experts` equal the host
+    generator's values bit for bit."""
+    R, l, f = cfg.n_routed, cfg.d_latent, cfg.ff_routed
+    per = f * l
+    for n in ("w_g", "w_u", "w_o"):
+        t = dev[n].reshape(R, per)
+        for e in experts:
+            host = S.host_tensor(cfg, n, int(e) * per, per)
+            got = t[int(e)]
+            got = got.view(torch.int16).cpu().numpy().view(np.uint16) if cfg.dtype == "bf16" else got.cpu().numpy()
+            assert np.array_equal(got, host), (n, e)
+
+
+_DENSE_CACHE: dict = {}
+
+
+def oracle_weights(cfg, dev: dict | None = None):
+    """fp64 weights for the oracle.  The dense ones (W_down, W_r, the shared
+    experts, W_up) come from the host generator, kept for the next test of
+    the same layer (the weights do not depend on N); with `dev` the routed
+    experts are read from the device copy (``DeviceExperts``), else
+    regenerated on the host one expert at a time."""
+    key = cfg.with_(name="", n_tokens=0)
+    W = _DENSE_CACHE.get(key)
+    if W is None:
+        _DENSE_CACHE.clear()
+        W = O.config_weights(cfg, cache_experts=2)
+        _DENSE_CACHE[key] = W
+    if dev is not None:
+        W = dataclasses.replace(W, experts=DeviceExperts(cfg, dev))
+    return W
+
+
+def stratified_tokens(ids: np.ndarray, R: int, n_target: int, near: np.ndarray | None = None,
+                      seed: int = 0) -> np.ndarray:
+    """Token rows for output parity at full size, sorted:
+      - for every position r an expert's pair list reaches (r < C), a token
+        whose pair sits at position r of some expert (so every row of the
+        grouped GEMMs' row tiles is checked; experts taken in rotation);
+      - tokens of the 8 most- and the 8 least-loaded experts with pairs;
+      - every near-tie token (when `near` is given), the first and the last;
+      - random tokens up to n_target (all tokens when n_target >= N)."""
+    N, k = ids.shape
+    if n_target >= N:
+        return np.arange(N)
+    rng = np.random.default_rng(seed)
+    disp = O.dispatch(ids, R)
+    pick = {0, N - 1}
+    eid = ids.reshape(-1)[disp.order]
+    tok = disp.order // k
+    for r in range(disp.capacity):
+        at = np.flatnonzero(disp.local_pos == r)
+        pick.add(int(tok[at[r % at.size]]))
+    used = np.flatnonzero(disp.counts)
+    by_load = used[np.argsort(disp.counts[used], kind="stable")]
+    for e in list(by_load[:8]) + list(by_load[-8:]):
+        sel = tok[eid == e]
+        pick.update(int(t) for t in sel[:: max(1, sel.size // 4)][:4])
+    if near is not None:
+        pick.update(int(t) for t in np.flatnonzero(near))
+    rest = np.setdiff1d(np.arange(N), np.fromiter(pick, dtype=np.int64))
+    extra = max(0, n_target - len(pick))
+    if extra:
+        pick.update(int(t) for t in rng.choice(rest, size=min(extra, rest.size), replace=False))
+    return np.array(sorted(pick), dtype=np.int64)

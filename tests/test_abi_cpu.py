@@ -65,6 +65,30 @@ def test_argument_errors(mutate, status):
     assert M.load().latentmoe_last_error()
 
 
+def test_situ_bound_must_fit_fp16_with_bf16_storage():
+    """bf16 storage keeps the SiTU hidden (|h| < beta1 * beta2) in fp16."""
+    c = S.CONFIGS["b05_n4096"]
+    ok = M.dims_of(c)
+    ok.beta1, ok.beta2 = 4.0, 16000.0  # 64000 < 65504
+    assert M.workspace_bytes(ok, M.ENTRY_FORWARD) > 0
+    bad = M.dims_of(c)
+    bad.beta1, bad.beta2 = 4.0, 16400.0  # 65600
+    assert _call_forward(bad) == 2
+    assert b"65504" in M.load().latentmoe_last_error()
+    f32 = M.dims_of(S.CONFIGS["toy_n128"])
+    f32.beta1, f32.beta2 = 4.0, 1e6  # fp32 storage: no fp16 intermediates
+    assert M.workspace_bytes(f32, M.ENTRY_FORWARD) > 0
+
+
+def test_forward_check_argument_errors():
+    lib = M.load()
+    dims = M.dims_of(S.CONFIGS["toy_n128"])
+    assert lib.latentmoe_forward_check(ctypes.byref(dims), None, 0, None) == 4
+    assert lib.latentmoe_forward_check(ctypes.byref(dims), 16, 8, None) == 4
+    empty = M.dims_of(S.CONFIGS["toy_n128"], n_tokens=0)
+    assert lib.latentmoe_forward_check(ctypes.byref(empty), None, 0, None) == 0
+
+
 def test_workspace_and_null_errors():
     dims = M.dims_of(S.CONFIGS["toy_n128"])
     assert _call_forward(dims, ws_bytes=10) == 4
@@ -82,8 +106,9 @@ def test_workspace_and_null_errors():
 
 def test_status_strings():
     lib = M.load()
-    for s in range(6):
-        assert lib.latentmoe_status_string(s)
+    for s in range(7):
+        assert lib.latentmoe_status_string(s) != b"unknown status"
+    assert lib.latentmoe_status_string(99) == b"unknown status"
 
 
 def test_router_entry_errors():

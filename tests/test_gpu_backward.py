@@ -1,6 +1,8 @@
 """Parity of the routed-block backward (latentmoe_routed_backward, through
 the C ABI) with the oracle's ``routed_backward`` on seeded inputs: z and du
 from the generator, routes from the oracle router on the configured x."""
+import time
+
 import numpy as np
 import pytest
 import torch
@@ -155,19 +157,28 @@ def test_routed_backward_empty_batch_zeroes_weight_grads():
 
 
 def _full_size(name, tok_sample, n_experts_sample):
+    """The routed block at a full-K3 size: dz and dprobs on the tokens
+    `tok_sample` picks (a list, or a callable of the routes), the weight
+    gradients of sampled experts over all their pairs, exact zeros for an
+    expert without pairs.  The oracle reads the routed weights from the
+    device copy (checked against the host generator on three experts)."""
     cfg = S.CONFIGS[name] if isinstance(name, str) else name
     _say(f"[routed_backward full] {cfg.name}")
-    W = O.config_weights(cfg, cache_experts=2)
-    ids, probs = _routes(cfg, W)
+    R = cfg.n_routed
     dev = {n: S.gen.device_tensor(cfg, n) for n in ("w_g", "w_u", "w_o", "z", "du")}
+    G.check_device_copy(cfg, dev, [0, R // 2, R - 1])
+    W = G.oracle_weights(cfg, dev)
+    ids, probs = _routes(cfg, W)
     out = _run_gpu(cfg, ids, probs, dev=dev)
-    del dev
+    del dev["z"], dev["du"]
     tol = G.TOL[cfg.dtype]
     # dz / dprobs of sampled tokens: their own pairs only
     rows = np.asarray(tok_sample(ids) if callable(tok_sample) else tok_sample)
     z, du = _z_du(cfg, rows)
+    t0 = time.perf_counter()
     ref = O.routed_backward(z, ids[rows], probs[rows].astype(np.float64), W.experts, cfg.n_routed,
                             cfg.beta1, cfg.beta2, du, want=[])
+    _say(f"   {rows.size} tokens (oracle {time.perf_counter() - t0:.1f} s)")
     _check("dz (sampled tokens)", G.download_f64(out["dz"][torch.as_tensor(rows)]), ref.dz, tol)
     _check("dprobs (sampled tokens)", G.download_f64(out["dprobs"][torch.as_tensor(rows)]), ref.dp, tol)
     # weight gradients of sampled experts: all their pairs
@@ -186,16 +197,20 @@ def _full_size(name, tok_sample, n_experts_sample):
     if empty.size:
         for nm in ("dw_g", "dw_u", "dw_o"):
             assert torch.all(out[nm][int(empty[0])].float() == 0), nm
+    del dev, out
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.slow
 def test_routed_backward_k3_decode_sample():
-    _full_size("k3full_n64", [0, 21, 42, 63], 3)
+    """Few-token full-K3 shape: dz and dprobs on all 64 tokens."""
+    _full_size("k3full_n64", list(range(64)), 3)
 
 
 @pytest.mark.slow
 def test_routed_backward_k3_prefill_sample():
-    _full_size("k3full_n8192", [0, 4097, 8191], 2)
+    """Prefill full-K3 shape: dz and dprobs on 1024 stratified tokens."""
+    _full_size("k3full_n8192", lambda ids: G.stratified_tokens(ids, 896, 1024), 2)
 
 
 @pytest.mark.slow
@@ -203,15 +218,15 @@ def test_routed_backward_k3_past_2g_elements():
     """The largest size: the full-K3 routed block at N = 70000 tokens, where the
     per-pair buffers (h and the gate / up pre-activations, N k f_r = 2.29e9
     elements; the expert outputs, N k l = 4.01e9) pass 2^31.  Sampled: the last
-    token and tokens routed to the two last experts (their pairs sit at the
-    end of the sorted order), and the weight gradients of the first, a middle
-    and the last expert over all their pairs."""
+    token, tokens routed to the two last experts (their pairs sit at the end
+    of the sorted order) and 256 stratified tokens, and the weight gradients
+    of the first, a middle and the last expert over all their pairs."""
     cfg = S.CONFIGS["k3full_n8192"].with_(name="k3full_n70000", n_tokens=70000)
     N, R = cfg.n_tokens, cfg.n_routed
 
     def late_pairs(ids):
         late = np.flatnonzero((ids >= R - 2).any(axis=1))
-        return [int(late[0]), int(late[-1]), N - 1]
+        return np.union1d(G.stratified_tokens(ids, R, 256), [int(late[0]), int(late[-1]), N - 1])
 
     _full_size(cfg, late_pairs, 3)
     torch.cuda.empty_cache()
@@ -315,11 +330,11 @@ def test_layer_backward_k3_decode_full():
     _say(f"[layer_backward full] {cfg.name}")
     dev = G.device_layer_inputs(cfg)
     dev["dy"] = S.gen.device_tensor(cfg, "dy")
-    W = O.config_weights(cfg, cache_experts=2)
+    G.check_device_copy(cfg, dev, [0, cfg.n_routed - 1])
+    W = G.oracle_weights(cfg, dev)
     x = O.config_x(cfg)
     ids, probs = _layer_routes(cfg, W)
     dx, grads = _run_layer_gpu(cfg, ids, probs, dev)
-    del dev
     dy = S.to_f64(S.host_tensor(cfg, "dy"), cfg.dtype).reshape(cfg.n_tokens, cfg.d_model)
     counts = np.bincount(ids.reshape(-1), minlength=cfg.n_routed)
     used = np.nonzero(counts)[0]
@@ -337,22 +352,27 @@ def test_layer_backward_k3_decode_full():
 
 @pytest.mark.slow
 def test_layer_backward_k3_prefill_sample():
-    """Full-K3 prefill shape: dx of sampled tokens (tokens are independent
-    given the routes, so the oracle runs on those rows alone)."""
+    """Full-K3 prefill shape: dx of 1024 stratified tokens (tokens are
+    independent given the routes, so the oracle runs on those rows alone)."""
     cfg = S.CONFIGS["k3full_n8192"]
     _say(f"[layer_backward full] {cfg.name}")
     dev = G.device_layer_inputs(cfg)
     dev["dy"] = S.gen.device_tensor(cfg, "dy")
-    W = O.config_weights(cfg, cache_experts=2)
+    G.check_device_copy(cfg, dev, [0, cfg.n_routed - 1])
+    W = G.oracle_weights(cfg, dev)
     ids, probs = _layer_routes(cfg, W, O.config_x(cfg))
     dx, grads = _run_layer_gpu(cfg, ids, probs, dev)
-    del dev, grads
-    rows = np.array([0, 4097, 8191])
+    del grads
+    rows = G.stratified_tokens(ids, cfg.n_routed, 1024)
     x = O.config_x(cfg, rows=rows)
     d = cfg.d_model
     dy = np.stack([S.to_f64(S.host_tensor(cfg, "dy", int(r) * d, d), cfg.dtype) for r in rows])
+    t0 = time.perf_counter()
     ref = O.layer_backward(x, W, dy, ids=ids[rows], want=[])
+    _say(f"   {rows.size} tokens (oracle {time.perf_counter() - t0:.1f} s)")
     _check("dx (sampled tokens)", G.download_f64(dx[torch.as_tensor(rows)]), ref["x"], G.TOL[cfg.dtype])
+    del dev
+    torch.cuda.empty_cache()
 
 
 def test_layer_backward_is_deterministic():
