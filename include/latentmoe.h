@@ -213,10 +213,29 @@ lmoe_status latentmoe_forward(const lmoe_dims* dims, const lmoe_weights* weights
  * LMOE_ERR_RANGE if an fp16 intermediate of that forward left fp16's range
  * (its y is then unspecified), LMOE_OK otherwise.  For callers of the
  * asynchronous form (C_host NULL), e.g. after replaying a captured forward.
- * Errors: INVALID_ARGUMENT for bad dims, WORKSPACE for a missing or short
- * workspace. */
+ * workspace NULL (with dims that fit it): the current device's fixed scratch,
+ * i.e. the last latentmoe_forward_noalloc on this device.
+ * Errors: INVALID_ARGUMENT for bad dims, WORKSPACE for a short workspace. */
 lmoe_status latentmoe_forward_check(const lmoe_dims* dims, const void* workspace, size_t workspace_bytes,
                                     void* stream);
+
+/* latentmoe_forward for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments and results as latentmoe_forward with C_host
+ * NULL (asynchronous, launches only), minus the workspace: the intermediates
+ * live in a fixed scratch array of 64 MiB that the library holds on each
+ * device it runs on until the process ends (enough for the full-K3 layer
+ * up to ~170 tokens, the 0.5b layer up to 4096).  All steps run on `stream`
+ * (no second stream).  The call allocates nothing (no hipMalloc, no
+ * library allocation); its first call on a device looks up the array's
+ * address there.  Every call on one device shares that device's array:
+ * calls that overlap in time on one device (other streams, other threads)
+ * race and must be ordered by the caller.  The range flag is read with
+ * latentmoe_forward_check(dims, NULL, 0, stream).  Errors: as
+ * latentmoe_forward, and LMOE_ERR_WORKSPACE when the dims need more scratch
+ * than the array holds (nothing is enqueued). */
+lmoe_status latentmoe_forward_noalloc(const lmoe_dims* dims, const lmoe_weights* weights, const void* x,
+                                      void* y, int32_t* ids, float* probs, int32_t* counts, void* stream);
 
 /* Backward of the routed-expert block u = sum_j p_j E_{ids_j}(z) (chapter
  * step 3 and the sparse-execution section, differentiated; the pages train

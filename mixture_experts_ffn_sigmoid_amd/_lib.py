@@ -22,6 +22,7 @@ EXPORTS = (
     "latentmoe_route", "latentmoe_dispatch", "latentmoe_experts", "latentmoe_forward",
     "latentmoe_forward_timed", "latentmoe_route_softmax", "latentmoe_router_losses_workspace_bytes",
     "latentmoe_router_losses", "latentmoe_routed_backward", "latentmoe_backward", "latentmoe_forward_check",
+    "latentmoe_forward_noalloc",
 )
 GRAD_NAMES = ("w_down", "w_router", "w_g", "w_u", "w_o", "sh_g", "sh_u", "sh_o", "rms_w", "w_up")
 TIMING_EVENTS = 9
@@ -80,6 +81,7 @@ def load() -> ctypes.CDLL:
                                             ctypes.POINTER(vp), i32]
     lib.latentmoe_route_softmax.argtypes = [D, vp, vp, vp, vp, vp, vp, st, vp]
     lib.latentmoe_forward_check.argtypes = [D, vp, st, vp]
+    lib.latentmoe_forward_noalloc.argtypes = [D, ctypes.POINTER(Weights), vp, vp, vp, vp, vp, vp]
     lib.latentmoe_router_losses_workspace_bytes.argtypes = [D]
     lib.latentmoe_router_losses_workspace_bytes.restype = st
     lib.latentmoe_router_losses.argtypes = [D, vp, vp, vp, vp, st, vp]
@@ -88,7 +90,8 @@ def load() -> ctypes.CDLL:
                                        st, vp]
     for fn in ("latentmoe_route", "latentmoe_dispatch", "latentmoe_experts", "latentmoe_forward",
                "latentmoe_forward_timed", "latentmoe_route_softmax", "latentmoe_router_losses",
-               "latentmoe_routed_backward", "latentmoe_backward", "latentmoe_forward_check"):
+               "latentmoe_routed_backward", "latentmoe_backward", "latentmoe_forward_check",
+               "latentmoe_forward_noalloc"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -232,9 +235,18 @@ def latentmoe_forward_timed(dims, weights, x, y, ids, probs, counts, events, wor
                                          stream_handle(stream), handles, len(events)))
 
 
+def latentmoe_forward_noalloc(dims, weights, x, y, ids, probs, counts, stream=None):
+    """latentmoe_forward without a workspace (the library's fixed device
+    scratch; asynchronous, no capacity read-back)."""
+    W = weights if isinstance(weights, Weights) else weights_struct(weights)
+    check(load().latentmoe_forward_noalloc(ctypes.byref(dims), ctypes.byref(W), ptr(x), ptr(y), ptr(ids),
+                                           ptr(probs), ptr(counts), stream_handle(stream)))
+
+
 def latentmoe_forward_check(dims, workspace, stream=None):
     """Raises LatentMoEError (status RANGE) if the last forward enqueued with
-    this workspace left fp16's range in an intermediate."""
+    this workspace (None: the fixed scratch of latentmoe_forward_noalloc)
+    left fp16's range in an intermediate."""
     ws = workspace
     check(load().latentmoe_forward_check(ctypes.byref(dims), ptr(ws),
                                          0 if ws is None else ws.numel() * ws.element_size(),

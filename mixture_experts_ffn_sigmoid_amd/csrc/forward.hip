@@ -124,7 +124,7 @@ lmoe_status run_shared(const Plan& p, const lmoe_dims* dm, const lmoe_weights* W
 template <typename T, typename TI>
 lmoe_status run_forward(const Plan& p, const lmoe_dims* dm, const lmoe_weights* W, const void* x,
                         void* y, int32_t* ids, float* probs, int32_t* counts, const ForwardWs& w,
-                        hipStream_t st, hipEvent_t* ev) {
+                        hipStream_t st, hipEvent_t* ev, bool one_stream) {
   int step = 0;
   auto mark = [&]() -> lmoe_status {  // optional per-step timing events
     if (ev) LMOE_HIP(hipEventRecord(ev[step], st));
@@ -149,7 +149,7 @@ lmoe_status run_forward(const Plan& p, const lmoe_dims* dm, const lmoe_weights* 
       if (join) (void)hipEventDestroy(join);
     }
   } evs;
-  const bool overlap = ev == nullptr && p.ns > 0 && p.N <= kOverlapMaxTokens;
+  const bool overlap = ev == nullptr && !one_stream && p.ns > 0 && p.N <= kOverlapMaxTokens;
   if (overlap) {
     LMOE_TRY(side_stream(&side));
     LMOE_HIP(hipEventCreateWithFlags(&evs.fork, hipEventDisableTiming));
@@ -432,9 +432,37 @@ lmoe_status latentmoe_experts(const lmoe_dims* dims, const void* padded, int64_t
 }  // extern "C"
 
 namespace {
+// Fixed device scratch of latentmoe_forward_noalloc (for callers that cannot
+// allocate).  Each device holds its own copy for the life of the process; in
+// host code the array's name is only a stand-in, so its device address is
+// looked up once per device and used everywhere instead.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+
+// Device address of `scratch` on the current device.
+lmoe_status scratch_ptr(char** out) {
+  static std::mutex mu;
+  static char* ptrs[kMaxDevices] = {};
+  int dev = 0;
+  LMOE_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(LMOE_ERR_UNSUPPORTED, "device index %d", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(LMOE_ERR_HIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+    ptrs[dev] = (char*)ptr;
+  }
+  *out = ptrs[dev];
+  return LMOE_OK;
+}
+
 lmoe_status forward_impl(const lmoe_dims* dims, const lmoe_weights* weights, const void* x, void* y,
                          int32_t* ids, float* probs, int32_t* counts, int64_t* C_host,
-                         void* workspace, size_t workspace_bytes, void* stream, hipEvent_t* ev) {
+                         void* workspace, size_t workspace_bytes, void* stream, hipEvent_t* ev,
+                         bool one_stream = false) {
   Plan p;
   LMOE_TRY(check_dims(dims, &p));
   if (C_host) *C_host = 0;
@@ -455,8 +483,8 @@ lmoe_status forward_impl(const lmoe_dims* dims, const lmoe_weights* weights, con
     return fail(LMOE_ERR_WORKSPACE, "forward needs %zu workspace bytes", need);
   carve_forward(p, (char*)workspace, &w);
   hipStream_t st = launch_stream(stream);
-  if (p.bf16) LMOE_TRY((run_forward<bf16_t, f16_t>(p, dims, W, x, y, ids, probs, counts, w, st, ev)));
-  else LMOE_TRY((run_forward<float, float>(p, dims, W, x, y, ids, probs, counts, w, st, ev)));
+  if (p.bf16) LMOE_TRY((run_forward<bf16_t, f16_t>(p, dims, W, x, y, ids, probs, counts, w, st, ev, one_stream)));
+  else LMOE_TRY((run_forward<float, float>(p, dims, W, x, y, ids, probs, counts, w, st, ev, one_stream)));
   if (C_host) {
     int32_t meta[4] = {0, 0, 0, 0};
     LMOE_HIP(hipMemcpyAsync(meta, w.meta, sizeof(meta), hipMemcpyDeviceToHost, st));
@@ -493,6 +521,22 @@ lmoe_status latentmoe_forward_timed(const lmoe_dims* dims, const lmoe_weights* w
                       stream, (hipEvent_t*)events);
 }
 
+lmoe_status latentmoe_forward_noalloc(const lmoe_dims* dims, const lmoe_weights* weights, const void* x,
+                                      void* y, int32_t* ids, float* probs, int32_t* counts, void* stream) {
+  Plan p;
+  LMOE_TRY(check_dims(dims, &p));
+  if (p.N == 0) return LMOE_OK;
+  ForwardWs w{};
+  const size_t need = carve_forward(p, nullptr, &w);
+  if (need > kScratchBytes)
+    return fail(LMOE_ERR_WORKSPACE, "the forward needs %zu bytes of scratch; the fixed scratch holds %zu "
+                                    "(use latentmoe_forward with a workspace)", need, kScratchBytes);
+  char* ws = nullptr;
+  LMOE_TRY(scratch_ptr(&ws));
+  return forward_impl(dims, weights, x, y, ids, probs, counts, nullptr, ws, kScratchBytes, stream, nullptr,
+                      /*one_stream=*/true);
+}
+
 lmoe_status latentmoe_forward_check(const lmoe_dims* dims, const void* workspace, size_t workspace_bytes,
                                     void* stream) {
   Plan p;
@@ -500,6 +544,12 @@ lmoe_status latentmoe_forward_check(const lmoe_dims* dims, const void* workspace
   if (p.N == 0) return LMOE_OK;
   ForwardWs w{};
   const size_t need = carve_forward(p, nullptr, &w);
+  if (!workspace && need <= kScratchBytes) {  // the fixed scratch of latentmoe_forward_noalloc
+    char* ws = nullptr;
+    LMOE_TRY(scratch_ptr(&ws));
+    workspace = ws;
+    workspace_bytes = kScratchBytes;
+  }
   if (!workspace || workspace_bytes < need)
     return fail(LMOE_ERR_WORKSPACE, "forward needs %zu workspace bytes", need);
   carve_forward(p, (char*)workspace, &w);

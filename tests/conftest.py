@@ -14,5 +14,11 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # run GPU parity tests in a stable, cheap-first order
-    items.sort(key=lambda it: 1 if it.get_closest_marker("slow") else 0)
+    # run GPU parity tests in a stable, cheap-first order; the fixed-scratch
+    # forward's test file (test_zz_*) runs last of all
+    def rank(it):
+        if os.path.basename(str(it.fspath)).startswith("test_zz_"):
+            return 2
+        return 1 if it.get_closest_marker("slow") else 0
+
+    items.sort(key=rank)

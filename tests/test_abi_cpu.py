@@ -83,10 +83,28 @@ def test_situ_bound_must_fit_fp16_with_bf16_storage():
 def test_forward_check_argument_errors():
     lib = M.load()
     dims = M.dims_of(S.CONFIGS["toy_n128"])
-    assert lib.latentmoe_forward_check(ctypes.byref(dims), None, 0, None) == 4
     assert lib.latentmoe_forward_check(ctypes.byref(dims), 16, 8, None) == 4
+    big = M.dims_of(S.CONFIGS["k3full_n8192"])  # needs more than the fixed scratch: NULL is not it
+    assert lib.latentmoe_forward_check(ctypes.byref(big), None, 0, None) == 4
     empty = M.dims_of(S.CONFIGS["toy_n128"], n_tokens=0)
     assert lib.latentmoe_forward_check(ctypes.byref(empty), None, 0, None) == 0
+
+
+def test_forward_noalloc_rejects_dims_beyond_its_scratch():
+    """The fixed-scratch forward refuses, before touching a device, dims whose
+    forward needs more than its 64 MiB array."""
+    lib = M.load()
+    fake = 4096
+    W = M.Weights(*([fake] * 11))
+    big = M.dims_of(S.CONFIGS["k3full_n8192"])
+    assert M.workspace_bytes(big, M.ENTRY_FORWARD) > 64 << 20
+    assert lib.latentmoe_forward_noalloc(ctypes.byref(big), ctypes.byref(W), fake, fake, fake, fake, fake, None) == 4
+    assert b"fixed scratch" in lib.latentmoe_last_error()
+    bad = M.dims_of(S.CONFIGS["toy_n128"])
+    bad.top_k = 0
+    assert lib.latentmoe_forward_noalloc(ctypes.byref(bad), ctypes.byref(W), fake, fake, fake, fake, fake, None) == 1
+    empty = M.dims_of(S.CONFIGS["toy_n128"], n_tokens=0)
+    assert lib.latentmoe_forward_noalloc(ctypes.byref(empty), ctypes.byref(W), fake, fake, fake, fake, fake, None) == 0
 
 
 def test_workspace_and_null_errors():
