@@ -68,14 +68,15 @@ GemmArgs routed_grouped(const Plan& p, const lmoe_dims* dm, const RoutedBwdWs& w
 Tile routed_tile(const Plan& p) { return p.tile_m == 64 ? TILE_V : p.tile_m == 128 ? TILE_M : TILE_W; }
 
 // Forward part of the routed-block backward: the dispatch bookkeeping, the
-// pre-activations g = z W_g^T and up = z W_u^T (fp32), the hidden h (TI) and
-// the expert outputs o = h W_o^T (fp32), all in sorted pair order.  Returns
-// the capacity C (one host read-back).  T: storage type of the weights;
-// TI: intermediate type; TZ: type of z.
+// pre-activations g = z W_g^T and up = z W_u^T (fp32), the hidden h (TI) and,
+// with want_o, the expert outputs o = h W_o^T (fp32; the layer backward needs
+// them for u), all in sorted pair order.  Returns the capacity C (one host
+// read-back).  T: storage type of the weights; TI: intermediate type; TZ:
+// type of z.
 template <typename T, typename TI, typename TZ>
 lmoe_status routed_recompute(const Plan& p, const lmoe_dims* dm, const void* z, const int32_t* ids,
                              const void* w_g, const void* w_u, const void* w_o, const RoutedBwdWs& w,
-                             int* C_out, hipStream_t st) {
+                             int* C_out, hipStream_t st, bool want_o) {
   const int64_t P = p.pairs;
   const int f = p.fr, l = p.l, R = p.R;
   const int64_t es = sizeof(T), ei = sizeof(TI);
@@ -106,6 +107,7 @@ lmoe_status routed_recompute(const Plan& p, const lmoe_dims* dm, const void* z, 
       grouped(z, l * ez, w_u, l * es, (int64_t)f * l * es, f, l, w.up, (int64_t)f * 4), tile, st)));
   situ_hidden_kernel<TI><<<blocks(P * f), 256, 0, st>>>(w.g, w.up, P * f, dm->beta1, dm->beta2, (TI*)w.hs);
   LMOE_HIP(hipGetLastError());
+  if (!want_o) return LMOE_OK;
   // 3. expert outputs o = h W_o^T (fp32, sorted rows)
   return gemm<TI, T, float, A_SORTED, B_SINGLE, E_STORE>(
       grouped(w.hs, f * ei, w_o, f * es, (int64_t)l * f * es, l, f, w.o, (int64_t)l * 4), tile, st);
@@ -128,24 +130,29 @@ lmoe_status routed_gradients(const Plan& p, const lmoe_dims* dm, const void* z, 
                      int K, void* out, int64_t ldo) {
     return routed_grouped(p, dm, w, a, lda, bw, ldb, bstride, nrows, K, out, ldo);
   };
-  // 3b. dprobs and dout = p * du (sorted rows)
-  pair_grad_kernel<TI><<<(unsigned)P, 256, 0, st>>>(du, w.o, probs, w.order, p.k, l, dprobs, (TI*)w.dout);
-  LMOE_HIP(hipGetLastError());
-  // 4. dh = dout W_o, then the SiTU backward -> [dg | du].  16-bit weights are
-  // read as stored (K-major B: K-row k of W_o[e] is its latent row k); fp32
-  // ones through a transposed copy W_o^T [R, f, l]
+  // 3b-4. v = W_o^T du per pair (du's row times the pair's W_o; 16-bit
+  // weights read as stored, K-major: K-row k of W_o[e] is its latent row k;
+  // fp32 ones through a transposed copy W_o^T [R, f, l]).  Then
+  // dprobs = <du, W_o h> = <v, h>, the hidden's gradient dh = p v (applied
+  // by the SiTU backward) and dout = p du (for dW_o): the expert outputs
+  // themselves are not needed.
   if constexpr (sizeof(T) == 2) {
-    GemmArgs g = grouped(w.dout, l * ei, w_o, f * es, (int64_t)l * f * es, f, l, w.dh, (int64_t)f * 4);
+    convert_kernel<TI><<<blocks((int64_t)p.N * l), 256, 0, st>>>(du, (int64_t)p.N * l, (TI*)w.du16);
+    LMOE_HIP(hipGetLastError());
+    GemmArgs g = grouped(w.du16, l * ei, w_o, f * es, (int64_t)l * f * es, f, l, w.dh, (int64_t)f * 4);
     g.kmaj_split = l;
-    LMOE_TRY((gemm<TI, T, float, A_SORTED, B_KMAJOR, E_STORE>(g, tile, st)));
+    LMOE_TRY((gemm<TI, T, float, A_GATHER, B_KMAJOR, E_STORE>(g, tile, st)));
   } else {
     LMOE_TRY(transpose_batched<T>((const T*)w_o, (int64_t)l * f, f, l, f, (T*)w.w_oT, (int64_t)f * l, l, 0, R,
                                    w.counts, st));
-    LMOE_TRY((gemm<TI, T, float, A_SORTED, B_SINGLE, E_STORE>(
-        grouped(w.dout, l * ei, w.w_oT, l * es, (int64_t)f * l * es, f, l, w.dh, (int64_t)f * 4), tile, st)));
+    LMOE_TRY((gemm<float, T, float, A_GATHER, B_SINGLE, E_STORE>(
+        grouped(du, l * 4, w.w_oT, l * es, (int64_t)f * l * es, f, l, w.dh, (int64_t)f * 4), tile, st)));
   }
+  pair_vh_kernel<TI><<<(unsigned)P, 256, 0, st>>>(w.dh, (const TI*)w.hs, du, probs, w.order, p.k, l, f, dprobs,
+                                                  (TI*)w.dout, w.sp);
+  LMOE_HIP(hipGetLastError());
   situ_backward_kernel<TI><<<(unsigned)std::min<int64_t>(P, 65536), 256, 0, st>>>(
-      w.dh, w.g, w.up, P, f, dm->beta1, dm->beta2, (TI*)w.dgu, 2 * (int64_t)f, 0);
+      w.dh, w.g, w.up, P, f, dm->beta1, dm->beta2, (TI*)w.dgu, 2 * (int64_t)f, 0, w.sp);
   LMOE_HIP(hipGetLastError());
   // 5. dz rows = [dg | du] [W_g ; W_u] (K = 2f: W_g's rows, then W_u's), summed per token
   float* dzrows = w.o;  // o is consumed
@@ -231,7 +238,7 @@ lmoe_status run_routed_backward(const Plan& p, const lmoe_dims* dm, const void* 
                                 const float* du, void* dz, int64_t ld_dz, float* dprobs, void* dw_g,
                                 void* dw_u, void* dw_o, const RoutedBwdWs& w, hipStream_t st) {
   int C = 0;
-  LMOE_TRY((routed_recompute<T, TI, TZ>(p, dm, z, ids, w_g, w_u, w_o, w, &C, st)));
+  LMOE_TRY((routed_recompute<T, TI, TZ>(p, dm, z, ids, w_g, w_u, w_o, w, &C, st, /*want_o=*/false)));
   return routed_gradients<T, TI, TZ, TDZ>(p, dm, z, probs, w_g, w_u, w_o, du, dz, ld_dz, dprobs, dw_g, dw_u,
                                           dw_o, w, C, st);
 }
@@ -270,7 +277,7 @@ lmoe_status run_layer_backward(const Plan& p, const lmoe_dims* dm, const lmoe_we
   // outputs), kept for its gradients below
   const RoutedBwdWs& rw = w.rw;
   int C = 0;
-  LMOE_TRY((routed_recompute<T, TI, TI>(p, dm, w.z, ids, W->w_g, W->w_u, W->w_o, rw, &C, st)));
+  LMOE_TRY((routed_recompute<T, TI, TI>(p, dm, w.z, ids, W->w_g, W->w_u, W->w_o, rw, &C, st, /*want_o=*/true)));
   // u = sum over the token's pairs (slot order) of p o, then RMSNorm(u)
   pair_sum_kernel<float><<<(unsigned)N, 256, 0, st>>>(rw.o, rw.inv, p.k, l, probs, w.u, l);
   LMOE_HIP(hipGetLastError());
@@ -307,7 +314,7 @@ lmoe_status run_layer_backward(const Plan& p, const lmoe_dims* dm, const lmoe_we
                                                                   w.dhs, (int64_t)nsf * 4),
                                                             dense_tile(N, nsf, false), st)));
     situ_backward_kernel<TI><<<(unsigned)std::min<int64_t>(N, 65536), 256, 0, st>>>(
-        w.dhs, w.ag, w.au, N, nsf, dm->beta1, dm->beta2, (TI*)w.dcat, kcat, l + rpad);
+        w.dhs, w.ag, w.au, N, nsf, dm->beta1, dm->beta2, (TI*)w.dcat, kcat, l + rpad, nullptr);
     LMOE_HIP(hipGetLastError());
   }
   // ---- step 3 backward (routed block) -> dz into dcat[:, :l], dprobs

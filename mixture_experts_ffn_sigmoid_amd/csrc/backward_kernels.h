@@ -208,42 +208,43 @@ __global__ __launch_bounds__(256) void situ_hidden_kernel(const float* __restric
     Elem<TD>::store(h + i, situ_hidden(g[i], u[i], beta1, beta2, ib1, ib2));
 }
 
-// Pair gradients, one workgroup per sorted pair q' (pair q = order[q'],
-// token n = q / k):  dprobs[q] = <du[n], o[q']>,  dout[q'] = probs[q] * du[n].
+// Pair gradients from v = W_o^T du (the product of du's row with the pair's
+// W_o, one row per sorted pair q', q = order[q'], token n = q / k):
+//   dprobs[q] = <v[q'], h[q']>  (= <du[n], W_o h[q']>, the pair's output o
+//   never formed),  dout[q'] = probs[q] * du[n]  (for dW_o),  sp[q'] = probs[q].
+// The gradient of the hidden is dh = p v, applied by the SiTU backward.
 template <typename TD>
-__global__ __launch_bounds__(256) void pair_grad_kernel(const float* __restrict__ du, const float* __restrict__ o,
-                                                        const float* __restrict__ probs,
-                                                        const int32_t* __restrict__ order, int top_k, int ell,
-                                                        float* __restrict__ dprobs, TD* __restrict__ dout) {
+__global__ __launch_bounds__(256) void pair_vh_kernel(const float* __restrict__ v, const TD* __restrict__ h,
+                                                      const float* __restrict__ du, const float* __restrict__ probs,
+                                                      const int32_t* __restrict__ order, int top_k, int ell, int f,
+                                                      float* __restrict__ dprobs, TD* __restrict__ dout,
+                                                      float* __restrict__ sp) {
   const int64_t qs = blockIdx.x;
   const int32_t q = order[qs];
-  const float* dur = du + (int64_t)(q / top_k) * ell;
-  const float* orow = o + qs * ell;
-  TD* drow = dout + qs * ell;
   const float pq = probs[q];
+  const float* vrow = v + qs * f;
+  const TD* hrow = h + qs * f;
   float acc = 0.f;
-  if (((((uintptr_t)du) | ((uintptr_t)o)) & 15) == 0 && (ell & 3) == 0) {  // 16-byte rows (uniform)
-    for (int c = 4 * (int)threadIdx.x; c < ell; c += 4 * 256) {
-      const f32x4 v = *(const f32x4*)(dur + c), w = *(const f32x4*)(orow + c);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc += v[i] * w[i];
-        Elem<TD>::store(drow + c + i, pq * v[i]);
-      }
-    }
-  } else {
-    for (int c = threadIdx.x; c < ell; c += 256) {
-      const float v = dur[c];
-      acc += v * orow[c];
-      Elem<TD>::store(drow + c, pq * v);
-    }
-  }
+  for (int c = threadIdx.x; c < f; c += 256) acc += vrow[c] * Elem<TD>::load(hrow + c);
+  const float* dur = du + (int64_t)(q / top_k) * ell;
+  TD* drow = dout + qs * ell;
+  for (int c = threadIdx.x; c < ell; c += 256) Elem<TD>::store(drow + c, pq * dur[c]);
   __shared__ float red[4];
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
   __syncthreads();
-  if (threadIdx.x == 0) dprobs[q] = (red[0] + red[1]) + (red[2] + red[3]);
+  if (threadIdx.x == 0) {
+    dprobs[q] = (red[0] + red[1]) + (red[2] + red[3]);
+    sp[qs] = pq;
+  }
+}
+
+// Elementwise fp32 -> TD (n values).
+template <typename TD>
+__global__ __launch_bounds__(256) void convert_kernel(const float* __restrict__ in, int64_t n, TD* __restrict__ out) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    Elem<TD>::store(out + i, in[i]);
 }
 
 // SiTU-GLU backward through the hidden: with G(a) = b1 tanh(a/b1) sigmoid(a)
@@ -252,22 +253,25 @@ __global__ __launch_bounds__(256) void pair_grad_kernel(const float* __restrict_
 //   G'(a) = (1 - tanh(a/b1)^2) sigmoid(a) + b1 tanh(a/b1) sigmoid(a) (1 - sigmoid(a)),
 //   U'(a) = 1 - tanh(a/b2)^2.
 // Row q of dgu (leading dimension ld, starting at column col0) holds
-// [dg | du] (f columns each) for row q of the rows x f pre-activations.
+// [dg | du] (f columns each) for row q of the rows x f pre-activations; with
+// row_scale, row q's dh is multiplied by row_scale[q] first.
 // Workgroups stride over rows and threads over columns (no index division);
 // tanh and sigma from the hardware exp and reciprocal (absolute error ~1e-7).
 template <typename TD>
 __global__ __launch_bounds__(256) void situ_backward_kernel(const float* __restrict__ dh, const float* __restrict__ g,
                                                             const float* __restrict__ u, int64_t rows, int f,
                                                             float beta1, float beta2, TD* __restrict__ dgu,
-                                                            int64_t ld, int64_t col0) {
+                                                            int64_t ld, int64_t col0,
+                                                            const float* __restrict__ row_scale) {
   const float ib1 = 1.0f / beta1, ib2 = 1.0f / beta2;
   for (int64_t q = blockIdx.x; q < rows; q += gridDim.x) {
     const float* gq = g + q * f;
     const float* uq = u + q * f;
     const float* dq = dh + q * f;
+    const float rs = row_scale ? row_scale[q] : 1.0f;
     TD* out = dgu + q * ld + col0;
     for (int j = threadIdx.x; j < f; j += 256) {
-      const float a = gq[j], b = uq[j], d = dq[j];
+      const float a = gq[j], b = uq[j], d = dq[j] * rs;
       const float tg = tanh_fast(a * ib1), tu = tanh_fast(b * ib2);
       const float sg = rcp_fast(1.0f + __expf(-a));
       const float gate = beta1 * tg * sg, up = beta2 * tu;

@@ -216,7 +216,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
       e_batch = L / per;
       L -= e_batch * per;
     }
-    constexpr int GM = 8;  // raster: groups of 8 M tiles sweep all N tiles
+    constexpr int GM = 4;  // raster: groups of 4 M tiles sweep all N tiles (4 and 8 measure alike; 16, 32 slower)
     const int group = L / (GM * args.n_tiles);
     const int first_m = group * GM;
     const int gsize = min(args.m_tiles - first_m, GM);

@@ -247,7 +247,9 @@ size_t carve_forward(const Plan& p, char* b, ForwardWs* w) {
 // of kr_len).
 struct RoutedBwdWs {
   int32_t *counts, *offsets, *order, *chunk_hist, *chunk_bad, *meta, *tile_list, *inv, *kr_off, *kr_len;
-  float *g, *up, *o, *dh;  // o also holds the dz rows once it is consumed
+  float *g, *up, *o, *dh;  // o also holds the dz rows once it is consumed; dh holds v = W_o^T du per pair
+  float* sp;               // probs of the sorted pairs
+  char* du16;              // du in the intermediate type (16-bit operands of v)
   char *hs, *dout, *dgu;   // intermediate type
   char *w_oT, *w_guT;      // storage type
   char *doutT, *hT, *dgT, *duT, *zT;
@@ -271,6 +273,8 @@ size_t carve_routed_backward(const Plan& p, char* b, RoutedBwdWs* w) {
   w->up = c.take<float>((size_t)P * p.fr * 4);
   w->o = c.take<float>((size_t)P * p.l * 4);
   w->dh = c.take<float>((size_t)P * p.fr * 4);
+  w->sp = c.take<float>((size_t)P * 4);
+  w->du16 = c.take<char>(ei == 2 ? (size_t)p.N * p.l * ei : 0);
   w->hs = c.take<char>((size_t)P * p.fr * ei);
   w->dout = c.take<char>((size_t)P * p.l * ei);
   w->dgu = c.take<char>((size_t)P * 2 * p.fr * ei);
