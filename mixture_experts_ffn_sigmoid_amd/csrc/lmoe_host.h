@@ -486,8 +486,8 @@ lmoe_status run_dispatch(const Plan& p, const int32_t* ids, int32_t* chunk_hist,
   LMOE_HIP(hipGetLastError());
   dispatch_scan_kernel<<<1, 1024, 0, st>>>(chunk_hist, p.nchunks, p.R, counts, offsets, chunk_bad, meta);
   LMOE_HIP(hipGetLastError());
-  dispatch_scatter_kernel<<<p.nchunks, 64, p.R * sizeof(int32_t), st>>>(ids, p.pairs, p.R,
-                                                                              chunk_hist, order);
+  dispatch_scatter_kernel<<<p.nchunks, kDispatchChunk, p.R * sizeof(int32_t), st>>>(ids, p.pairs, p.R,
+                                                                                          chunk_hist, order);
   LMOE_HIP(hipGetLastError());
   return LMOE_OK;
 }

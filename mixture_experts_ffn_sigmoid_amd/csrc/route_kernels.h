@@ -194,7 +194,10 @@ __global__ __launch_bounds__(256) void dispatch_hist_kernel(const int32_t* __res
 // Dispatch step 2 (one workgroup of 1024 threads): per expert, a running sum
 // over chunks turns chunk_hist into each chunk's first sorted position;
 // counts, offsets (exclusive scan over experts), meta[0] = C = max counts and
-// meta[2] = number of ids outside [0, R).
+// meta[2] = number of ids outside [0, R).  Each thread walks its experts'
+// chunk counts kScanBatch at a time (the loads of a batch are independent, so
+// their latencies overlap instead of adding up chunk by chunk).
+constexpr int kScanBatch = 16;
 __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t* __restrict__ chunk_hist,
                                                              int nchunks, int R,
                                                              int32_t* __restrict__ counts,
@@ -203,21 +206,25 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t* __restrict
                                                              int32_t* __restrict__ meta) {
   __shared__ int32_t part[1024];
   __shared__ int32_t cmax[1024];
+  __shared__ int32_t bad_part[1024];
   const int t = threadIdx.x;
-  if (t == 0) {
-    int bad = 0;
-    for (int c = 0; c < nchunks; ++c) bad += chunk_bad[c];
-    meta[2] = bad;
-  }
+  int bad = 0;
+  for (int c = t; c < nchunks; c += 1024) bad += chunk_bad[c];
+  bad_part[t] = bad;
   const int ept = (R + 1023) / 1024;  // experts per thread, contiguous
   const int e0 = min(t * ept, R), e1 = min(e0 + ept, R);
   int my_total = 0, my_max = 0;
   for (int e = e0; e < e1; ++e) {
     int run = 0;
-    for (int c = 0; c < nchunks; ++c) {
-      const int h = chunk_hist[(int64_t)c * R + e];
-      chunk_hist[(int64_t)c * R + e] = run;
-      run += h;
+    for (int c0 = 0; c0 < nchunks; c0 += kScanBatch) {
+      int h[kScanBatch];
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i) h[i] = c0 + i < nchunks ? chunk_hist[(int64_t)(c0 + i) * R + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i) {
+        if (c0 + i < nchunks) chunk_hist[(int64_t)(c0 + i) * R + e] = run;
+        run += h[i];
+      }
     }
     counts[e] = run;
     my_total += run;
@@ -226,21 +233,33 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t* __restrict
   part[t] = my_total;
   cmax[t] = my_max;
   __syncthreads();
-  for (int s = 1; s < 1024; s <<= 1) {  // inclusive scan (sum) and suffix max
+  for (int s = 1; s < 1024; s <<= 1) {  // inclusive scan (sum), suffix max, total of bad ids
     const int a = t >= s ? part[t - s] : 0;
     const int m = t + s < 1024 ? cmax[t + s] : 0;
+    const int b = t + s < 1024 ? bad_part[t + s] : 0;
     __syncthreads();
     part[t] += a;
     cmax[t] = max(cmax[t], m);
+    bad_part[t] += b;
     __syncthreads();
   }
   int base = part[t] - my_total;
   for (int e = e0; e < e1; ++e) {
     offsets[e] = base;
-    for (int c = 0; c < nchunks; ++c) chunk_hist[(int64_t)c * R + e] += base;
+    for (int c0 = 0; c0 < nchunks; c0 += kScanBatch) {
+      int h[kScanBatch];
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i) h[i] = c0 + i < nchunks ? chunk_hist[(int64_t)(c0 + i) * R + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kScanBatch; ++i)
+        if (c0 + i < nchunks) chunk_hist[(int64_t)(c0 + i) * R + e] = h[i] + base;
+    }
     base += counts[e];
   }
-  if (t == 0) meta[0] = cmax[0];
+  if (t == 0) {
+    meta[0] = cmax[0];
+    meta[2] = bad_part[0];
+  }
 }
 
 // Grouped-GEMM work list (one workgroup of 1024 threads): every expert with
@@ -274,48 +293,47 @@ __global__ __launch_bounds__(1024) void tile_list_kernel(const int32_t* __restri
   if (t == 1023) meta[1] = part[1023];
 }
 
-// Dispatch step 3: stable scatter.  One wave per chunk walks its pairs in
-// order, 64 at a time (all of the chunk's ids are fetched up front);
-// a pair's rank among equal experts of its batch is the number of lower lanes
-// with the same expert (lane values read across the wave with readlane, no
-// LDS round trip), and a per-expert cursor in LDS (seeded with the chunk's
-// first positions) carries the order across batches.
-__global__ __launch_bounds__(64) void dispatch_scatter_kernel(const int32_t* __restrict__ ids,
-                                                              int64_t pairs, int R,
-                                                              const int32_t* __restrict__ chunk_base,
-                                                              int32_t* __restrict__ order) {
+// Dispatch step 3: stable scatter.  One workgroup of kDispatchChunk / 64
+// waves per chunk, wave w owning the chunk's pairs 64 w .. 64 w + 63 (one per
+// lane).  Each wave first ranks its pairs among the wave's pairs of the same
+// expert (lanes grouped by expert with ballots, one round per distinct
+// expert in the wave); then the waves, in order, add their ranks to
+// per-expert cursors in LDS (seeded with the chunk's first positions), so
+// pairs of one expert land in ascending pair order.
+constexpr int kScatterWaves = kDispatchChunk / 64;
+__global__ __launch_bounds__(kDispatchChunk) void dispatch_scatter_kernel(const int32_t* __restrict__ ids,
+                                                                          int64_t pairs, int R,
+                                                                          const int32_t* __restrict__ chunk_base,
+                                                                          int32_t* __restrict__ order) {
   extern __shared__ int32_t cursor[];  // [R]
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int32_t* base = chunk_base + (int64_t)blockIdx.x * R;
-#pragma unroll 16
-  for (int e = lane; e < R; e += 64) cursor[e] = base[e];  // loads issued together, not one latency each
-  __syncthreads();
-  const int64_t q0 = (int64_t)blockIdx.x * kDispatchChunk;
-  const int64_t q1 = min(q0 + kDispatchChunk, pairs);
-  auto expert_of = [&](int64_t q) -> int {  // -1: past the chunk, or an id outside [0, R) (not counted)
-    if (q >= q1) return -1;
-    const int e = ids[q];
-    return (e >= 0 && e < R) ? e : -1;
-  };
-  constexpr int kBatches = kDispatchChunk / 64;
-  int eb[kBatches];  // the chunk's ids, fetched together
-#pragma unroll
-  for (int b = 0; b < kBatches; ++b) eb[b] = expert_of(q0 + b * 64 + lane);
-#pragma unroll
-  for (int b = 0; b < kBatches; ++b) {
-    const int64_t q = q0 + b * 64 + lane;
-    const int e = eb[b];
-    int before = 0, after = 0;
-#pragma unroll 2  // a rolled loop: unrolled, its readlane results exhaust the scalar registers
-    for (int j = 0; j < 64; ++j) {
-      const int ej = __builtin_amdgcn_readlane(e, j);
-      before += (j < lane && ej == e) ? 1 : 0;
-      after += (j > lane && ej == e) ? 1 : 0;
+  for (int e = tid; e < R; e += kDispatchChunk) cursor[e] = base[e];
+  const int64_t q = (int64_t)blockIdx.x * kDispatchChunk + tid;
+  int e = -1;  // past the end, or an id outside [0, R): not placed (not counted by the histogram)
+  if (q < pairs) {
+    const int v = ids[q];
+    e = (v >= 0 && v < R) ? v : -1;
+  }
+  int before = 0;     // lanes below with the same expert
+  bool last = true;   // no lane above with the same expert
+  uint64_t todo = __ballot(e >= 0);  // wave-uniform
+  while (todo) {
+    const int lead = __ffsll((unsigned long long)todo) - 1;
+    const int el = __builtin_amdgcn_readlane(e, lead);
+    const uint64_t m = __ballot(e == el);
+    if (e == el) {
+      before = __popcll(m & ((1ull << lane) - 1));
+      last = (m >> lane) == 1ull;
     }
-    if (e >= 0) {
+    todo &= ~m;
+  }
+  __syncthreads();  // cursors seeded
+  for (int w = 0; w < kScatterWaves; ++w) {
+    if (wave == w && e >= 0) {
       const int pos = cursor[e] + before;
       order[pos] = (int32_t)q;
-      if (after == 0) cursor[e] = pos + 1;  // the batch's last pair of expert e
+      if (last) cursor[e] = pos + 1;  // the wave's last pair of expert e
     }
     __syncthreads();
   }
