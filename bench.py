@@ -83,11 +83,14 @@ def host_cpu() -> dict:
     return {"affinity_cores": len(os.sched_getaffinity(0)), "cpu_model": model}
 
 
-def cpu_baseline(cfg, n_sample: int, threads: int | None = None):
+def cpu_baseline(cfg, n_sample: int, threads: int | None = None, device_experts: bool = False):
     """The oracle (test infrastructure, untuned) on the first n_sample tokens of
     the workload, on this host's cores (BLAS threads = `threads`, default all
-    cores of the affinity mask).  Weights the sample needs are generated
-    beforehand (untimed); the timed region is the oracle forward."""
+    cores of the affinity mask).  The routed experts the sample needs are
+    generated beforehand on the host, or, with device_experts, copied as the
+    oracle asks for them from the device copy of the seeded weights (cast to
+    fp64 on the device, which is exact); the copy time is measured and left
+    out.  The timed region is the oracle forward."""
     import numpy as np
     from threadpoolctl import threadpool_info, threadpool_limits
 
@@ -101,23 +104,37 @@ def cpu_baseline(cfg, n_sample: int, threads: int | None = None):
     routes = O.route(x, W.w_router, W.bias, cfg.top_k)
     need = sorted(set(routes.ids.reshape(-1).tolist()))
     per = cfg.ff_routed * cfg.d_latent
-    fr, l = cfg.ff_routed, cfg.d_latent
-    stored = {e: tuple(S.to_f64(S.host_tensor(cfg, n, e * per, per), cfg.dtype) for n in ("w_g", "w_u", "w_o"))
-              for e in need}
+    fr, l, R = cfg.ff_routed, cfg.d_latent, cfg.n_routed
+    fetch_s = [0.0]
+    if device_experts:
+        import torch
 
-    def experts(e):  # the oracle reads stored (bf16 / fp32) weights as exact fp64
-        g, u, o = stored[e]
-        return g.reshape(fr, l), u.reshape(fr, l), o.reshape(l, fr)
+        dev = {n: S.gen.device_tensor(cfg, n) for n in ("w_g", "w_u", "w_o")}
+        shapes = {"w_g": (R, fr, l), "w_u": (R, fr, l), "w_o": (R, l, fr)}
+
+        def experts(e):
+            t0 = time.perf_counter()
+            out = tuple(dev[n].reshape(shapes[n])[e].double().cpu().numpy() for n in ("w_g", "w_u", "w_o"))
+            fetch_s[0] += time.perf_counter() - t0
+            return out
+    else:
+        stored = {e: tuple(S.to_f64(S.host_tensor(cfg, n, e * per, per), cfg.dtype) for n in ("w_g", "w_u", "w_o"))
+                  for e in need}
+
+        def experts(e):  # the oracle reads stored (bf16 / fp32) weights as exact fp64
+            g, u, o = stored[e]
+            return g.reshape(fr, l), u.reshape(fr, l), o.reshape(l, fr)
 
     W.experts = experts
     with threadpool_limits(limits=threads, user_api="blas"):
         used = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] + [1])
         t0 = time.perf_counter()
         O.forward(x, W)
-        dt = time.perf_counter() - t0
+        dt = time.perf_counter() - t0 - fetch_s[0]
+    src = "device copy of the seeded weights, copy time excluded" if device_experts else "host-generated"
     return {"value": round(n_sample / dt, 3), "unit": "tokens/s", "cores": used, "kind": "oracle",
             "sample": f"first {n_sample} of {cfg.n_tokens} tokens of {cfg.name} (all five steps, fp64 numpy, "
-                      f"{len(need)} routed experts touched, BLAS threads {used}); {dt:.2f} s",
+                      f"{len(need)} routed experts touched ({src}), BLAS threads {used}); {dt:.2f} s",
             "seconds": round(dt, 3), "gflops": round(cfg.flops() * n_sample / cfg.n_tokens / dt / 1e9, 2), **cpu}
 
 
@@ -413,7 +430,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="k3full_n8192", choices=sorted(S.CONFIGS))
-    ap.add_argument("--cpu-sample", type=int, default=24, help="tokens for the CPU oracle baseline (0: skip)")
+    ap.add_argument("--cpu-sample", type=int, default=2048, help="tokens for the CPU oracle baseline (0: skip)")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward legs (routed block and whole layer)")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the few-token (64-token, full-K3) forward measured after the prefill workload")
@@ -471,9 +488,11 @@ def main():
         out["routed_backward"] = backward_leg(cfg, bufs["ids"], bufs["probs"], max(2, args.steps // 4), 1)
         out["layer_backward"] = layer_backward_leg(cfg, bufs["ids"], bufs["probs"], max(2, args.steps // 4), 1)
     if args.cpu_sample > 0:
-        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_sample)
-    if cfg.name == "k3full_n8192" and not args.no_secondary:
         del bufs, fm
+        torch.cuda.empty_cache()
+        out["cpu_baseline"] = cpu_baseline(cfg, args.cpu_sample, device_experts=cfg.d_latent * cfg.ff_routed > 10**6)
+    if cfg.name == "k3full_n8192" and not args.no_secondary:
+        fm = bufs = None
         torch.cuda.empty_cache()
         out["secondary"] = secondary_decode(args.steps, args.warmup)
     if cfg.name == "k3full_n8192" and not args.no_small:
