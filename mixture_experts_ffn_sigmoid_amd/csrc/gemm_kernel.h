@@ -189,7 +189,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
                 "K-major B: 16-bit operands, whole K rows per DMA instruction");
   static_assert(A_INST % NW == 0 && B_INST % NW == 0 && BM % RPI == 0 && BN % RPI == 0, "DMA split");
   static_assert(SA >= 2 && SB >= SA && UNROLL <= 8, "ring shape");
-  __shared__ __attribute__((aligned(1024))) char smem[RING];
+  // One LDS object for everything (the operand rings and, for E_SLOTS, the
+  // slot rows and weights after them): with a second __shared__ object the
+  // compiler can no longer tell which object an LDS-DMA writes, and it waits
+  // for every DMA in flight (vmcnt 0) before each fragment read.
+  constexpr int kSlotBytes = EMODE == E_SLOTS ? BM * 8 : 0;
+  __shared__ __attribute__((aligned(1024))) char smem[RING + kSlotBytes];
   char* const ringA = smem;
   char* const ringB = smem + SA * kStageA;
 
@@ -248,8 +253,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
   // latency hides behind the main loop) into LDS outside the operand ring;
   // the main loop's barriers publish them to every wave.  With cap > 0 the
   // pairs at positions >= cap of their expert are dropped: weight 0.
-  __shared__ int slot_row[EMODE == E_SLOTS ? BM : 1];
-  __shared__ float slot_p[EMODE == E_SLOTS ? BM : 1];
+  int* const slot_row = (int*)(smem + RING);              // E_SLOTS: [BM]
+  float* const slot_p = (float*)(smem + RING + BM * 4);  // E_SLOTS: [BM]
   if constexpr (EMODE == E_SLOTS) {
     for (int r = tid; r < BM; r += 64 * NW) {
       const int q = r < rows_valid ? args.order[off + m0 + r] : 0;
