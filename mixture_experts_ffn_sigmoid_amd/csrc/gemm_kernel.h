@@ -488,18 +488,54 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
       const int ch = kHalf ? (2 * c + lh) : (NC * lh + c);
 #pragma unroll
       for (int i = 0; i < NA; ++i) fa[c][i] = *(const u32x4*)(As + swz(wm * WTM + i * 32 + lr, ch));
+      if constexpr (BMODE != B_KMAJOR) {  // (K-major B: read_b_kmaj)
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        if constexpr (BMODE == B_KMAJOR) {
-          typedef __attribute__((address_space(3))) i16x4* lds_i16x4_t;
-          const char* q = Bs + kmaj_frag[j] + c * 16 * ROWK;
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t)q);
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t)(q + 4 * ROWK));
-          const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-          fb[c][j] = u32x4{l2[0], l2[1], h2[0], h2[1]};
+        for (int j = 0; j < TN; ++j) fb[c][j] = *(const u32x4*)(Bs + swz(b_tile_row(j) + lr, ch));
+      }
+    };
+    // B_KMAJOR: the B fragments of chunks C0 .. C0+CN-1 through gfx950's
+    // transposing LDS read (ds_read_b64_tr_b16), issued together and waited
+    // for in the same asm block.  The builtin for this read carries no alias
+    // information, and the compiler then waits for every LDS-DMA in flight
+    // (vmcnt 0) before each such read; here the wave waits only for its own
+    // LDS reads.
+    auto read_b_kmaj = [&](const char* Bs, auto c0_c, auto cn_c) {
+      constexpr int C0 = decltype(c0_c)::value, CN = decltype(cn_c)::value;
+      if constexpr (BMODE == B_KMAJOR && CN > 0) {
+        static_assert(TN == 2 && CN <= 2, "K-major B: two 32-column sub-tiles per wave, one or two chunks");
+        typedef __attribute__((address_space(3))) const char* lds_cptr;
+        const uint32_t a0 = (uint32_t)(size_t)(lds_cptr)(Bs + kmaj_frag[0]);
+        const uint32_t a1 = (uint32_t)(size_t)(lds_cptr)(Bs + kmaj_frag[1]);
+        u32x2 r[CN][TN][2];  // [chunk][sub-tile][K-rows 0-3 | 8-11 of the 16-row group]
+        if constexpr (CN == 1) {
+          asm volatile(
+              "ds_read_b64_tr_b16 %0, %4 offset:%6\n\t"
+              "ds_read_b64_tr_b16 %1, %4 offset:%7\n\t"
+              "ds_read_b64_tr_b16 %2, %5 offset:%6\n\t"
+              "ds_read_b64_tr_b16 %3, %5 offset:%7\n\t"
+              "s_waitcnt lgkmcnt(0)"
+              : "=&v"(r[0][0][0]), "=&v"(r[0][0][1]), "=&v"(r[0][1][0]), "=&v"(r[0][1][1])
+              : "v"(a0), "v"(a1), "i"(C0 * 16 * ROWK), "i"(C0 * 16 * ROWK + 4 * ROWK));
         } else {
-          fb[c][j] = *(const u32x4*)(Bs + swz(b_tile_row(j) + lr, ch));
+          asm volatile(
+              "ds_read_b64_tr_b16 %0, %8 offset:%10\n\t"
+              "ds_read_b64_tr_b16 %1, %8 offset:%11\n\t"
+              "ds_read_b64_tr_b16 %2, %9 offset:%10\n\t"
+              "ds_read_b64_tr_b16 %3, %9 offset:%11\n\t"
+              "ds_read_b64_tr_b16 %4, %8 offset:%12\n\t"
+              "ds_read_b64_tr_b16 %5, %8 offset:%13\n\t"
+              "ds_read_b64_tr_b16 %6, %9 offset:%12\n\t"
+              "ds_read_b64_tr_b16 %7, %9 offset:%13\n\t"
+              "s_waitcnt lgkmcnt(0)"
+              : "=&v"(r[0][0][0]), "=&v"(r[0][0][1]), "=&v"(r[0][1][0]), "=&v"(r[0][1][1]),
+                "=&v"(r[1][0][0]), "=&v"(r[1][0][1]), "=&v"(r[1][1][0]), "=&v"(r[1][1][1])
+              : "v"(a0), "v"(a1), "i"(C0 * 16 * ROWK), "i"(C0 * 16 * ROWK + 4 * ROWK),
+                "i"((C0 + 1) * 16 * ROWK), "i"((C0 + 1) * 16 * ROWK + 4 * ROWK));
         }
+#pragma unroll
+        for (int c = 0; c < CN; ++c)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) fb[C0 + c][j] = u32x4{r[c][j][0][0], r[c][j][0][1], r[c][j][1][0], r[c][j][1][1]};
       }
     };
     auto mfma_chunk = [&](auto c_c) {
@@ -530,11 +566,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
       }
     };
     constexpr int MPC = NA * TN * (kHalf ? 1 : 4);  // MFMAs per chunk
-    constexpr int RPC = NA + TN * (BMODE == B_KMAJOR ? 2 : 1);  // fragment reads per chunk
+    constexpr int RPC = NA + (BMODE == B_KMAJOR ? 0 : TN);  // compiler-visible fragment reads per chunk
     // tile 0 landed and visible; its first chunks into registers
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(kNewer0));
     barrier();
     sfor<H>([&](auto c_c) { read_chunk(ringA, ringB, c_c); });
+    read_b_kmaj(ringB, IntC<0>{}, IntC<H>{});
 
     auto one = [&](int kt, auto u_c) {
       constexpr int u = decltype(u_c)::value;  // kt % UNROLL: stages are static
@@ -542,6 +579,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
       const char* Bs = ringB + (u % SB) * kStageB;
       // phase 1
       sfor<NC - H>([&](auto c_c) { read_chunk(As, Bs, IntC<H + decltype(c_c)::value>{}); });
+      read_b_kmaj(Bs, IntC<H>{}, IntC<NC - H>{});
       sfor<H>([&](auto c_c) { mfma_chunk(c_c); });
       // one MFMA (its operands were read in the previous phase), then the
       // reads, which must be complete at the barrier, then the other MFMAs;
@@ -557,6 +595,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
       sfor<H>([&](auto c_c) {
         read_chunk(ringA + ((u + 1) % SA) * kStageA, ringB + ((u + 1) % SB) * kStageB, c_c);
       });
+      read_b_kmaj(ringB + ((u + 1) % SB) * kStageB, IntC<0>{}, IntC<H>{});
       dma_step(clampt(kt + SA), ringA + (u % SA) * kStageA, clampt(kt + SB), ringB + (u % SB) * kStageB);
       sfor<NC - H>([&](auto c_c) { mfma_chunk(IntC<H + decltype(c_c)::value>{}); });
       // the next tile's reads first (phase 1 of the next step needs them at once),
