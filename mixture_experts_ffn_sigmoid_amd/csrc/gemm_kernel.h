@@ -189,6 +189,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
                 "K-major B: 16-bit operands, whole K rows per DMA instruction");
   static_assert(A_INST % NW == 0 && B_INST % NW == 0 && BM % RPI == 0 && BN % RPI == 0, "DMA split");
   static_assert(SA >= 2 && SB >= SA && UNROLL <= 8, "ring shape");
+  // Dense 16-bit products on two-stage rings take the one-barrier schedule
+  // (main loop below); the others the two-phase one.
+  constexpr bool k1Bar = SA == 2 && SB == 2 && !GROUPED && kHalf && BMODE != B_KMAJOR;
   // One LDS object for everything (the operand rings and, for E_SLOTS, the
   // slot rows and weights after them): with a second __shared__ object the
   // compiler can no longer tell which object an LDS-DMA writes, and it waits
@@ -454,6 +457,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
   // prologue: the DMA of virtual steps -SB..-1 (A tiles 0..SA-1, B tiles 0..SB-1);
   // an empty K range (KT == 0, uniform over the workgroup) has no DMA and no
   // main loop: its tile is stored as zeros
+  if constexpr (k1Bar) {
+    if (KT > 0) dma_step(0, ringA, 0, ringB);  // step 0 only; step kt + 1 loads during step kt
+  } else
 #pragma unroll
   for (int s = -SB; s < 0 && KT > 0; ++s) {
     const int ta = s + SA, tb = s + SB;
@@ -567,6 +573,51 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
     };
     constexpr int MPC = NA * TN * (kHalf ? 1 : 4);  // MFMAs per chunk
     constexpr int RPC = NA + (BMODE == B_KMAJOR ? 0 : TN);  // compiler-visible fragment reads per chunk
+    if constexpr (k1Bar) {
+      // One barrier per K step.  Step kt's tiles sit in stage kt % 2, and
+      // during the step the DMA fills the other stage with step kt + 1 (a
+      // whole step to land, where the two-phase schedule gives a two-stage
+      // ring half a step).  The MFMAs of a step's last chunk run after the
+      // barrier, while the next step's first fragments are read, so the
+      // matrix cores have work across it.  Results are bit-identical to the
+      // two-phase schedule (same MFMAs in the same order per accumulator).
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      barrier();
+      auto step1 = [&](int kt, auto u_c, auto first_c) {
+        constexpr int u = decltype(u_c)::value;
+        constexpr bool first = decltype(first_c)::value;
+        const char* As = ringA + u * kStageA;
+        const char* Bs = ringB + u * kStageB;
+        read_chunk(As, Bs, IntC<0>{});
+        if constexpr (!first) mfma_chunk(IntC<NC - 1>{});  // the previous step's last chunk
+        // the stage of step kt - 1 is free: every wave passed the barrier after reading it
+        dma_step(clampt(kt + 1), ringA + (1 - u) * kStageA, clampt(kt + 1), ringB + (1 - u) * kStageB);
+        if constexpr (first) {
+          __builtin_amdgcn_sched_group_barrier(0x100, RPC, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, NI, 0);
+        } else {
+          sched_interleave<MPC, RPC, NI>();
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        sfor<NC - 1>([&](auto c_c) {
+          constexpr int c = decltype(c_c)::value;
+          read_chunk(As, Bs, IntC<c + 1>{});
+          mfma_chunk(IntC<c>{});
+          sched_interleave<MPC, RPC, 0>();
+          __builtin_amdgcn_sched_barrier(0);
+        });
+        __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0_imm(0));  // step kt + 1 landed, this step's reads done
+        barrier();
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      step1(0, IntC<0>{}, IntC<true>{});
+      for (int kt = 1; kt < KT; kt += 2) {
+        step1(kt, IntC<1>{}, IntC<false>{});
+        if (kt + 1 < KT) step1(kt + 1, IntC<0>{}, IntC<false>{});
+      }
+      mfma_chunk(IntC<NC - 1>{});
+      return;
+    }
     // tile 0 landed and visible; its first chunks into registers
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(kNewer0));
     barrier();
