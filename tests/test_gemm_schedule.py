@@ -13,6 +13,10 @@ stages; a prologue issues virtual steps -SB..-1 (A tile s + SA when >= 0, B
 tile s + SB); step kt waits with vmcnt(kNewer) for tile kt + 1 and then issues
 A tile kt + SA and B tile kt + SB into the stages tile kt released (B before A
 when SB == SA, after it when SB > SA); tiles past the end reload tile KT - 1.
+The one-barrier schedule of gemm_kernel (dense 16-bit products on two-stage
+rings): the prologue issues step 0 into stage 0 and waits for it; step kt
+reads stage kt % 2, issues step kt + 1 (past the end: a reload of step KT - 1)
+into the other stage and ends with vmcnt(0) and the barrier.
 wgrad_kernel (csrc/wgrad_kernel.h): the A strip and B(0), then per column tile
 t: wait for B(t), issue B(t+1) into the other buffer, multiply, stage, 8 stores.
 """
@@ -79,6 +83,30 @@ def test_a_wait_one_operation_too_shallow_is_caught(SA, SB):
         gemm_schedule(SA, SB, 16, 2, 4, wait_delta=1)
 
 
+def onebar_schedule(KT, A_W, B_W, wait_delta=0):
+    """Replays the one-barrier schedule's issue order (A then B each step, as
+    dma_step issues them with SA == SB); wait_delta shifts its vmcnt(0)."""
+    issued, last = [], {}  # issued: stage written, in issue order
+
+    def issue_step(t, stage):
+        for op, w in (("A", A_W), ("B", B_W)):
+            issued.extend([stage] * w)
+            last[(op, t)] = len(issued) - 1
+
+    def landed(t, n):
+        return all(last[(op, t)] < len(issued) - n for op in "AB")
+
+    issue_step(0, 0)
+    assert landed(0, wait_delta), (KT, "step 0")
+    for kt in range(KT):
+        reading = kt % 2
+        issue_step(min(kt + 1, KT - 1) if kt + 1 < KT else KT, (kt + 1) % 2)
+        # nothing issued since the last barrier writes the stage this step reads
+        assert all(st != reading for st in issued[len(issued) - (A_W + B_W):]), (KT, kt)
+        if kt + 1 < KT:  # the barrier that ends step kt: step kt + 1 has landed
+            assert landed(kt + 1, wait_delta), (KT, kt)
+
+
 def wgrad_schedule(KG, NT, wait_delta=0, stores=8, nwave=8):
     """Replays wgrad_kernel's issue order per wave: the A strip's two 128-row
     blocks (into B buffer 1 and the staging buffer), B tile 0 (into B buffer
@@ -112,6 +140,14 @@ def wgrad_schedule(KG, NT, wait_delta=0, stores=8, nwave=8):
         # the MFMAs read buffer t % 2 and the staging writes "S"
         assert all(b not in (t % 2, "S") for _, b in flying), (KG, NT, t)
         issue(("S", t), stores)
+
+
+def test_one_barrier_schedule_is_exact():
+    for KT in range(1, 70):
+        for A_W, B_W in WIDTHS:
+            onebar_schedule(KT, A_W, B_W)
+    with pytest.raises(AssertionError):
+        onebar_schedule(8, 4, 4, wait_delta=1)
 
 
 @pytest.mark.parametrize("KG", [2, 4, 6])
