@@ -344,16 +344,35 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
     const char* base;
     int64_t ld;
   };
-  auto b_step = [&](int kt) -> BStep {
+  // B_KSEG: the segment of the K step being fetched is kept as a cursor.  The
+  // DMA walks B's K steps in order (clamped steps repeat the last one), so the
+  // segment table in the kernel arguments is read, and the lanes' row offsets
+  // in the segment computed, only when a boundary is passed (b_seek, at the
+  // top of a step, outside its scheduling regions).  Searching the table at
+  // every step put a scalar load and its wait into every K step.
+  int seg_i = 0, seg_next = 0;       // current segment; its end (kSegUnit units)
+  const char* seg_row0 = nullptr;    // segment base at this tile's rows, minus the segment's first K byte
+  int64_t seg_ldv = 0;
+  uint32_t seg_off[BMODE == B_KSEG ? B_W : 1];  // per lane: row and chunk offset in the segment
+  auto seg_enter = [&](int i) {
+    seg_i = i;
+    seg_ldv = args.seg_ld[i];
+    seg_row0 = args.seg_base[i] + (int64_t)nt * BN * seg_ldv - (int64_t)args.seg_kt0[i] * kSegUnit;
+    seg_next = i + 1 < args.nseg ? args.seg_kt0[i + 1] : 0x7fffffff;
+#pragma unroll
+    for (int ii = 0; ii < (BMODE == B_KSEG ? B_W : 1); ++ii)
+      seg_off[ii] = (uint32_t)(b_brow[ii] * seg_ldv) + b_chunk[ii];
+  };
+  if constexpr (BMODE == B_KSEG) seg_enter(0);
+  auto b_seek = [&](int kt) {  // before the DMA of B K step kt
     if constexpr (BMODE == B_KSEG) {
       constexpr int U = KB / kSegUnit;  // segment units per K step
-      const int kta = kt + kt0;         // K step within the whole K range
-      int s = 0;
-      while (s + 1 < args.nseg && kta * U >= args.seg_kt0[s + 1]) ++s;
-      const int64_t ld = args.seg_ld[s];
-      return {args.seg_base[s] + (int64_t)nt * BN * ld +
-                  ((int64_t)kta * ROWB - (int64_t)args.seg_kt0[s] * kSegUnit),
-              ld};
+      while ((kt + kt0) * U >= seg_next) seg_enter(seg_i + 1);
+    }
+  };
+  auto b_step = [&](int kt) -> BStep {
+    if constexpr (BMODE == B_KSEG) {
+      return {seg_row0 + (int64_t)(kt + kt0) * ROWB, seg_ldv};
     } else {
       return {nullptr, 0};
     }
@@ -365,7 +384,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
   auto dma_b = [&](int kt, const BStep& bs, char* stage, int ii) {
     const char* g;
     if constexpr (BMODE == B_KSEG) {
-      g = bs.base + ((uint32_t)(b_brow[ii] * bs.ld) + b_chunk[ii]);
+      g = bs.base + seg_off[ii];
     } else if constexpr (BMODE == B_KMAJOR) {
       const int k0 = (kt + kt0) * KE;  // first K row of the step (workgroup-uniform)
       const char* rows = k0 < args.kmaj_split ? kmaj_b0 + (int64_t)k0 * ldb
@@ -458,11 +477,15 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
   // an empty K range (KT == 0, uniform over the workgroup) has no DMA and no
   // main loop: its tile is stored as zeros
   if constexpr (k1Bar) {
-    if (KT > 0) dma_step(0, ringA, 0, ringB);  // step 0 only; step kt + 1 loads during step kt
+    if (KT > 0) {  // step 0 only; step kt + 1 loads during step kt
+      b_seek(0);
+      dma_step(0, ringA, 0, ringB);
+    }
   } else
 #pragma unroll
   for (int s = -SB; s < 0 && KT > 0; ++s) {
     const int ta = s + SA, tb = s + SB;
+    b_seek(clampt(tb));
     const BStep bs = b_step(clampt(tb));
     if constexpr (!kAFirst) {
 #pragma unroll
@@ -586,6 +609,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
       auto step1 = [&](int kt, auto u_c, auto first_c) {
         constexpr int u = decltype(u_c)::value;
         constexpr bool first = decltype(first_c)::value;
+        b_seek(clampt(kt + 1));
         const char* As = ringA + u * kStageA;
         const char* Bs = ringB + u * kStageB;
         read_chunk(As, Bs, IntC<0>{});
@@ -626,6 +650,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
 
     auto one = [&](int kt, auto u_c) {
       constexpr int u = decltype(u_c)::value;  // kt % UNROLL: stages are static
+      b_seek(clampt(kt + SB));
       const char* As = ringA + (u % SA) * kStageA;
       const char* Bs = ringB + (u % SB) * kStageB;
       // phase 1
