@@ -194,6 +194,49 @@ def test_route_entry(name):
     assert torch.equal(ids, ids2) and torch.equal(probs, probs2)
 
 
+@pytest.mark.parametrize("R,k", [(5, 3), (300, 8), (700, 16), (1500, 8)])
+def test_route_expert_counts(R, k):
+    """Both routers across expert counts: fewer experts than a wave's lanes,
+    several experts per lane, and past 1024.  Sets as in test_route_entry,
+    winners in descending order of s + b (softmax: of the logit), weights from
+    the chosen scores."""
+    cfg = S.LayerConfig(f"route_r{R}", 96, 256, 128, R, k, 1, 64, 256, "bf16", seed=30 + R % 17, bias="uniform")
+    _say(f"[route R={R} k={k}]")
+    host = S.host_inputs(cfg)
+    dev = G.device_layer_inputs(cfg, host=host)
+    N = cfg.n_tokens
+    dims = M.dims_of(cfg)
+    W = O.config_weights(cfg, cache_experts=0)
+    x = O.config_x(cfg)
+    routes = O.route(x, W.w_router, W.bias, k)
+    ids = torch.empty((N, k), dtype=torch.int32, device="cuda")
+    probs = torch.empty((N, k), dtype=torch.float32, device="cuda")
+    M.latentmoe_route(dims, dev["x"], dev["w_router"], dev["bias"], ids, probs, None,
+                      torch.empty(M.workspace_bytes(dims, M.ENTRY_ROUTE), dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    g = ids.cpu().numpy().astype(np.int64)
+    near = G.check_routes(g, routes, W.bias, k)
+    v = routes.s + W.bias[None, :]
+    gv = np.take_along_axis(v, g, axis=1)
+    assert (np.diff(gv[~near], axis=1) <= 1e-6).all()
+    gs = np.take_along_axis(routes.s, g, axis=1)
+    np.testing.assert_allclose(probs.cpu().numpy(), gs / gs.sum(1, keepdims=True), rtol=0, atol=2e-5)
+    # legacy softmax router
+    M.latentmoe_route_softmax(dims, dev["x"], dev["w_router"], ids, probs, None,
+                              torch.empty(M.workspace_bytes(dims, M.ENTRY_ROUTE), dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    lo = x @ W.w_router.T
+    o_ids, _ = O.route_softmax_topk(lo, k)
+    g = ids.cpu().numpy().astype(np.int64)
+    assert ((g >= 0) & (g < R)).all()
+    near = _softmax_margin(lo, k) <= G.MARGIN
+    assert (np.sort(g[~near], 1) == np.sort(o_ids[~near], 1)).all()
+    sel = np.take_along_axis(lo, g, axis=1)
+    assert (np.diff(sel[~near], axis=1) <= 1e-6).all()
+    e = np.exp(sel - sel.max(1, keepdims=True))
+    np.testing.assert_allclose(probs.cpu().numpy(), e / e.sum(1, keepdims=True), rtol=0, atol=2e-5)
+
+
 def _ids_case(rng, N, R, k, skew=False):
     if skew:  # most tokens pick the same experts
         ids = np.stack([np.arange(k) if rng.random() < 0.8 else rng.permutation(R)[:k] for _ in range(N)])
