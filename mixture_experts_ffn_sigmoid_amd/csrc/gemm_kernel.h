@@ -38,9 +38,14 @@
 //   E_STORE   plain store (fp32 or storage dtype), masked to valid rows/cols
 //   E_SITU    SiTU-GLU hidden of the (gate, up) accumulator pair, stored as OutT
 //   E_SLOTS   p-weighted result of sorted pair q written to its own slot row q
-// Runtime option (A_DENSE with E_STORE): split K (ksplit > 1): the grid also
-// runs over K slices of kslice steps, each storing an fp32 partial product
-// (summed afterwards by splitk_reduce_kernel).
+// Runtime options (A_DENSE with E_STORE):
+//   split K (ksplit > 1): the grid also runs over K slices of kslice steps,
+//     each storing an fp32 partial product (summed afterwards by
+//     splitk_reduce_kernel);
+//   tail split (tsplit > 1, 16-bit operands): only the tiles of each XCD's
+//     last, partly filled wave are cut into K slices, so that wave's compute
+//     units all have work (fp32 partial blocks summed afterwards by
+//     tail_reduce_kernel).
 #pragma once
 
 #include "lmoe_common.h"
@@ -97,6 +102,17 @@ struct GemmArgs {
   // product at out + s * o_batch_stride
   int ksplit;
   int kslice;
+  // tail split (A_DENSE with E_STORE, 16-bit operands, tsplit > 1, m_tiles *
+  // n_tiles a multiple of 8): XCD x owns logical tiles [x P, (x + 1) P), P = m_tiles *
+  // n_tiles / 8, and takes workgroups 8 j + x, j = 0, 1, ...  Its first twhole
+  // tiles run whole (j < twhole); each of its other P - twhole tiles runs as
+  // tsplit K slices of kslice steps (j = twhole + tsplit * t + slice), which
+  // store their fp32 partial products as BM x BN blocks (tile-local rows and
+  // columns, row-major) at tpart, block (tail tile, slice), tail tile
+  // x (P - twhole) + t.  Grid: 8 (twhole + tsplit (P - twhole)).
+  int tsplit;
+  int twhole;
+  char* tpart;
   // host side only: fp32 workspace for the K slices of few-row products
   // (NULL: no split)
   char* part;
@@ -156,6 +172,19 @@ __device__ __forceinline__ void sched_interleave() {
 
 constexpr int gcd_(int a, int b) { return b == 0 ? a : gcd_(b, a % b); }
 
+// Logical dense tile L -> (M tile, N tile): groups of 4 M tiles sweep all N
+// tiles, so neighbouring ids share A and B panels (groups of 4 and 8 measure
+// alike; 16 and 32 slower).
+__device__ __forceinline__ void dense_tile_coords(int L, int m_tiles, int n_tiles, int* mt, int* nt) {
+  constexpr int GM = 4;
+  const int group = L / (GM * n_tiles);
+  const int first_m = group * GM;
+  const int gsize = min(m_tiles - first_m, GM);
+  const int in = L - group * GM * n_tiles;
+  *mt = first_m + in % gsize;
+  *nt = in / gsize;
+}
+
 template <typename TA, typename TB, typename OutT, int BM, int BN, int WGM, int WGN, int AMODE,
           int BMODE, int EMODE, int SA, int SB, int KB>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs args) {
@@ -168,7 +197,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
   constexpr int TM = WTM / 32, TN = WTN / 32;
   constexpr bool GROUPED = AMODE == A_GATHER || AMODE == A_PADDED || AMODE == A_SORTED;
   constexpr bool KBATCH = AMODE == A_KBATCH;
-  const bool split = AMODE == A_DENSE && EMODE == E_STORE && args.ksplit > 1;  // uniform
+  const bool split_all = AMODE == A_DENSE && EMODE == E_STORE && args.ksplit > 1;  // uniform
+  // the tail split exists for 16-bit operands only (the fp32 tile has no
+  // registers to spare for it)
+  constexpr bool kTail = AMODE == A_DENSE && EMODE == E_STORE && kHalf;
   // K step: KB bytes of every tile row = NCH 16-byte chunks.  One LDS-DMA
   // wave instruction moves 64 lanes x 16 bytes = RPI tile rows.
   static_assert(KB == 64 || KB == 128, "K step of 64 or 128 bytes");
@@ -201,11 +233,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
   char* const ringA = smem;
   char* const ringB = smem + SA * kStageA;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index is uniform across the wave: saying so keeps the LDS-DMA
+  // destinations (M0) in scalar registers
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WGN, wn = wave % WGN;
   const int lr = lane & 31, lh = lane >> 5;
 
   int mt, nt, e_batch = 0;
+  int tail_id = -1;  // tail split: this workgroup's tail tile (-1: a whole tile)
   if constexpr (GROUPED) {
     // The grid is sized by a bound on the tile list; only the first
     // tile_count * n_tiles workgroup ids carry work.  Those ids reach the
@@ -218,20 +253,29 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
     nt = L % args.n_tiles;
   } else {
     const int per = args.m_tiles * args.n_tiles;
-    const int total = per * (KBATCH ? args.nbatch : split ? args.ksplit : 1);
-    int L = xcd_contiguous_id(blockIdx.x, total);
-    if (KBATCH || split) {  // batch / K slice
-      e_batch = L / per;
-      L -= e_batch * per;
+    int L;
+    if (kTail && args.tsplit > 1) {
+      const int x = blockIdx.x % 8, j = blockIdx.x / 8, P = per / 8;
+      if (j < args.twhole) {
+        L = x * P + j;
+      } else {
+        const int t = (j - args.twhole) / args.tsplit;
+        e_batch = (j - args.twhole) % args.tsplit;  // K slice
+        tail_id = x * (P - args.twhole) + t;
+        L = x * P + args.twhole + t;
+      }
+    } else {
+      const int total = per * (KBATCH ? args.nbatch : split_all ? args.ksplit : 1);
+      L = xcd_contiguous_id(blockIdx.x, total);
+      if (KBATCH || split_all) {  // batch / K slice
+        e_batch = L / per;
+        L -= e_batch * per;
+      }
     }
-    constexpr int GM = 4;  // raster: groups of 4 M tiles sweep all N tiles (4 and 8 measure alike; 16, 32 slower)
-    const int group = L / (GM * args.n_tiles);
-    const int first_m = group * GM;
-    const int gsize = min(args.m_tiles - first_m, GM);
-    const int in = L - group * GM * args.n_tiles;
-    mt = first_m + in % gsize;
-    nt = in / gsize;
+    dense_tile_coords(L, args.m_tiles, args.n_tiles, &mt, &nt);
   }
+  const bool tail = tail_id >= 0;           // uniform
+  const bool split = split_all || tail;     // this workgroup covers one K slice
 
   int m0, rows_valid, e = 0;
   int64_t off = 0;
@@ -249,7 +293,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
   const int klen = KBATCH ? args.kr_len[e_batch] : args.K;
   const int64_t lda = KBATCH ? (int64_t)klen * (int64_t)sizeof(TA) : args.lda;  // bytes
   const int64_t ldb = KBATCH ? (int64_t)klen * (int64_t)sizeof(TB) : args.ldb;
-  char* const outp = args.out + ((KBATCH || split) ? e_batch * args.o_batch_stride : 0);
+  char* const outp = tail ? args.tpart + ((int64_t)tail_id * args.tsplit + e_batch) * (BM * BN * 4)
+                          : args.out + ((KBATCH || split_all) ? e_batch * args.o_batch_stride : 0);
   const int kt0 = split ? e_batch * args.kslice : 0;  // first K step of this workgroup's slice
   const int64_t k0b = (int64_t)kt0 * ROWB;
   // E_SLOTS: slot row q and weight p_q of every tile row, fetched now (their
@@ -714,7 +759,23 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
     main_loop(IntC<TM>{});
   }
 
-  // ---- epilogue.  Each wave stages its finished output tile in LDS (the
+  // ---- epilogue.  A tail-split K slice stores its fp32 partial product as
+  // the tile's BM x BN block (every row and column: values past the valid
+  // range come from clamped operand rows, finite, and are never read).
+  if constexpr (kTail) {
+    if (tail) {
+      float* const tp = (float*)outp;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            tp[(wm * WTM + i * 32 + 8 * (v >> 2) + 4 * lh + (v & 3)) * BN + wn * WTN + j * 32 + lr] = acc[i][j][v];
+      return;
+    }
+  }
+  // Each wave stages its finished output tile in LDS (the
   // operand ring is free once every wave has passed the barrier below) and
   // writes it back as 16-byte row chunks; falls back to per-element stores
   // when the staged tile would not fit.
@@ -853,6 +914,63 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     }
   }
   if (out_of_range && range_flag) *range_flag = 1;
+}
+
+// The tail tiles of a tail-split product (GemmArgs: tsplit, twhole, tpart):
+// out tile = sum of its K slices' fp32 partial blocks in slice order, stored
+// as OutT (row stride ldo bytes) within M x N.  One workgroup per 16 rows of
+// a tail tile; thread t sums BN / 16 consecutive columns of row t / 16.
+template <typename OutT, int BM, int BN>
+__global__ __launch_bounds__(256) void tail_reduce_kernel(const GemmArgs a) {
+  static_assert(BM % 16 == 0 && BN % 64 == 0, "16-row blocks, 4-column groups");
+  constexpr int CW = BN / 16;  // columns per thread
+  constexpr bool kRangeCheck = __is_same(OutT, f16_t);
+  const int tail_id = blockIdx.x / (BM / 16), rb = blockIdx.x % (BM / 16);
+  const int P = a.m_tiles * a.n_tiles / 8, rem = P - a.twhole;
+  int mt, nt;
+  dense_tile_coords((tail_id / rem) * P + a.twhole + tail_id % rem, a.m_tiles, a.n_tiles, &mt, &nt);
+  const int r = rb * 16 + (int)threadIdx.x / 16, c0 = ((int)threadIdx.x % 16) * CW;
+  const int m = mt * BM + r, n0 = nt * BN + c0;
+  if (m >= a.M || n0 >= a.N) return;
+  const float* src = (const float*)a.tpart + (int64_t)tail_id * a.tsplit * (BM * BN) + r * BN + c0;
+  f32x4 acc[CW / 4];
+#pragma unroll
+  for (int q = 0; q < CW / 4; ++q) acc[q] = *(const f32x4*)(src + 4 * q);
+  for (int sl = 1; sl < a.tsplit; ++sl) {
+    const float* s = src + (int64_t)sl * (BM * BN);
+    f32x4 b[CW / 4];
+#pragma unroll
+    for (int q = 0; q < CW / 4; ++q) b[q] = *(const f32x4*)(s + 4 * q);
+#pragma unroll
+    for (int q = 0; q < CW / 4; ++q) acc[q] += b[q];
+  }
+  bool out_of_range = false;
+  OutT* dst = (OutT*)(a.out + (int64_t)m * a.ldo) + n0;
+  const bool whole = n0 + CW <= a.N && (((uintptr_t)a.out | (uintptr_t)a.ldo) & 15) == 0;
+  if (whole) {
+    // CW values as 16-byte stores (n0 * sizeof(OutT) is a multiple of 32)
+    OutT vals[CW];
+#pragma unroll
+    for (int q = 0; q < CW; ++q) {
+      const float v = acc[q / 4][q % 4];
+      if constexpr (kRangeCheck) out_of_range |= f16_out_of_range(v);
+      Elem<OutT>::store(&vals[q], v);
+    }
+    constexpr int NV = CW * (int)sizeof(OutT) / 16;
+#pragma unroll
+    for (int q = 0; q < NV; ++q) {
+      u32x4 w;
+      __builtin_memcpy(&w, (const char*)vals + 16 * q, 16);
+      *((u32x4*)dst + q) = w;
+    }
+  } else {
+    for (int q = 0; q < CW && n0 + q < a.N; ++q) {
+      const float v = acc[q / 4][q % 4];
+      if constexpr (kRangeCheck) out_of_range |= f16_out_of_range(v);
+      Elem<OutT>::store(dst + q, v);
+    }
+  }
+  if (kRangeCheck && out_of_range && a.range_flag) *a.range_flag = 1;
 }
 
 }  // namespace lmoe

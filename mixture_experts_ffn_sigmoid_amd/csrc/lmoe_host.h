@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -157,6 +158,76 @@ int64_t splitk_bytes(int64_t M, int64_t N, int64_t k_bytes) {
   return S > 1 ? (int64_t)S * M * N * 4 : 0;
 }
 
+// Block tiles (rows x cols, waves, A / B LDS stages, bytes of K per step):
+//   S  64 x 128 (256 for gate/up pairs), 4 waves, 3/3, 128: few-row dense products
+//   M 128 x 128, 4 waves, 3/3, 128
+//   L 256 x 256, 8 waves, 2/2, 128 (128 KB of LDS): large dense products
+//   W 192 x 256, 8 waves, 2/3, 128 (144 KB): grouped expert products that
+//     stream their weights (B) from HBM; the B ring is one stage deeper than
+//     the ring of the (L2-resident) A rows
+//   V  64 x 256, 4 waves, 2/3, 128: the same for a handful of rows per expert
+//   V2 64 x 256, 4 waves, 2/3, 64 (56 KB, two workgroups per CU): the routed
+//     down projection with a handful of rows per expert, whose tiles have few
+//     K steps: one workgroup's ring fill overlaps the other's streaming
+//   M2 128 x 128, 4 waves, 3/3, 64 (48 KB, three workgroups per CU): short-K
+//     products whose time goes into storing the output tile
+enum Tile { TILE_S = 0, TILE_M = 1, TILE_L = 2, TILE_W = 3, TILE_V = 4, TILE_M2 = 5, TILE_V2 = 6 };
+
+// Dense products: 32-row tiles for a handful of tokens, 256 x 256 when that
+// still gives about one tile per compute unit, else 128 x 128.
+Tile dense_tile(int64_t M, int64_t cols, bool dual) {
+  if (M <= 64) return TILE_S;
+  const int64_t big = ((M + 255) / 256) * ((cols + (dual ? 127 : 255)) / (dual ? 128 : 256));
+  return big >= 240 ? TILE_L : TILE_M;
+}
+
+// Compute units per XCD of the current device (8 XCDs), 32 (gfx950's 256 /
+// 8) when no device answers.  Cached per device.
+int cus_per_xcd() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 32;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8) return 32;
+    n = cus / 8;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+// Tail split of a large dense product (256 x 256 tiles, GemmArgs tsplit):
+// each XCD runs P tiles on its `cus` compute units, so its last wave holds
+// rem = P mod cus tiles and leaves the other units idle.  Cutting those tiles
+// into S = cus / rem K slices (S <= 4, >= 8 K steps each) turns that wave
+// into one of 1 / S of the time, for S fp32 partial blocks per tail tile
+// (summed by tail_reduce_kernel).  Applies to 16-bit operands when the tile
+// count is a multiple of 8 and rem <= cus / 2.
+struct TailPlan {
+  int S = 1, whole = 0, kslice = 0, tail_tiles = 0;
+  int64_t bytes = 0;
+};
+constexpr int kTailTile = 256;            // the tile the tail split runs on
+constexpr int64_t kTailBlocksMax = 8 * 32;  // partial blocks the forward workspace reserves
+constexpr int64_t kTailBlockBytes = (int64_t)kTailTile * kTailTile * 4;
+TailPlan tail_split_plan(int64_t m_tiles, int64_t n_tiles, int64_t steps, int cus) {
+  TailPlan tp;
+  const int64_t per = m_tiles * n_tiles;
+  if (per <= 0 || per % 8 != 0 || cus < 2) return tp;
+  const int64_t P = per / 8, rem = P % cus;
+  if (rem == 0) return tp;
+  const int64_t S = std::min<int64_t>(cus / rem, 4);
+  if (S < 2 || steps / S < 8) return tp;
+  const int64_t kslice = (steps + S - 1) / S;
+  tp.S = (int)((steps + kslice - 1) / kslice);  // every slice non-empty
+  tp.kslice = (int)kslice;
+  tp.whole = (int)(P - rem);
+  tp.tail_tiles = (int)(8 * rem);
+  tp.bytes = 8 * rem * tp.S * kTailBlockBytes;
+  return tp;
+}
+
 struct Carver {
   char* base;
   size_t off = 0;
@@ -237,6 +308,10 @@ size_t carve_forward(const Plan& p, char* b, ForwardWs* w) {
   const int64_t pr = std::min<int64_t>(p.N, 64);
   w->part_bytes = std::max({splitk_bytes(pr, p.l, (int64_t)p.d * p.es), splitk_bytes(pr, p.R, (int64_t)p.d * p.es),
                             splitk_bytes(pr, p.d, p.ldh * p.es)});
+  // the tail split of the latent and merge products on 256 x 256 tiles
+  // (a fixed reservation, so the workspace never shrinks as N grows)
+  if (dense_tile(p.N, p.l, false) == TILE_L || dense_tile(p.N, p.d, false) == TILE_L)
+    w->part_bytes = std::max(w->part_bytes, kTailBlocksMax * kTailBlockBytes);
   w->part = c.take<char>((size_t)w->part_bytes);
   return c.off;
 }
@@ -370,7 +445,9 @@ lmoe_status side_stream(hipStream_t* out) {
 template <typename TA, typename TB, typename OutT, int BM, int BN, int WGM, int WGN, int AM, int BMD,
           int EM, int SA, int SB, int KB>
 lmoe_status launch_gemm(GemmArgs a, hipStream_t st) {
-  const int64_t grid = (int64_t)a.m_tiles * a.n_tiles * (AM == A_KBATCH ? a.nbatch : a.ksplit > 1 ? a.ksplit : 1);
+  const int64_t per = (int64_t)a.m_tiles * a.n_tiles;
+  const int64_t grid = a.tsplit > 1 ? 8 * (a.twhole + (per / 8 - a.twhole) * (int64_t)a.tsplit)
+                                    : per * (AM == A_KBATCH ? a.nbatch : a.ksplit > 1 ? a.ksplit : 1);
   if (grid <= 0) return LMOE_OK;
   if (grid > INT32_MAX) return fail(LMOE_ERR_UNSUPPORTED, "GEMM grid too large");
   gemm_kernel<TA, TB, OutT, BM, BN, WGM, WGN, AM, BMD, EM, SA, SB, KB>
@@ -379,20 +456,6 @@ lmoe_status launch_gemm(GemmArgs a, hipStream_t st) {
   return LMOE_OK;
 }
 
-// Block tiles (rows x cols, waves, A / B LDS stages, bytes of K per step):
-//   S  64 x 128 (256 for gate/up pairs), 4 waves, 3/3, 128: few-row dense products
-//   M 128 x 128, 4 waves, 3/3, 128
-//   L 256 x 256, 8 waves, 2/2, 128 (128 KB of LDS): large dense products
-//   W 192 x 256, 8 waves, 2/3, 128 (144 KB): grouped expert products that
-//     stream their weights (B) from HBM; the B ring is one stage deeper than
-//     the ring of the (L2-resident) A rows
-//   V  64 x 256, 4 waves, 2/3, 128: the same for a handful of rows per expert
-//   V2 64 x 256, 4 waves, 2/3, 64 (56 KB, two workgroups per CU): the routed
-//     down projection with a handful of rows per expert, whose tiles have few
-//     K steps: one workgroup's ring fill overlaps the other's streaming
-//   M2 128 x 128, 4 waves, 3/3, 64 (48 KB, three workgroups per CU): short-K
-//     products whose time goes into storing the output tile
-enum Tile { TILE_S = 0, TILE_M = 1, TILE_L = 2, TILE_W = 3, TILE_V = 4, TILE_M2 = 5, TILE_V2 = 6 };
 
 template <typename TA, typename TB, typename OutT, int AM, int BMD, int EM, int BM, int BN, int WGM,
           int WGN, int SA, int SB, int KB = 64>
@@ -436,6 +499,24 @@ lmoe_status gemm(GemmArgs a, Tile t, hipStream_t st) {
       LMOE_HIP(hipGetLastError());
       return LMOE_OK;
     }
+    if (sizeof(TA) == 2 && t == TILE_L && a.part && a.M > 0 && a.N > 0 && (int64_t)a.K * 2 % 128 == 0) {
+      GemmArgs g = a;
+      g.m_tiles = (a.M + kTailTile - 1) / kTailTile;
+      g.n_tiles = (a.N + kTailTile - 1) / kTailTile;
+      const TailPlan tp = tail_split_plan(g.m_tiles, g.n_tiles, (int64_t)a.K * sizeof(TA) / 128, cus_per_xcd());
+      if (tp.S > 1 && tp.bytes <= a.part_bytes) {
+        g.tsplit = tp.S;
+        g.twhole = tp.whole;
+        g.kslice = tp.kslice;
+        g.tpart = a.part;
+        g.part = nullptr;
+        const lmoe_status ts = gemm_cfg<TA, TB, OutT, AM, BMD, EM, kTailTile, kTailTile, 2, 4, 2, 2, 128>(g, st);
+        if (ts != LMOE_OK) return ts;
+        tail_reduce_kernel<OutT, kTailTile, kTailTile><<<(unsigned)tp.tail_tiles * (kTailTile / 16), 256, 0, st>>>(g);
+        LMOE_HIP(hipGetLastError());
+        return LMOE_OK;
+      }
+    }
   }
   if constexpr (AM == A_DENSE || AM == A_KBATCH) {
     switch (t) {
@@ -454,13 +535,6 @@ lmoe_status gemm(GemmArgs a, Tile t, hipStream_t st) {
   }
 }
 
-// Dense products: 32-row tiles for a handful of tokens, 256 x 256 when that
-// still gives about one tile per compute unit, else 128 x 128.
-Tile dense_tile(int64_t M, int64_t cols, bool dual) {
-  if (M <= 64) return TILE_S;
-  const int64_t big = ((M + 255) / 256) * ((cols + (dual ? 127 : 255)) / (dual ? 128 : 256));
-  return big >= 240 ? TILE_L : TILE_M;
-}
 
 GemmArgs base_args(const lmoe_dims* dm) {
   GemmArgs a;

@@ -45,6 +45,11 @@ def _small_cfgs():
         # (4 slices each, the merge's slices crossing its shared / W_up segment boundary)
         S.LayerConfig("wide_d_bf16_n40", 40, 2048, 256, 16, 4, 1, 256, 2048, "bf16", seed=13, bias="uniform"),
         S.LayerConfig("wide_d_f32_n17", 17, 1024, 128, 16, 2, 1, 128, 1024, "f32", seed=14),
+        # the merge product on 256 x 256 tiles with a partly filled last wave:
+        # 12 x 32 tiles, 48 per XCD, of which the last 16 run as two K slices
+        # of 8 steps (tail split), with ragged rows (2900 = 11 * 256 + 84) and
+        # columns (8064 = 31 * 256 + 128)
+        S.LayerConfig("tail_split_bf16", 2900, 8064, 128, 8, 2, 1, 128, 896, "bf16", seed=15, bias="uniform"),
     ]
 
 
