@@ -354,6 +354,8 @@ lmoe_status run_layer_backward(const Plan& p, const lmoe_dims* dm, const lmoe_we
   f.seg_kt0[f.nseg] = (int)(kcat * ei / kSegUnit);
   f.out = (char*)dx;
   f.ldo = (int64_t)d * 4;
+  f.part = w.tpart;  // partial blocks for the tail split (NULL unless dx runs on 256 x 256 tiles)
+  f.part_bytes = w.tpart_bytes;
   LMOE_TRY((gemm<TI, T, float, A_DENSE, B_KSEG, E_STORE>(f, dense_tile(N, d, false), st)));
   // ---- dense weight gradients: products over tokens (K = npad, zero-padded transposes)
   set_ints_kernel<<<1, 64, 0, st>>>(w.seg, (int32_t)N, 0, 0, (int32_t)npad);

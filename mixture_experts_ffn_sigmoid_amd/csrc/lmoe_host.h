@@ -377,6 +377,8 @@ struct LayerBwdWs {
   char *w_upT, *shoT, *w_downT, *w_rT, *sgT, *suT;  // storage type
   int32_t* seg;
   char *dyT, *rnT, *hsT, *dcatT, *xT;  // intermediate type
+  char* tpart;  // fp32 partial blocks of dx's tail split (NULL: none)
+  int64_t tpart_bytes;
 };
 size_t carve_layer_backward(const Plan& p, char* b, LayerBwdWs* w) {
   Carver c{b};
@@ -415,6 +417,9 @@ size_t carve_layer_backward(const Plan& p, char* b, LayerBwdWs* w) {
   w->hsT = c.take<char>((size_t)w->nsf * w->npad * ei);
   w->dcatT = c.take<char>((size_t)w->kcat * w->npad * ei);
   w->xT = c.take<char>((size_t)p.d * w->npad * ei);
+  // dx on 256 x 256 tiles with 16-bit operands may take the tail split
+  w->tpart_bytes = (ei == 2 && dense_tile(N, p.d, false) == TILE_L) ? kTailBlocksMax * kTailBlockBytes : 0;
+  w->tpart = w->tpart_bytes ? c.take<char>((size_t)w->tpart_bytes) : nullptr;
   return c.off;
 }
 

@@ -246,6 +246,9 @@ def _layer_cfgs():
         S.LayerConfig("kR_bf16", 70, 128, 64, 6, 6, 3, 128, 64, "bf16", seed=8, bias="uniform"),
         S.LayerConfig("wide_k_bf16", 333, 256, 128, 40, 9, 1, 192, 256, "bf16", seed=9, bias="uniform"),
         _STRIP,
+        # dx on 256 x 256 tiles (12 x 32, 48 per XCD) whose last 16 tiles per
+        # XCD run as two K slices (tail split), ragged in rows and columns
+        S.LayerConfig("tail_split_bf16", 2900, 8064, 128, 8, 2, 1, 128, 896, "bf16", seed=15, bias="uniform"),
     ]
 
 
