@@ -19,6 +19,12 @@ reads stage kt % 2, issues step kt + 1 (past the end: a reload of step KT - 1)
 into the other stage and ends with vmcnt(0) and the barrier.
 wgrad_kernel (csrc/wgrad_kernel.h): the A strip and B(0), then per column tile
 t: wait for B(t), issue B(t+1) into the other buffer, multiply, stage, 8 stores.
+
+The tail split of the dense 256 x 256 products (gemm_kernel's tsplit,
+tail_split_plan and tail_reduce_kernel in csrc/lmoe_host.h and
+csrc/gemm_kernel.h) is modelled the same way: its workgroup -> (tile, K slice)
+numbering must cover every tile exactly once (whole, or as all of its slices),
+keep every slice non-empty, and stay inside the reserved partial blocks.
 """
 import pytest
 
@@ -156,3 +162,84 @@ def test_wgrad_vmcnt_schedule_is_exact(KG):
         wgrad_schedule(KG, NT)
     with pytest.raises(AssertionError):
         wgrad_schedule(KG, 4, wait_delta=1)
+
+
+def tail_plan(m_tiles, n_tiles, steps, cus):
+    """tail_split_plan: (S, whole tiles per XCD, kslice) or None."""
+    per = m_tiles * n_tiles
+    if per <= 0 or per % 8 or cus < 2:
+        return None
+    P = per // 8
+    rem = P % cus
+    if rem == 0:
+        return None
+    S = min(cus // rem, 4)
+    if S < 2 or steps // S < 8:
+        return None
+    kslice = -(-steps // S)
+    return -(-steps // kslice), P - rem, kslice
+
+
+def tail_tile_coords(L, m_tiles, n_tiles):
+    """dense_tile_coords: raster groups of 4 M tiles."""
+    g = L // (4 * n_tiles)
+    first = 4 * g
+    gs = min(m_tiles - first, 4)
+    i = L - g * 4 * n_tiles
+    return first + i % gs, i // gs
+
+
+def tail_workgroups(m_tiles, n_tiles, steps, S, whole, kslice):
+    """Yields (tile, slice or None, tail id, first K step, K steps) per workgroup."""
+    P = m_tiles * n_tiles // 8
+    for b in range(8 * (whole + (P - whole) * S)):
+        x, j = b % 8, b // 8
+        if j < whole:
+            yield x * P + j, None, None, 0, steps
+        else:
+            t, sl = divmod(j - whole, S)
+            kt0 = sl * kslice
+            yield x * P + whole + t, sl, x * (P - whole) + t, kt0, min(kslice, steps - kt0)
+
+
+@pytest.mark.parametrize("cus", [32, 16])
+def test_tail_split_covers_every_tile_once(cus):
+    tested = 0
+    for m_tiles in range(1, 41):
+        for n_tiles in range(1, 41):
+            for steps in (16, 23, 56, 344, 646):
+                plan = tail_plan(m_tiles, n_tiles, steps, cus)
+                if plan is None:
+                    continue
+                S, whole, kslice = plan
+                P = m_tiles * n_tiles // 8
+                rem = P - whole
+                assert 2 <= S <= 4 and 8 * rem * S <= 8 * cus  # within the reserved blocks
+                seen = {}
+                for L, sl, tid, kt0, kt in tail_workgroups(m_tiles, n_tiles, steps, S, whole, kslice):
+                    assert 0 <= L < m_tiles * n_tiles and kt >= 1
+                    seen.setdefault(L, []).append((sl, kt0, kt))
+                    if tid is not None:
+                        assert 0 <= tid * S + sl < 8 * rem * S
+                        # tail_reduce_kernel's inverse of the tail id
+                        assert (tid // rem) * P + whole + tid % rem == L
+                assert len(seen) == m_tiles * n_tiles
+                for L, parts in seen.items():
+                    if parts[0][0] is None:
+                        assert parts == [(None, 0, steps)]
+                    else:
+                        parts.sort()
+                        assert [p[0] for p in parts] == list(range(S))
+                        assert sum(p[2] for p in parts) == steps  # the slices tile K
+                        assert all(parts[i][1] + parts[i][2] == parts[i + 1][1] for i in range(S - 1))
+                coords = {tail_tile_coords(L, m_tiles, n_tiles) for L in range(m_tiles * n_tiles)}
+                assert coords == {(a, b) for a in range(m_tiles) for b in range(n_tiles)}
+                tested += 1
+    assert tested > 100
+
+
+def test_tail_split_merge_shape():
+    """The merge at 8192 tokens: 32 x 28 tiles, 112 per XCD on 32 CUs; the last
+    16 of each XCD run as two K slices of 172 steps."""
+    assert tail_plan(32, 28, 344, 32) == (2, 96, 172)
+    assert tail_plan(32, 14, 56, 32) is None  # the latent: last wave 3/4 full
