@@ -73,7 +73,8 @@ __device__ __forceinline__ void wgrad_strip(const char* a_blk, const char* b_blk
   constexpr int NWAVE = kWgradWaves, NTHR = kWgradThreads;
   constexpr int KS = 2 * KG;              // MFMA K steps of 16
   constexpr int kDma = KG * (8 / NWAVE);  // DMA instructions per wave per 128-row block
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // (the wave index is uniform: readfirstlane keeps the DMA destinations scalar)
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // waves 4 (rows) x 2 (columns): 64 x 64 of the tile each
   const int wm = wave >> 1, wn = wave & 1, lr = lane & 31, lh = lane >> 5;
   const int NT = N / kWgradTile;
@@ -101,10 +102,10 @@ __device__ __forceinline__ void wgrad_strip(const char* a_blk, const char* b_blk
         fa[s][i] = *(const u32x4*)(Ab + wg_pos(s >> 1, (wm & 1) * 64 + i * 32 + lr, 2 * (s & 1) + lh));
   }
 
-  // per-lane parts of the staging address: row wm*64 + 4*lh (+ constants),
-  // chunk (wn*8 + lr/8) ^ 4*lh (^ constants), byte (lr % 8) * 2
-  const int st_base = (wm * 64 + 4 * lh) * 256 + (lr & 7) * 2;
-  const int st_chunk = (wn * 8 + (lr >> 3)) ^ (4 * lh);
+  // The MFMAs take the B fragment first, so each 32 x 32 accumulator holds
+  // the transposed sub-tile: lane l has output row lr and columns
+  // 8 (v / 4) + 4 lh + v % 4, i.e. four runs of four consecutive columns,
+  // each staged with one 8-byte LDS write.
   constexpr int kStores = kWgradStrip * 256 / 16 / NTHR;  // 16-byte stores per thread per tile
   for (int t = 0; t < NT; ++t) {
     const char* const B = bbuf(t);
@@ -134,20 +135,25 @@ __device__ __forceinline__ void wgrad_strip(const char* a_blk, const char* b_blk
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, fa[s][i]),
-                                                             __builtin_bit_cast(f16x8, fb[j]), acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, fb[j]),
+                                                             __builtin_bit_cast(f16x8, fa[s][i]), acc[i][j], 0, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 2; ++i) {
+      const int row = wm * 64 + i * 32 + lr;
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          // row = wm*64 + 4*lh + i*32 + 8*(v/4) + v%4, whose low 4 bits are 4*lh + 8*((v/4)%2) + v%4
-          const int rc = i * 32 + 8 * (v >> 2) + (v & 3);
-          const int cx = 8 * ((v >> 2) & 1) + (v & 3);
-          Elem<TO>::store((TO*)(S + st_base + rc * 256 + ((st_chunk ^ (4 * j) ^ cx) << 4)), acc[i][j][v]);
+        for (int q = 0; q < 4; ++q) {
+          // columns wn*64 + j*32 + 8q + 4lh + (0..3): bytes 8 lh.. of chunk wn*8 + j*4 + q
+          TO four[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) Elem<TO>::store(&four[u], acc[i][j][4 * q + u]);
+          u32x2 w;
+          __builtin_memcpy(&w, four, 8);
+          *(u32x2*)(S + wg_spos(row, wn * 8 + j * 4 + q) + 8 * lh) = w;
         }
+    }
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(wg_lgkm0());
     __builtin_amdgcn_s_barrier();
