@@ -173,7 +173,29 @@ lmoe_status routed_gradients(const Plan& p, const lmoe_dims* dm, const void* z, 
   }
   pair_sum_kernel<TDZ><<<(unsigned)p.N, 256, 0, st>>>(dzrows, w.inv, p.k, l, nullptr, (TDZ*)dz, ld_dz);
   LMOE_HIP(hipGetLastError());
-  // 6. weight gradients: per expert, products over its pairs (K = padded pair range)
+  // 6. weight gradients: per expert, products over its pairs.  Up to
+  // kWgradKMax pairs per expert, with 16-bit operands and 256-multiple
+  // widths, one workgroup per 256-row strip reads the pair rows as stored
+  // (K-major), keeps its A fragments in registers and sweeps the columns;
+  // otherwise the pair rows are transposed into zero-padded per-expert
+  // segments for batched GEMM tiles (128 x 128, 64-byte K steps in a 3-stage
+  // ring: 48 KB of LDS, three tiles per compute unit).
+  if constexpr (sizeof(TI) == 2 && sizeof(T) == 2 && sizeof(TZ) == 2) {
+    if ((C + 63) / 64 * 64 <= kWgradKMax && l % kWgradStrip == 0 && f % kWgradStrip == 0) {
+      auto strips = [&](const TI* a, int64_t lda, int M, const auto* b, int64_t ldb, const int32_t* b_order, int N,
+                        void* out) -> lmoe_status {
+        wgrad_kernel<<<(unsigned)((int64_t)R * (M / kWgradStrip)), kWgradThreads, 0, st>>>(
+            a, lda, b, ldb, b_order, p.k, w.counts, w.offsets, M, N, (T*)out);
+        LMOE_HIP(hipGetLastError());
+        return LMOE_OK;
+      };
+      const TI* dgu = (const TI*)w.dgu;
+      LMOE_TRY(strips((const TI*)w.dout, l * ei, l, (const TI*)w.hs, f * ei, nullptr, f, dw_o));
+      LMOE_TRY(strips(dgu, 2 * f * ei, f, (const TZ*)z, l * (int64_t)sizeof(TZ), w.order, l, dw_g));
+      LMOE_TRY(strips(dgu + f, 2 * f * ei, f, (const TZ*)z, l * (int64_t)sizeof(TZ), w.order, l, dw_u));
+      return LMOE_OK;
+    }
+  }
   const unsigned ysegs = (unsigned)((C + 63) / 64);
   if (ysegs > 0) {
     const dim3 gl(l / 64, ysegs, R), gf(f / 64, ysegs, R);
@@ -204,25 +226,6 @@ lmoe_status routed_gradients(const Plan& p, const lmoe_dims* dm, const void* z, 
     g.o_batch_stride = (int64_t)M * N * es;
     return g;
   };
-  // Every expert's K is its padded pair count (at most C rounded up to 64).
-  // Up to kWgradKMax, with 16-bit operands and 256-multiple widths, one
-  // workgroup per 256-row strip keeps its A fragments in registers and sweeps
-  // the columns; otherwise batched GEMM tiles (128 x 128, 64-byte K steps in
-  // a 3-stage ring: 48 KB of LDS, three tiles per compute unit).
-  if constexpr (sizeof(TI) == 2 && sizeof(T) == 2) {
-    if ((C + 63) / 64 * 64 <= kWgradKMax && l % kWgradStrip == 0 && f % kWgradStrip == 0) {
-      auto strips = [&](const void* a, int M, const void* b, int N, void* out) -> lmoe_status {
-        wgrad_kernel<TI, T><<<(unsigned)((int64_t)R * (M / kWgradStrip)), kWgradThreads, 0, st>>>(
-            (const TI*)a, (const TI*)b, w.kr_off, w.kr_len, M, N, (T*)out);
-        LMOE_HIP(hipGetLastError());
-        return LMOE_OK;
-      };
-      LMOE_TRY(strips(w.doutT, l, w.hT, f, dw_o));
-      LMOE_TRY(strips(w.dgT, f, w.zT, l, dw_g));
-      LMOE_TRY(strips(w.duT, f, w.zT, l, dw_u));
-      return LMOE_OK;
-    }
-  }
   constexpr Tile kWgradGemmTile = TILE_M2;
   LMOE_TRY((gemm<TI, TI, T, A_KBATCH, B_SINGLE, E_STORE>(batched(w.doutT, l, w.hT, f, dw_o), kWgradGemmTile, st)));
   LMOE_TRY((gemm<TI, TI, T, A_KBATCH, B_SINGLE, E_STORE>(batched(w.dgT, f, w.zT, l, dw_g), kWgradGemmTile, st)));

@@ -56,11 +56,6 @@ enum { A_DENSE = 0, A_GATHER = 1, A_PADDED = 2, A_SORTED = 3, A_KBATCH = 4 };
 enum { B_SINGLE = 0, B_DUAL = 1, B_KSEG = 2, B_KMAJOR = 3 };
 enum { E_STORE = 0, E_SITU = 1, E_SLOTS = 2 };
 
-template <int V>
-struct IntC {
-  static constexpr int value = V;
-};
-
 constexpr int kMaxSeg = 17;
 constexpr int kSegUnit = 64;  // B_KSEG segment boundaries are given in 64-byte units of K
 
@@ -138,15 +133,6 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 
 // s_waitcnt immediate that also waits for every LDS operation of this wave (lgkmcnt 0).
 constexpr int vmcnt_lgkm0_imm(int n) { return (n & 0xF) | (((n >> 4) & 3) << 14) | (0x7 << 4); }
-
-// Compile-time loop: f(IntC<0>{}), ..., f(IntC<N-1>{}).
-template <int N, int I = 0, typename F>
-__device__ __forceinline__ void sfor(F&& f) {
-  if constexpr (I < N) {
-    f(IntC<I>{});
-    sfor<N, I + 1>(f);
-  }
-}
 
 // Instruction order of one scheduling region (scheduling-group barriers;
 // masks 0x008 MFMA, 0x100 LDS read, 0x020 VMEM read = LDS-DMA): NM MFMAs,

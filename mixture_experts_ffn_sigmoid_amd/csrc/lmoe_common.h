@@ -17,6 +17,20 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+
+// Compile-time loop: f(IntC<0>{}), ..., f(IntC<N-1>{}).
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void sfor(F&& f) {
+  if constexpr (I < N) {
+    f(IntC<I>{});
+    sfor<N, I + 1>(f);
+  }
+}
+
 __device__ __forceinline__ float bf16_to_f32(bf16_t h) {
   return __uint_as_float(((uint32_t)h) << 16);
 }

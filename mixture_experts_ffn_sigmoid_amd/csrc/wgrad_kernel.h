@@ -1,11 +1,15 @@
 // Per-expert weight gradients with a short reduction:
 //
-//   dW[e] (M x N, row-major) = A_e B_e^T,
+//   dW[e] (M x N, row-major) = sum over the expert's pairs q of a_q^T b_q,
 //
-// A_e the row-major [M, K_e] block at element kr_off[e] * M of `a`, B_e the
-// [N, K_e] block at kr_off[e] * N of `b`, K_e = kr_len[e] in {0, 64, 128, 192}
-// (an expert's pairs, zero-padded to a multiple of 64).  M is a multiple of
-// 256 and N of 128; 16-bit operands, fp32 accumulation.
+// a_q (M values) and b_q (N values) rows of pair-row buffers as stored
+// (K-major operands: the reduction runs over rows): a_q = row off_e + q of
+// `a` at column offset 0, b_q = row off_e + q of `b`, or, gathered, the
+// token's row order[off_e + q] / top_k.  K_e = counts[e] <= 192 pairs,
+// padded to a multiple of 64 (the padded rows of the A strip are zeroed in
+// LDS; those of B repeat its last pair row, finite, multiplied by zero).  M
+// is a multiple of 256 and N of 128; 16-bit operands (a bf16 b is widened to
+// fp16 in registers), fp32 accumulation.
 //
 // A general GEMM tile spends most of its life waiting for its few K steps'
 // operands.  Here one workgroup (8 waves, 4 x 2) owns an expert's 256-row
@@ -15,6 +19,12 @@
 // tile t+1 streams in (LDS-DMA) while tile t is multiplied, staged in a third
 // buffer and written back as 16-byte row chunks.  The loads of a CU queue with
 // its stores; a 256-row strip reads each B tile once per 64 KB of output.
+//
+// LDS images of the operands hold K-row k (one pair row's 256 strip columns
+// or 128 tile columns) at k * ROWK, 16-byte chunks XOR-swizzled per K-row;
+// MFMA fragments come out through gfx950's transposing LDS read
+// ds_read_b64_tr_b16: within each 16-lane group, lanes 4j..4j+3 name 4
+// consecutive values of K-row j and lane i receives column i of the 4 rows.
 #pragma once
 
 #include "lmoe_common.h"
@@ -22,8 +32,8 @@
 namespace lmoe {
 
 constexpr int kWgradKMax = 192;    // largest K_e this kernel takes
-constexpr int kWgradTile = 128;    // columns of an output tile, rows of a B tile
-constexpr int kWgradStrip = 256;   // rows of an A strip and of an output tile
+constexpr int kWgradTile = 128;    // columns of an output tile (of a B tile's K-rows)
+constexpr int kWgradStrip = 256;   // rows of an output tile (columns of an A strip's K-rows)
 constexpr int kWgradBuf = kWgradTile * kWgradKMax * 2;     // one B tile (48 KB)
 constexpr int kWgradStage = kWgradStrip * kWgradTile * 2;  // one staged output tile (64 KB)
 constexpr int kWgradLds = 2 * kWgradBuf + kWgradStage;    // 160 KB: one workgroup per CU
@@ -36,79 +46,133 @@ typedef __attribute__((address_space(3))) void wg_lds_void_t;
 constexpr int wg_vmcnt(int n) { return (n & 0xF) | (((n >> 4) & 3) << 14) | (0x7 << 4) | (0xF << 8); }
 constexpr int wg_lgkm0() { return 0xF | (0x3 << 14) | (0x7 << 4); }
 
-// LDS operand layout: KG groups of 32 K values; group g holds the tile's 128
-// rows x 64 bytes at g * 8 KB, row r's four 16-byte chunks XOR-swizzled by
-// (r / 4) % 4 so that a fragment read of 32 consecutive rows hits every bank
-// group evenly.
-__device__ __forceinline__ int wg_pos(int g, int row, int chunk) {
-  return g * (kWgradTile * 64) + row * 64 + ((chunk ^ ((row >> 2) & 3)) << 4);
-}
+// Byte of value (K-row r, column n) in an operand image of ROWK bytes per
+// K-row.  The swizzle makes a transposing read, which takes 64 bytes from each
+// of K-rows 0-3 and 8-11 of a 16-row group, hit distinct banks.
+template <int ROWK>
+__device__ __forceinline__ int wk_sw(int r) { return (4 * (r & 3) + 16 * ((r >> 3) & 1)) & (ROWK / 16 - 1); }
+template <int ROWK>
+__device__ __forceinline__ int wk_pos(int r, int n) { return r * ROWK + (((n >> 3) ^ wk_sw<ROWK>(r)) << 4) + (n & 7) * 2; }
 
-// LDS-DMA of the [128, K] row slice at `blk` (row stride K elements) into an
-// operand buffer.  Group g is 8 instructions of 1 KB; wave w of NWAVE issues
-// instructions w, w + NWAVE, ...  Instruction i lands rows 16 i .. 16 i + 15:
-// lane l takes row 16 i + l / 4 and the global chunk (l % 4) ^ ((l / 16) % 4),
-// its row's swizzle, so one per-lane byte offset serves every instruction.
-template <int KG, int NWAVE>
-__device__ __forceinline__ void wg_dma(const char* blk, int K, char* buf, int wave, uint32_t lane_off) {
-#pragma unroll
-  for (int g = 0; g < KG; ++g) {
-#pragma unroll
-    for (int ii = 0; ii < 8 / NWAVE; ++ii) {
-      const int inst = wave + NWAVE * ii;
-      const char* src = blk + ((int64_t)inst * 16 * K * 2 + g * 64) + lane_off;
-      __builtin_amdgcn_global_load_lds((const void*)src,
-                                       (wg_lds_void_t*)(buf + g * (kWgradTile * 64) + inst * 1024), 16, 0, 0);
-    }
-  }
+// Two MFMA fragments (32 columns x 16 K each) from an operand image:
+// lane l = 16 g + q reads 4 columns of K-row rb (rb = 8 (g / 2) + q / 4) at
+// LDS byte p (K-rows 0-3 / 8-11) and p + 4 ROWK (K-rows 4-7 / 12-15); the
+// transposing read hands it column l % 32 of K values 8 (l / 32) .. + 7.
+// The reads wait for themselves (lgkmcnt 0) in the same asm block: through
+// the builtin, which carries no alias information, the compiler would wait
+// for every LDS-DMA and store in flight first.
+template <int ROWK, int OFF>
+__device__ __forceinline__ void wk_read2(uint32_t p0, uint32_t p1, u32x4& f0, u32x4& f1) {
+  u32x2 r00, r01, r10, r11;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4 offset:%6\n\t"
+      "ds_read_b64_tr_b16 %1, %4 offset:%7\n\t"
+      "ds_read_b64_tr_b16 %2, %5 offset:%6\n\t"
+      "ds_read_b64_tr_b16 %3, %5 offset:%7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r00), "=&v"(r01), "=&v"(r10), "=&v"(r11)
+      : "v"(p0), "v"(p1), "i"(OFF), "i"(OFF + 4 * ROWK));
+  f0 = u32x4{r00[0], r00[1], r01[0], r01[1]};
+  f1 = u32x4{r10[0], r10[1], r11[0], r11[1]};
 }
 
 // Staged output tile: 256 rows of 256 bytes, 16-byte chunk c of row r at
 // chunk c ^ (r % 16).
 __device__ __forceinline__ int wg_spos(int row, int chunk) { return row * 256 + ((chunk ^ (row & 15)) << 4); }
 
-template <typename TO, int KG>
-__device__ __forceinline__ void wgrad_strip(const char* a_blk, const char* b_blk, int K, int N, char* out,
-                                            int64_t ldo, char* smem) {
+// Operand rows of one expert: row k (< cnt) at base + row(k) * ld bytes,
+// row(k) = off + k, or order[off + k] / top_k when gathered.
+struct WgRows {
+  const char* base;
+  int64_t ld;
+  const int32_t* order;  // NULL: rows in sorted pair order
+  int top_k;
+  __device__ __forceinline__ const char* row(int off, int k) const {
+    const int64_t r = order ? (int64_t)(order[off + k] / top_k) : (int64_t)(off + k);
+    return base + r * ld;
+  }
+};
+
+template <typename TB, typename TO, int KG>
+__device__ __forceinline__ void wgrad_strip(const WgRows A, const WgRows B, int off, int cnt, int m0, int N,
+                                            char* out, int64_t ldo, char* smem) {
   constexpr int NWAVE = kWgradWaves, NTHR = kWgradThreads;
   constexpr int KS = 2 * KG;              // MFMA K steps of 16
-  constexpr int kDma = KG * (8 / NWAVE);  // DMA instructions per wave per 128-row block
+  constexpr int KP = 32 * KG;             // padded K (pair rows)
+  constexpr int kDma = KG * (8 / NWAVE);  // DMA instructions per wave for a B tile (the A strip: 2 kDma)
+  constexpr int ROWA = 2 * kWgradStrip, ROWB = 2 * kWgradTile;  // bytes per K-row of the images
+  constexpr bool kWidenB = __is_same(TB, bf16_t);
   // (the wave index is uniform: readfirstlane keeps the DMA destinations scalar)
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // waves 4 (rows) x 2 (columns): 64 x 64 of the tile each
-  const int wm = wave >> 1, wn = wave & 1, lr = lane & 31, lh = lane >> 5;
+  const int wm = wave >> 1, wn = wave & 1;
   const int NT = N / kWgradTile;
   auto bbuf = [&](int t) { return smem + (t & 1) * kWgradBuf; };  // column tile t's B buffer
   char* const S = smem + 2 * kWgradBuf;                           // staged output tile
-  auto b_tile = [&](int t) { return b_blk + (int64_t)t * kWgradTile * K * 2; };
-  const uint32_t lane_off = (uint32_t)((lane >> 2) * K * 2 + (((lane & 3) ^ ((lane >> 4) & 3)) << 4));
+  char* const Aimg = bbuf(1);  // the A strip: KP K-rows of 512 bytes over B buffer 1 and the staging buffer
+  typedef __attribute__((address_space(3))) const char* lds_cptr;
+  auto lds_addr = [](const char* p) -> uint32_t { return (uint32_t)(size_t)(lds_cptr)p; };
 
-  // the A strip's two 128-row blocks into B buffer 1 and the staging buffer
-  // (contiguous), B tile 0 into B buffer 0; then the strip into registers
-  wg_dma<KG, NWAVE>(a_blk, K, bbuf(1), wave, lane_off);
-  wg_dma<KG, NWAVE>(a_blk + (int64_t)kWgradTile * K * 2, K, bbuf(1) + kWgradBuf, wave, lane_off);
-  wg_dma<KG, NWAVE>(b_tile(0), K, bbuf(0), wave, lane_off);
+  // DMA plan.  Instruction i of an image fills its bytes [1024 i, +1024):
+  // lane l lands at byte 16 l, i.e. K-row (1024 i + 16 l) / ROWK and physical
+  // chunk (16 l % ROWK) / 16, and fetches the logical chunk swizzled there.
+  // K-rows past the expert's pairs reload its last pair row.  Wave w issues
+  // instructions w, w + 8, ...
+  // B tile: K-row 4 i + l / 16; its swizzle depends on (l / 16) % 4 only.
+  const int bchunk = ((lane & 15) ^ (4 * ((lane >> 4) & 3))) * 16;
+  const char* brow[kDma];
+#pragma unroll
+  for (int ii = 0; ii < kDma; ++ii) brow[ii] = B.row(off, min(4 * (wave + NWAVE * ii) + (lane >> 4), cnt - 1)) + bchunk;
+  auto dma_b = [&](int t, char* buf) {
+#pragma unroll
+    for (int ii = 0; ii < kDma; ++ii)
+      __builtin_amdgcn_global_load_lds((const void*)(brow[ii] + (int64_t)t * (kWgradTile * 2)),
+                                       (wg_lds_void_t*)(buf + (wave + NWAVE * ii) * 1024), 16, 0, 0);
+  };
+  // the A strip (K-row 2 i + l / 32), then B tile 0; then the strip into registers
+#pragma unroll
+  for (int ii = 0; ii < 2 * kDma; ++ii) {
+    const int inst = wave + NWAVE * ii, r = 2 * inst + (lane >> 5);
+    const int c = (lane & 31) ^ wk_sw<ROWA>(r);
+    const char* src = A.row(off, min(r, cnt - 1)) + (int64_t)(m0 + 8 * c) * 2;
+    __builtin_amdgcn_global_load_lds((const void*)src, (wg_lds_void_t*)(Aimg + inst * 1024), 16, 0, 0);
+  }
+  dma_b(0, bbuf(0));
   __builtin_amdgcn_s_waitcnt(wg_vmcnt(kDma));  // issued after the strip: B tile 0 only
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
+  // the padded K-rows of the strip become zeros (they multiply the repeated B rows)
+  {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (int id = tid; id < (KP - cnt) * (ROWA / 16); id += NTHR) *(u32x4*)(Aimg + cnt * ROWA + id * 16) = z;
+  }
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(wg_lgkm0());
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  // fragment addresses: K-row rb of columns c0 + 16 (g % 2) + 4 (q % 4) (the
+  // swizzle of K-row 16 s + rb (+ 4) equals that of rb)
+  const int rb = 8 * (lane >> 5) + ((lane >> 2) & 3);
+  const int cl = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   u32x4 fa[KS][2];
   {
-    const char* Ab = bbuf(1) + (wm >> 1) * kWgradBuf;  // this wave's 64 rows lie in one block
+    const uint32_t a0 = lds_addr(Aimg + wk_pos<ROWA>(rb, wm * 64 + cl));
+    const uint32_t a1 = lds_addr(Aimg + wk_pos<ROWA>(rb, wm * 64 + 32 + cl));
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        fa[s][i] = *(const u32x4*)(Ab + wg_pos(s >> 1, (wm & 1) * 64 + i * 32 + lr, 2 * (s & 1) + lh));
+    for (int s = 0; s < KS; ++s) wk_read2<ROWA, 0>(a0 + s * 16 * ROWA, a1 + s * 16 * ROWA, fa[s][0], fa[s][1]);
   }
+  const uint32_t b0 = lds_addr(smem + wk_pos<ROWB>(rb, wn * 64 + cl));
+  const uint32_t b1 = lds_addr(smem + wk_pos<ROWB>(rb, wn * 64 + 32 + cl));
 
   // The MFMAs take the B fragment first, so each 32 x 32 accumulator holds
-  // the transposed sub-tile: lane l has output row lr and columns
-  // 8 (v / 4) + 4 lh + v % 4, i.e. four runs of four consecutive columns,
-  // each staged with one 8-byte LDS write.
+  // the transposed sub-tile: lane l has output row l % 32 and columns
+  // 8 (v / 4) + 4 (l / 32) + v % 4, i.e. four runs of four consecutive
+  // columns, each staged with one 8-byte LDS write.
+  const int lr = lane & 31, lh = lane >> 5;
   constexpr int kStores = kWgradStrip * 256 / 16 / NTHR;  // 16-byte stores per thread per tile
   for (int t = 0; t < NT; ++t) {
-    const char* const B = bbuf(t);
+    const uint32_t bofs = (t & 1) * kWgradBuf;
     // B tile t has landed (issued after it: the stores of tile t-1, none
     // before tile 0), and every wave is done reading the A strip or the
     // staged tile t-1 and B tile t-1: B tile t+1 may stream into the other
@@ -118,7 +182,7 @@ __device__ __forceinline__ void wgrad_strip(const char* a_blk, const char* b_blk
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (t + 1 < NT) wg_dma<KG, NWAVE>(b_tile(t + 1), K, bbuf(t + 1), wave, lane_off);
+    if (t + 1 < NT) dma_b(t + 1, bbuf(t + 1));
     f32x16 acc[2][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -126,18 +190,32 @@ __device__ __forceinline__ void wgrad_strip(const char* a_blk, const char* b_blk
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      u32x4 fb[2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) fb[j] = *(const u32x4*)(B + wg_pos(s >> 1, wn * 64 + j * 32 + lr, 2 * (s & 1) + lh));
+    // step s's MFMAs are issued before step s + 1's fragment reads, whose
+    // wait then overlaps them
+    u32x4 fb[2][2];
+    auto read_b = [&](auto s_c, u32x4* f) {
+      constexpr int s = decltype(s_c)::value;
+      wk_read2<ROWB, s * 16 * ROWB>(b0 + bofs, b1 + bofs, f[0], f[1]);
+      if constexpr (kWidenB) {
+        f[0] = bf16x8_to_f16x8(f[0]);
+        f[1] = bf16x8_to_f16x8(f[1]);
+      }
+    };
+    read_b(IntC<0>{}, fb[0]);
+    sfor<KS>([&](auto s_c) {
+      constexpr int s = decltype(s_c)::value;
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, fb[j]),
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, fb[s & 1][j]),
                                                              __builtin_bit_cast(f16x8, fa[s][i]), acc[i][j], 0, 0, 0);
-    }
+      if constexpr (s + 1 < KS) {
+        __builtin_amdgcn_sched_barrier(0);
+        read_b(IntC<s + 1>{}, fb[(s + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    });
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int row = wm * 64 + i * 32 + lr;
@@ -169,27 +247,33 @@ __device__ __forceinline__ void wgrad_strip(const char* a_blk, const char* b_blk
   __builtin_amdgcn_s_waitcnt(wg_vmcnt(0));
 }
 
-template <typename TI, typename TO>
-__global__ __launch_bounds__(kWgradThreads) void wgrad_kernel(const TI* __restrict__ a, const TI* __restrict__ b,
-                                                    const int32_t* __restrict__ kr_off,
-                                                    const int32_t* __restrict__ kr_len, int M, int N,
+// dW[e] = A_e^T B_e for every expert e (grid: experts x M / 256 strips).
+// a: pair rows of M values (row stride lda bytes), b: rows of N values (ldb
+// bytes), gathered through b_order / top_k when b_order is not NULL.
+template <typename TA, typename TB, typename TO>
+__global__ __launch_bounds__(kWgradThreads) void wgrad_kernel(const TA* __restrict__ a, int64_t lda,
+                                                    const TB* __restrict__ b, int64_t ldb,
+                                                    const int32_t* __restrict__ b_order, int top_k,
+                                                    const int32_t* __restrict__ counts,
+                                                    const int32_t* __restrict__ offsets, int M, int N,
                                                     TO* __restrict__ out) {
-  static_assert(sizeof(TI) == 2 && sizeof(TO) == 2, "16-bit operands and output");
+  static_assert(__is_same(TA, f16_t) && sizeof(TB) == 2 && sizeof(TO) == 2, "fp16 A, 16-bit B and output");
   __shared__ __attribute__((aligned(1024))) char smem[kWgradLds];
   const int strips = M / kWgradStrip;
   // the strips of one expert are neighbours on one XCD: they share B_e in its L2
   const int L = xcd_contiguous_id(blockIdx.x, gridDim.x);
   const int e = L / strips, ms = L % strips;
-  const int K = kr_len[e];
+  const int cnt = counts[e], off = offsets[e];
   const int64_t ldo = (int64_t)N * 2;
   char* o = (char*)(out + ((int64_t)e * M + (int64_t)ms * kWgradStrip) * N);
-  const char* ab = (const char*)(a + (int64_t)kr_off[e] * M + (int64_t)ms * kWgradStrip * K);
-  const char* bb = (const char*)(b + (int64_t)kr_off[e] * N);
-  switch (K) {
-    case 64: wgrad_strip<TO, 2>(ab, bb, K, N, o, ldo, smem); break;
-    case 128: wgrad_strip<TO, 4>(ab, bb, K, N, o, ldo, smem); break;
-    case 192: wgrad_strip<TO, 6>(ab, bb, K, N, o, ldo, smem); break;
-    default: {  // no pairs: a zero gradient (K above the maximum never reaches here)
+  const WgRows A{(const char*)a, lda, nullptr, 1};
+  const WgRows B{(const char*)b, ldb, b_order, top_k};
+  const int m0 = ms * kWgradStrip;
+  switch ((cnt + 63) / 64) {
+    case 1: wgrad_strip<TB, TO, 2>(A, B, off, cnt, m0, N, o, ldo, smem); break;
+    case 2: wgrad_strip<TB, TO, 4>(A, B, off, cnt, m0, N, o, ldo, smem); break;
+    case 3: wgrad_strip<TB, TO, 6>(A, B, off, cnt, m0, N, o, ldo, smem); break;
+    default: {  // no pairs: a zero gradient (more than kWgradKMax never reaches here)
       const u32x4 z = {0u, 0u, 0u, 0u};
       const int chunks = N / 8;  // 16-byte chunks per row
       for (int id = threadIdx.x; id < kWgradStrip * chunks; id += kWgradThreads)
