@@ -80,7 +80,6 @@ lmoe_status routed_recompute(const Plan& p, const lmoe_dims* dm, const void* z, 
   const int64_t P = p.pairs;
   const int f = p.fr, l = p.l, R = p.R;
   const int64_t es = sizeof(T), ei = sizeof(TI);
-  auto blocks = [](int64_t n) { return (unsigned)std::min<int64_t>((n + 255) / 256, 65536); };
   // 1. bookkeeping: counts, offsets, stable order, C, tile list, inverse order, padded K ranges
   LMOE_TRY(run_dispatch(p, ids, w.chunk_hist, w.chunk_bad, w.counts, w.offsets, w.order, w.meta, st));
   tile_list_kernel<<<1, 1024, 0, st>>>(w.counts, R, p.tile_m, w.tile_list, w.meta);
@@ -99,14 +98,17 @@ lmoe_status routed_recompute(const Plan& p, const lmoe_dims* dm, const void* z, 
                      int K, void* out, int64_t ldo) {
     return routed_grouped(p, dm, w, a, lda, bw, ldb, bstride, nrows, K, out, ldo);
   };
-  // 2. pre-activations of every pair: g = z W_g^T, up = z W_u^T (fp32, sorted rows)
+  // 2. pre-activations of every pair, g = z W_g^T and up = z W_u^T (fp32,
+  // sorted rows), and the hidden h from one dual (gate, up) product
   const int64_t ez = sizeof(TZ);
-  LMOE_TRY((gemm<TZ, T, float, A_GATHER, B_SINGLE, E_STORE>(
-      grouped(z, l * ez, w_g, l * es, (int64_t)f * l * es, f, l, w.g, (int64_t)f * 4), tile, st)));
-  LMOE_TRY((gemm<TZ, T, float, A_GATHER, B_SINGLE, E_STORE>(
-      grouped(z, l * ez, w_u, l * es, (int64_t)f * l * es, f, l, w.up, (int64_t)f * 4), tile, st)));
-  situ_hidden_kernel<TI><<<blocks(P * f), 256, 0, st>>>(w.g, w.up, P * f, dm->beta1, dm->beta2, (TI*)w.hs);
-  LMOE_HIP(hipGetLastError());
+  {
+    GemmArgs g = grouped(z, l * ez, w_g, l * es, (int64_t)f * l * es, f, l, w.hs, (int64_t)f * ei);
+    g.b1 = (const char*)w_u;
+    g.pre_g = (char*)w.g;
+    g.pre_u = (char*)w.up;
+    g.pre_ld = (int64_t)f * 4;
+    LMOE_TRY((gemm<TZ, T, TI, A_GATHER, B_DUAL, E_PRE>(g, tile, st)));
+  }
   if (!want_o) return LMOE_OK;
   // 3. expert outputs o = h W_o^T (fp32, sorted rows)
   return gemm<TI, T, float, A_SORTED, B_SINGLE, E_STORE>(
@@ -287,13 +289,13 @@ lmoe_status run_layer_backward(const Plan& p, const lmoe_dims* dm, const lmoe_we
   combine_rmsnorm_kernel<float, TI><<<(unsigned)N, 256, 0, st>>>(w.u, 1, l, nullptr, W->rms_w, dm->rms_eps,
                                                                  (TI*)w.rn, l, nullptr);
   LMOE_HIP(hipGetLastError());
-  if (nsf > 0) {
-    LMOE_TRY((gemm<T, T, float, A_DENSE, B_SINGLE, E_STORE>(
-        dense(x, d * es, (int)N, W->sh_g, d * es, nsf, d, w.ag, (int64_t)nsf * 4), dense_tile(N, nsf, false), st)));
-    LMOE_TRY((gemm<T, T, float, A_DENSE, B_SINGLE, E_STORE>(
-        dense(x, d * es, (int)N, W->sh_u, d * es, nsf, d, w.au, (int64_t)nsf * 4), dense_tile(N, nsf, false), st)));
-    situ_hidden_kernel<TI><<<blocks(N * nsf), 256, 0, st>>>(w.ag, w.au, N * nsf, dm->beta1, dm->beta2, (TI*)w.hs);
-    LMOE_HIP(hipGetLastError());
+  if (nsf > 0) {  // the shared pre-activations (fp32) and hidden from one dual (gate, up) product
+    GemmArgs g = dense(x, d * es, (int)N, W->sh_g, d * es, nsf, d, w.hs, (int64_t)nsf * ei);
+    g.b1 = (const char*)W->sh_u;
+    g.pre_g = (char*)w.ag;
+    g.pre_u = (char*)w.au;
+    g.pre_ld = (int64_t)nsf * 4;
+    LMOE_TRY((gemm<T, T, TI, A_DENSE, B_DUAL, E_PRE>(g, dense_tile(N, nsf, true), st)));
   }
   // ---- step 5 backward: dr = dy W_up, dh_shared = dy [S_o^j], RMSNorm backward
   LMOE_TRY(transpose_batched<T>((const T*)W->w_up, 0, l, d, l, (T*)w.w_upT, 0, d, 0, 1, nullptr, st));

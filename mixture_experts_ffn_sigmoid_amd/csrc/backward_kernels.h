@@ -198,16 +198,6 @@ __global__ __launch_bounds__(256) void segment_transpose16_kernel(
   }
 }
 
-// h = SiTU hidden of the (gate, up) pre-activations, n elements.
-template <typename TD>
-__global__ __launch_bounds__(256) void situ_hidden_kernel(const float* __restrict__ g, const float* __restrict__ u,
-                                                          int64_t n, float beta1, float beta2,
-                                                          TD* __restrict__ h) {
-  const float ib1 = 1.0f / beta1, ib2 = 1.0f / beta2;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
-    Elem<TD>::store(h + i, situ_hidden(g[i], u[i], beta1, beta2, ib1, ib2));
-}
-
 // Pair gradients from v = W_o^T du (the product of du's row with the pair's
 // W_o, one row per sorted pair q', q = order[q'], token n = q / k):
 //   dprobs[q] = <v[q'], h[q']>  (= <du[n], W_o h[q']>, the pair's output o

@@ -37,6 +37,8 @@
 //             (ds_read_b64_tr_b16); 16-bit operands only
 //   E_STORE   plain store (fp32 or storage dtype), masked to valid rows/cols
 //   E_SITU    SiTU-GLU hidden of the (gate, up) accumulator pair, stored as OutT
+//   E_PRE     E_SITU that also stores the gate and up accumulators themselves
+//             (fp32 pre-activations at pre_g / pre_u, rows like the hidden's)
 //   E_SLOTS   p-weighted result of sorted pair q written to its own slot row q
 // Runtime options (A_DENSE with E_STORE):
 //   split K (ksplit > 1): the grid also runs over K slices of kslice steps,
@@ -54,7 +56,7 @@ namespace lmoe {
 
 enum { A_DENSE = 0, A_GATHER = 1, A_PADDED = 2, A_SORTED = 3, A_KBATCH = 4 };
 enum { B_SINGLE = 0, B_DUAL = 1, B_KSEG = 2, B_KMAJOR = 3 };
-enum { E_STORE = 0, E_SITU = 1, E_SLOTS = 2 };
+enum { E_STORE = 0, E_SITU = 1, E_SLOTS = 2, E_PRE = 3 };
 
 constexpr int kMaxSeg = 17;
 constexpr int kSegUnit = 64;  // B_KSEG segment boundaries are given in 64-byte units of K
@@ -117,6 +119,10 @@ struct GemmArgs {
   int64_t ldo;  // bytes (E_SLOTS: fp32 elements per slot row * 4)
   const float* probs;
   float beta1, beta2;
+  // E_PRE: fp32 gate / up pre-activations, row stride pre_ld bytes
+  char* pre_g;
+  char* pre_u;
+  int64_t pre_ld;
   // E_STORE / E_SLOTS with fp16 output: set to 1 when a stored value leaves
   // fp16's range (|v| >= 65520 rounds to inf) or is NaN (NULL: no check)
   int32_t* range_flag;
@@ -777,7 +783,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
   const int col0 = BMODE == B_DUAL ? nt * (BN / 2) + wn * (WTN / 2) : nt * BN + wn * WTN;
 
   auto value = [&](int i, int j, int v) -> float {
-    if constexpr (EMODE == E_SITU)
+    if constexpr (EMODE == E_SITU || EMODE == E_PRE)
       return situ_hidden(acc[i][j][v], acc[i][j + TN / 2][v], args.beta1, args.beta2, inv_b1, inv_b2);
     else
       return acc[i][j][v];
@@ -787,7 +793,25 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
     else return GROUPED ? off + m0 + r : (int64_t)(m0 + r);
   };
 
-  constexpr bool kRangeCheck = EMODE != E_SITU && __is_same(OutT, f16_t);
+  constexpr bool kRangeCheck = EMODE != E_SITU && EMODE != E_PRE && __is_same(OutT, f16_t);
+  if constexpr (EMODE == E_PRE) {
+    static_assert(BMODE == B_DUAL, "pre-activations of a (gate, up) pair");
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int col = col0 + j * 32 + lr;
+        if (col >= args.N) continue;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int r = wm * WTM + i * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
+          if (r >= rows_valid) continue;
+          const int64_t o = out_row(r) * args.pre_ld + (int64_t)col * 4;
+          *(float*)(args.pre_g + o) = acc[i][j][v];
+          *(float*)(args.pre_u + o) = acc[i][j + TN / 2][v];
+        }
+      }
+  }
   bool out_of_range = false;
   if constexpr (kStaged) {
     asm volatile("" ::: "memory");
