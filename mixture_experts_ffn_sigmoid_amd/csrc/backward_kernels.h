@@ -214,11 +214,44 @@ __global__ __launch_bounds__(256) void pair_vh_kernel(const float* __restrict__ 
   const float pq = probs[q];
   const float* vrow = v + qs * f;
   const TD* hrow = h + qs * f;
-  float acc = 0.f;
-  for (int c = threadIdx.x; c < f; c += 256) acc += vrow[c] * Elem<TD>::load(hrow + c);
   const float* dur = du + (int64_t)(q / top_k) * ell;
   TD* drow = dout + qs * ell;
-  for (int c = threadIdx.x; c < ell; c += 256) Elem<TD>::store(drow + c, pq * dur[c]);
+  float acc = 0.f;
+  // uniform: four values per thread and access (rows stay aligned; v, h and
+  // dout are workspace buffers, du the caller's)
+  if ((f & 3) == 0 && (ell & 3) == 0 && (((uintptr_t)du) & 15) == 0) {
+    for (int c = 4 * (int)threadIdx.x; c < f; c += 4 * 256) {
+      const f32x4 vv = *(const f32x4*)(vrow + c);
+      TD hv[4];
+      if constexpr (sizeof(TD) == 2) {
+        const u32x2 w = *(const u32x2*)(hrow + c);
+        __builtin_memcpy(hv, &w, 8);
+      } else {
+        const f32x4 w = *(const f32x4*)(hrow + c);
+        __builtin_memcpy(hv, &w, 16);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc += vv[j] * Elem<TD>::load(&hv[j]);
+    }
+    for (int c = 4 * (int)threadIdx.x; c < ell; c += 4 * 256) {
+      const f32x4 dv = *(const f32x4*)(dur + c);
+      TD ov[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) Elem<TD>::store(&ov[j], pq * dv[j]);
+      if constexpr (sizeof(TD) == 2) {
+        u32x2 w;
+        __builtin_memcpy(&w, ov, 8);
+        *(u32x2*)(drow + c) = w;
+      } else {
+        f32x4 w;
+        __builtin_memcpy(&w, ov, 16);
+        *(f32x4*)(drow + c) = w;
+      }
+    }
+  } else {
+    for (int c = threadIdx.x; c < f; c += 256) acc += vrow[c] * Elem<TD>::load(hrow + c);
+    for (int c = threadIdx.x; c < ell; c += 256) Elem<TD>::store(drow + c, pq * dur[c]);
+  }
   __shared__ float red[4];
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
