@@ -424,6 +424,41 @@ def small_workloads(names, steps: int, warmup: int, cpu: bool) -> dict:
     return out
 
 
+def library_dense(cfg, steps: int, warmup: int) -> dict:
+    """The layer's three large dense products as plain library GEMMs
+    (torch.mm on ROCm = hipBLASLt), bf16 in and out, fp32 accumulation,
+    no epilogue: shared gate/up x [S_g; S_u]^T, the merge [h_sh | u] [S_o |
+    W_up]^T and the latent x W_down^T, at the workload's shapes.  A
+    comparison for the fused kernels' step times, not part of the layer."""
+    import torch
+
+    N, d, l, fs, ns = cfg.n_tokens, cfg.d_model, cfg.d_latent, cfg.ff_shared, cfg.n_shared
+    g = torch.Generator(device="cuda").manual_seed(0)
+    shapes = {"shared_gateup": (N, d, 2 * ns * fs), "merge_gemm": (N, ns * fs + l, d), "latent_gemm": (N, d, l)}
+    out = {}
+    for name, (m, k, n) in shapes.items():
+        a = torch.randn((m, k), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+        b = (torch.randn((n, k), generator=g, device="cuda", dtype=torch.float32) / k ** 0.5).to(torch.bfloat16)
+        c = torch.empty((m, n), device="cuda", dtype=torch.bfloat16)
+        bt = b.t()  # nn.Linear layout: C = A B^T
+        for _ in range(warmup):
+            torch.mm(a, bt, out=c)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            torch.mm(a, bt, out=c)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        fl = 2.0 * m * n * k
+        out[name] = {"m": m, "n": n, "k": k, "ms": round(ms, 4), "tflops": round(fl / ms / 1e9, 1),
+                     "mfma_frac": round(fl / ms / 1e9 / PEAK_MFMA_TFLOPS["bf16"], 4)}
+        del a, b, c, bt
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -438,9 +473,15 @@ def main():
                     help="skip the toy / 0.5b / skewed 0.5b layers measured after the prefill workload")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 1 GiB device copy (FETCH_SIZE / WRITE_SIZE calibration)")
+    ap.add_argument("--library-dense", action="store_true",
+                    help="only time the workload's three large dense products as plain library (hipBLASLt) GEMMs")
     args = ap.parse_args()
     if args.calibrate_copy:
         copy_calibration()
+        return
+    if args.library_dense:
+        print(json.dumps({"workload": args.workload, "library_dense": library_dense(
+            S.CONFIGS[args.workload], args.steps, args.warmup)}), flush=True)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
