@@ -278,7 +278,9 @@ lmoe_status latentmoe_routed_backward(const lmoe_dims* dims, const void* z, cons
  * [N, k] as returned by latentmoe_forward for this x.  Outputs: dx [N, d]
  * fp32 and every parameter gradient in `grads` (storage dtype, rms_w fp32;
  * fp32 accumulation, one rounding).  The forward quantities (z, u, the shared
- * pre-activations) are recomputed.  Reads C back once; otherwise
+ * pre-activations) are recomputed; u is formed as the forward forms it (the
+ * p-weighted expert outputs held in the intermediate type, summed in slot
+ * order).  Reads C back once; otherwise
  * asynchronous.  Workspace: latentmoe_workspace_bytes(dims,
  * LMOE_ENTRY_BACKWARD) bytes of device memory.  Errors: INVALID_ARGUMENT for
  * bad dims, NULL pointers or ids outside [0, R); WORKSPACE. */

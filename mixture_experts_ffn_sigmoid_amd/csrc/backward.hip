@@ -68,15 +68,13 @@ GemmArgs routed_grouped(const Plan& p, const lmoe_dims* dm, const RoutedBwdWs& w
 Tile routed_tile(const Plan& p) { return p.tile_m == 64 ? TILE_V : p.tile_m == 128 ? TILE_M : TILE_W; }
 
 // Forward part of the routed-block backward: the dispatch bookkeeping, the
-// pre-activations g = z W_g^T and up = z W_u^T (fp32), the hidden h (TI) and,
-// with want_o, the expert outputs o = h W_o^T (fp32; the layer backward needs
-// them for u), all in sorted pair order.  Returns the capacity C (one host
-// read-back).  T: storage type of the weights; TI: intermediate type; TZ:
-// type of z.
+// pre-activations g = z W_g^T and up = z W_u^T (fp32) and the hidden h (TI),
+// in sorted pair order.  Returns the capacity C (one host read-back).  T:
+// storage type of the weights; TI: intermediate type; TZ: type of z.
 template <typename T, typename TI, typename TZ>
 lmoe_status routed_recompute(const Plan& p, const lmoe_dims* dm, const void* z, const int32_t* ids,
-                             const void* w_g, const void* w_u, const void* w_o, const RoutedBwdWs& w,
-                             int* C_out, hipStream_t st, bool want_o) {
+                             const void* w_g, const void* w_u, const RoutedBwdWs& w, int* C_out,
+                             hipStream_t st) {
   const int64_t P = p.pairs;
   const int f = p.fr, l = p.l, R = p.R;
   const int64_t es = sizeof(T), ei = sizeof(TI);
@@ -101,18 +99,12 @@ lmoe_status routed_recompute(const Plan& p, const lmoe_dims* dm, const void* z, 
   // 2. pre-activations of every pair, g = z W_g^T and up = z W_u^T (fp32,
   // sorted rows), and the hidden h from one dual (gate, up) product
   const int64_t ez = sizeof(TZ);
-  {
-    GemmArgs g = grouped(z, l * ez, w_g, l * es, (int64_t)f * l * es, f, l, w.hs, (int64_t)f * ei);
-    g.b1 = (const char*)w_u;
-    g.pre_g = (char*)w.g;
-    g.pre_u = (char*)w.up;
-    g.pre_ld = (int64_t)f * 4;
-    LMOE_TRY((gemm<TZ, T, TI, A_GATHER, B_DUAL, E_PRE>(g, tile, st)));
-  }
-  if (!want_o) return LMOE_OK;
-  // 3. expert outputs o = h W_o^T (fp32, sorted rows)
-  return gemm<TI, T, float, A_SORTED, B_SINGLE, E_STORE>(
-      grouped(w.hs, f * ei, w_o, f * es, (int64_t)l * f * es, l, f, w.o, (int64_t)l * 4), tile, st);
+  GemmArgs g = grouped(z, l * ez, w_g, l * es, (int64_t)f * l * es, f, l, w.hs, (int64_t)f * ei);
+  g.b1 = (const char*)w_u;
+  g.pre_g = (char*)w.g;
+  g.pre_u = (char*)w.up;
+  g.pre_ld = (int64_t)f * 4;
+  return gemm<TZ, T, TI, A_GATHER, B_DUAL, E_PRE>(g, tile, st);
 }
 
 // Gradient part of the routed-block backward, on the quantities
@@ -173,7 +165,7 @@ lmoe_status routed_gradients(const Plan& p, const lmoe_dims* dm, const void* z, 
                 (int64_t)l * 4),
         tile, st)));
   }
-  pair_sum_kernel<TDZ><<<(unsigned)p.N, 256, 0, st>>>(dzrows, w.inv, p.k, l, nullptr, (TDZ*)dz, ld_dz);
+  pair_sum_kernel<TDZ><<<(unsigned)p.N, 256, 0, st>>>(dzrows, w.inv, p.k, l, (TDZ*)dz, ld_dz);
   LMOE_HIP(hipGetLastError());
   // 6. weight gradients: per expert, products over its pairs.  Up to
   // kWgradKMax pairs per expert, with 16-bit operands and 256-multiple
@@ -243,7 +235,7 @@ lmoe_status run_routed_backward(const Plan& p, const lmoe_dims* dm, const void* 
                                 const float* du, void* dz, int64_t ld_dz, float* dprobs, void* dw_g,
                                 void* dw_u, void* dw_o, const RoutedBwdWs& w, hipStream_t st) {
   int C = 0;
-  LMOE_TRY((routed_recompute<T, TI, TZ>(p, dm, z, ids, w_g, w_u, w_o, w, &C, st, /*want_o=*/false)));
+  LMOE_TRY((routed_recompute<T, TI, TZ>(p, dm, z, ids, w_g, w_u, w, &C, st)));
   return routed_gradients<T, TI, TZ, TDZ>(p, dm, z, probs, w_g, w_u, w_o, du, dz, ld_dz, dprobs, dw_g, dw_u,
                                           dw_o, w, C, st);
 }
@@ -278,16 +270,24 @@ lmoe_status run_layer_backward(const Plan& p, const lmoe_dims* dm, const lmoe_we
                                                        dense_tile(N, l, false), st)));
   LMOE_TRY((gemm<T, T, float, A_DENSE, B_SINGLE, E_STORE>(
       dense(x, d * es, (int)N, W->w_router, d * es, R, d, w.logits, (int64_t)R * 4), dense_tile(N, R, false), st)));
-  // the routed block's forward quantities (pre-activations, hidden, expert
-  // outputs), kept for its gradients below
+  // the routed block's forward quantities (pre-activations, hidden), kept
+  // for its gradients below
   const RoutedBwdWs& rw = w.rw;
   int C = 0;
-  LMOE_TRY((routed_recompute<T, TI, TI>(p, dm, w.z, ids, W->w_g, W->w_u, W->w_o, rw, &C, st, /*want_o=*/true)));
-  // u = sum over the token's pairs (slot order) of p o, then RMSNorm(u)
-  pair_sum_kernel<float><<<(unsigned)N, 256, 0, st>>>(rw.o, rw.inv, p.k, l, probs, w.u, l);
-  LMOE_HIP(hipGetLastError());
-  combine_rmsnorm_kernel<float, TI><<<(unsigned)N, 256, 0, st>>>(w.u, 1, l, nullptr, W->rms_w, dm->rms_eps,
-                                                                 (TI*)w.rn, l, nullptr);
+  LMOE_TRY((routed_recompute<T, TI, TI>(p, dm, w.z, ids, W->w_g, W->w_u, rw, &C, st)));
+  // u and RMSNorm(u) formed as the forward forms them: the down product
+  // writes each pair's p-weighted output (type TI) into the token's slot row
+  // (rw.o's space, free until the dz rows), the slots are summed in slot
+  // order into u (fp32, kept for the RMSNorm backward) and normalised
+  {
+    const Tile tile = routed_tile(p);
+    GemmArgs g = routed_grouped(p, dm, rw, rw.hs, (int64_t)p.fr * ei, W->w_o, (int64_t)p.fr * es,
+                                (int64_t)l * p.fr * es, l, p.fr, rw.o, (int64_t)l * ei);
+    g.probs = probs;
+    LMOE_TRY((gemm<TI, T, TI, A_SORTED, B_SINGLE, E_SLOTS>(g, tile == TILE_V ? TILE_V2 : tile, st)));
+  }
+  combine_rmsnorm_kernel<TI, TI><<<(unsigned)N, 256, 0, st>>>((const TI*)rw.o, p.k, l, w.u, W->rms_w,
+                                                              dm->rms_eps, (TI*)w.rn, l, nullptr);
   LMOE_HIP(hipGetLastError());
   if (nsf > 0) {  // the shared pre-activations (fp32) and hidden from one dual (gate, up) product
     GemmArgs g = dense(x, d * es, (int)N, W->sh_g, d * es, nsf, d, w.hs, (int64_t)nsf * ei);

@@ -313,20 +313,15 @@ __global__ __launch_bounds__(256) void inverse_order_kernel(const int32_t* __res
   if (i < pairs) inv[order[i]] = (int32_t)i;
 }
 
-// dz[n] (row stride ld) = sum over slots j (in slot order) of wts[n k + j] *
-// rows[inv[n k + j]] (wts NULL = ones), one workgroup per token; top_k <= 64.
-// 16-byte row loads where rows and ell allow them.
+// dz[n] (row stride ld) = sum over slots j (in slot order) of rows[inv[n k + j]],
+// one workgroup per token; top_k <= 64.  16-byte row loads where rows and
+// ell allow them.
 template <typename TD>
 __global__ __launch_bounds__(256) void pair_sum_kernel(const float* __restrict__ rows, const int32_t* __restrict__ inv,
-                                                       int top_k, int ell, const float* __restrict__ wts,
-                                                       TD* __restrict__ dz, int64_t ld) {
+                                                       int top_k, int ell, TD* __restrict__ dz, int64_t ld) {
   const int64_t n = blockIdx.x;
   __shared__ int64_t src[64];  // first element of each slot's row
-  __shared__ float wq[64];
-  if ((int)threadIdx.x < top_k) {
-    src[threadIdx.x] = (int64_t)inv[n * top_k + threadIdx.x] * ell;
-    wq[threadIdx.x] = wts ? wts[n * top_k + threadIdx.x] : 1.0f;
-  }
+  if ((int)threadIdx.x < top_k) src[threadIdx.x] = (int64_t)inv[n * top_k + threadIdx.x] * ell;
   __syncthreads();
   TD* out = dz + n * ld;
   if ((((uintptr_t)rows) & 15) == 0 && (ell & 3) == 0) {  // uniform
@@ -335,9 +330,8 @@ __global__ __launch_bounds__(256) void pair_sum_kernel(const float* __restrict__
 #pragma unroll 4
       for (int j = 0; j < top_k; ++j) {
         const f32x4 v = *(const f32x4*)(rows + src[j] + c);
-        const float w = wq[j];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[q] += w * v[q];
+        for (int q = 0; q < 4; ++q) acc[q] += v[q];
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q) Elem<TD>::store(out + c + q, acc[q]);
@@ -345,7 +339,7 @@ __global__ __launch_bounds__(256) void pair_sum_kernel(const float* __restrict__
   } else {
     for (int c = threadIdx.x; c < ell; c += 256) {
       float acc = 0.f;
-      for (int j = 0; j < top_k; ++j) acc += wq[j] * rows[src[j] + c];
+      for (int j = 0; j < top_k; ++j) acc += rows[src[j] + c];
       Elem<TD>::store(out + c, acc);
     }
   }

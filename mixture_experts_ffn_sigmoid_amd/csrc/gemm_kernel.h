@@ -116,7 +116,7 @@ struct GemmArgs {
   int64_t part_bytes;
   // out
   char* out;
-  int64_t ldo;  // bytes (E_SLOTS: fp32 elements per slot row * 4)
+  int64_t ldo;  // bytes per output row (E_SLOTS: per slot row)
   const float* probs;
   float beta1, beta2;
   // E_PRE: fp32 gate / up pre-activations, row stride pre_ld bytes

@@ -322,7 +322,7 @@ size_t carve_forward(const Plan& p, char* b, ForwardWs* w) {
 // of kr_len).
 struct RoutedBwdWs {
   int32_t *counts, *offsets, *order, *chunk_hist, *chunk_bad, *meta, *tile_list, *inv, *kr_off, *kr_len;
-  float *g, *up, *o, *dh;  // o also holds the dz rows once it is consumed; dh holds v = W_o^T du per pair
+  float *g, *up, *o, *dh;  // o: the layer backward's slot rows, then the dz rows; dh: v = W_o^T du per pair
   float* sp;               // probs of the sorted pairs
   char* du16;              // du in the intermediate type (16-bit operands of v)
   char *hs, *dout, *dgu;   // intermediate type
