@@ -39,7 +39,8 @@
  *    latentmoe_workspace_bytes(dims, entry) bytes; the library allocates no
  *    device memory.  Calls that share a workspace must be ordered on one
  *    stream.  The one state kept between calls: latentmoe_forward's
- *    overlapped path (N <= 2048, n_shared > 0) creates, on first use by a
+ *    overlapped path (n_shared > 0 and N d n_s f_s <= 2048 * 7168 * 18432, i.e.
+ *    up to 2048 tokens at the full-K3 widths) creates, on first use by a
  *    host thread on a device, a second non-blocking stream of default
  *    priority for that thread and device, kept until the process ends.
  *  - Matrices (x, y, z, the padded tensor, u, du, dz, dy, dx and every weight
@@ -192,17 +193,18 @@ lmoe_status latentmoe_experts(const lmoe_dims* dims, const void* padded, int64_t
  * expert.  If C_host is not NULL the call waits on `stream`, writes
  * C = max counts there and returns LMOE_ERR_RANGE if an fp16 intermediate
  * left fp16's range; with C_host NULL the call is fully asynchronous: it
- * only enqueues kernels (and, below 2048 tokens, an event fork and join with
- * a second stream), so a caller may capture it in a HIP graph, and
- * latentmoe_forward_check reads the range flag afterwards.
+ * only enqueues kernels (and, on the overlapped path, an event fork and
+ * join with a second stream), so a caller may capture it in a HIP graph,
+ * and latentmoe_forward_check reads the range flag afterwards.
  * The routed experts read their rows straight from z through the sorted
  * pair order (the padded tensor is not materialised), skip empty experts and
  * padding rows, and the scatter-add is deterministic (each pair writes its own
- * slot; slots are summed in slot order).  For N <= 2048 the shared experts'
- * gate/up GEMM runs on a second, library-owned stream (one per calling host
- * thread and device), forked from and joined back into `stream` with events
- * (capturable as a fork/join in a HIP graph); all other work is on
- * `stream`. */
+ * slot; slots are summed in slot order).  When N d n_s f_s <= 2048 * 7168 *
+ * 18432 (the overlapped path: up to 2048 tokens at the full-K3 widths) the
+ * shared experts' gate/up GEMM runs on a second, library-owned stream (one
+ * per calling host thread and device), forked from and joined back into
+ * `stream` with events (capturable as a fork/join in a HIP graph); all other
+ * work is on `stream`. */
 lmoe_status latentmoe_forward(const lmoe_dims* dims, const lmoe_weights* weights, const void* x,
                               void* y, int32_t* ids, float* probs, int32_t* counts,
                               int64_t* C_host, void* workspace, size_t workspace_bytes,
@@ -321,7 +323,7 @@ lmoe_status latentmoe_router_losses(const lmoe_dims* dims, const float* logits, 
  *   3 dispatch (hist, scan, scatter)  7 slot sum + RMSNorm
  *   4 shared gate/up GEMM             8 merge GEMM [h_shared | RMSNorm(u)] -> y
  * The elapsed time between events[i-1] and events[i] is step i's device time.
- * All steps run in order on `stream` (latentmoe_forward, for N <= 2048,
+ * All steps run in order on `stream` (latentmoe_forward, on its overlapped path,
  * runs step 4 on a second stream of its own next to steps 1-3 and 5-7).  C is
  * not read back.  Otherwise identical to latentmoe_forward. */
 #define LMOE_FORWARD_TIMING_EVENTS 9

@@ -96,14 +96,14 @@ lmoe_status routed_recompute(const Plan& p, const lmoe_dims* dm, const void* z, 
                      int K, void* out, int64_t ldo) {
     return routed_grouped(p, dm, w, a, lda, bw, ldb, bstride, nrows, K, out, ldo);
   };
-  // 2. pre-activations of every pair, g = z W_g^T and up = z W_u^T (fp32,
+  // 2. pre-activations of every pair, g = z W_g^T and up = z W_u^T (type TI,
   // sorted rows), and the hidden h from one dual (gate, up) product
   const int64_t ez = sizeof(TZ);
   GemmArgs g = grouped(z, l * ez, w_g, l * es, (int64_t)f * l * es, f, l, w.hs, (int64_t)f * ei);
   g.b1 = (const char*)w_u;
-  g.pre_g = (char*)w.g;
-  g.pre_u = (char*)w.up;
-  g.pre_ld = (int64_t)f * 4;
+  g.pre_g = w.g;
+  g.pre_u = w.up;
+  g.pre_ld = (int64_t)f * ei;
   return gemm<TZ, T, TI, A_GATHER, B_DUAL, E_PRE>(g, tile, st);
 }
 
@@ -145,27 +145,28 @@ lmoe_status routed_gradients(const Plan& p, const lmoe_dims* dm, const void* z, 
   pair_vh_kernel<TI><<<(unsigned)P, 256, 0, st>>>(w.dh, (const TI*)w.hs, du, probs, w.order, p.k, l, f, dprobs,
                                                   (TI*)w.dout, w.sp);
   LMOE_HIP(hipGetLastError());
-  situ_backward_kernel<TI><<<(unsigned)std::min<int64_t>(P, 65536), 256, 0, st>>>(
-      w.dh, w.g, w.up, P, f, dm->beta1, dm->beta2, (TI*)w.dgu, 2 * (int64_t)f, 0, w.sp);
+  situ_backward_kernel<TI, TI><<<(unsigned)std::min<int64_t>(P, 65536), 256, 0, st>>>(
+      w.dh, (const TI*)w.g, (const TI*)w.up, P, f, dm->beta1, dm->beta2, (TI*)w.dgu, 2 * (int64_t)f, 0, w.sp);
   LMOE_HIP(hipGetLastError());
-  // 5. dz rows = [dg | du] [W_g ; W_u] (K = 2f: W_g's rows, then W_u's), summed per token
-  float* dzrows = w.o;  // o is consumed
+  // 5. dz rows = [dg | du] [W_g ; W_u] (K = 2f: W_g's rows, then W_u's; type
+  // TI), summed per token in fp32
+  TI* dzrows = (TI*)w.o;
   if constexpr (sizeof(T) == 2) {
-    GemmArgs g = grouped(w.dgu, 2 * f * ei, w_g, l * es, (int64_t)f * l * es, l, 2 * f, dzrows, (int64_t)l * 4);
+    GemmArgs g = grouped(w.dgu, 2 * f * ei, w_g, l * es, (int64_t)f * l * es, l, 2 * f, dzrows, (int64_t)l * ei);
     g.b1 = (const char*)w_u;
     g.kmaj_split = f;
-    LMOE_TRY((gemm<TI, T, float, A_SORTED, B_KMAJOR, E_STORE>(g, tile, st)));
+    LMOE_TRY((gemm<TI, T, TI, A_SORTED, B_KMAJOR, E_STORE>(g, tile, st)));
   } else {
     LMOE_TRY(transpose_batched<T>((const T*)w_g, (int64_t)f * l, l, f, l, (T*)w.w_guT, (int64_t)l * 2 * f,
                                    2 * f, 0, R, w.counts, st));
     LMOE_TRY(transpose_batched<T>((const T*)w_u, (int64_t)f * l, l, f, l, (T*)w.w_guT, (int64_t)l * 2 * f,
                                    2 * f, f, R, w.counts, st));
-    LMOE_TRY((gemm<TI, T, float, A_SORTED, B_SINGLE, E_STORE>(
+    LMOE_TRY((gemm<TI, T, TI, A_SORTED, B_SINGLE, E_STORE>(
         grouped(w.dgu, 2 * f * ei, w.w_guT, 2 * f * es, (int64_t)l * 2 * f * es, l, 2 * f, dzrows,
-                (int64_t)l * 4),
+                (int64_t)l * ei),
         tile, st)));
   }
-  pair_sum_kernel<TDZ><<<(unsigned)p.N, 256, 0, st>>>(dzrows, w.inv, p.k, l, (TDZ*)dz, ld_dz);
+  pair_sum_kernel<TI, TDZ><<<(unsigned)p.N, 256, 0, st>>>(dzrows, w.inv, p.k, l, (TDZ*)dz, ld_dz);
   LMOE_HIP(hipGetLastError());
   // 6. weight gradients: per expert, products over its pairs.  Up to
   // kWgradKMax pairs per expert, with 16-bit operands and 256-multiple
@@ -289,12 +290,12 @@ lmoe_status run_layer_backward(const Plan& p, const lmoe_dims* dm, const lmoe_we
   combine_rmsnorm_kernel<TI, TI><<<(unsigned)N, 256, 0, st>>>((const TI*)rw.o, p.k, l, w.u, W->rms_w,
                                                               dm->rms_eps, (TI*)w.rn, l, nullptr);
   LMOE_HIP(hipGetLastError());
-  if (nsf > 0) {  // the shared pre-activations (fp32) and hidden from one dual (gate, up) product
+  if (nsf > 0) {  // the shared pre-activations and hidden (type TI) from one dual (gate, up) product
     GemmArgs g = dense(x, d * es, (int)N, W->sh_g, d * es, nsf, d, w.hs, (int64_t)nsf * ei);
     g.b1 = (const char*)W->sh_u;
-    g.pre_g = (char*)w.ag;
-    g.pre_u = (char*)w.au;
-    g.pre_ld = (int64_t)nsf * 4;
+    g.pre_g = w.ag;
+    g.pre_u = w.au;
+    g.pre_ld = (int64_t)nsf * ei;
     LMOE_TRY((gemm<T, T, TI, A_DENSE, B_DUAL, E_PRE>(g, dense_tile(N, nsf, true), st)));
   }
   // ---- step 5 backward: dr = dy W_up, dh_shared = dy [S_o^j], RMSNorm backward
@@ -318,8 +319,8 @@ lmoe_status run_layer_backward(const Plan& p, const lmoe_dims* dm, const lmoe_we
     LMOE_TRY((gemm<T, T, float, A_DENSE, B_SINGLE, E_STORE>(dense(dy, d * es, (int)N, w.shoT, d * es, nsf, d,
                                                                   w.dhs, (int64_t)nsf * 4),
                                                             dense_tile(N, nsf, false), st)));
-    situ_backward_kernel<TI><<<(unsigned)std::min<int64_t>(N, 65536), 256, 0, st>>>(
-        w.dhs, w.ag, w.au, N, nsf, dm->beta1, dm->beta2, (TI*)w.dcat, kcat, l + rpad, nullptr);
+    situ_backward_kernel<TI, TI><<<(unsigned)std::min<int64_t>(N, 65536), 256, 0, st>>>(
+        w.dhs, (const TI*)w.ag, (const TI*)w.au, N, nsf, dm->beta1, dm->beta2, (TI*)w.dcat, kcat, l + rpad, nullptr);
     LMOE_HIP(hipGetLastError());
   }
   // ---- step 3 backward (routed block) -> dz into dcat[:, :l], dprobs

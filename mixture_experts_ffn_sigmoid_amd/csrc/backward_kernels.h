@@ -280,21 +280,22 @@ __global__ __launch_bounds__(256) void convert_kernel(const float* __restrict__ 
 // row_scale, row q's dh is multiplied by row_scale[q] first.
 // Workgroups stride over rows and threads over columns (no index division);
 // tanh and sigma from the hardware exp and reciprocal (absolute error ~1e-7).
-template <typename TD>
-__global__ __launch_bounds__(256) void situ_backward_kernel(const float* __restrict__ dh, const float* __restrict__ g,
-                                                            const float* __restrict__ u, int64_t rows, int f,
+// TP: type of the stored pre-activations (read as fp32).
+template <typename TP, typename TD>
+__global__ __launch_bounds__(256) void situ_backward_kernel(const float* __restrict__ dh, const TP* __restrict__ g,
+                                                            const TP* __restrict__ u, int64_t rows, int f,
                                                             float beta1, float beta2, TD* __restrict__ dgu,
                                                             int64_t ld, int64_t col0,
                                                             const float* __restrict__ row_scale) {
   const float ib1 = 1.0f / beta1, ib2 = 1.0f / beta2;
   for (int64_t q = blockIdx.x; q < rows; q += gridDim.x) {
-    const float* gq = g + q * f;
-    const float* uq = u + q * f;
+    const TP* gq = g + q * f;
+    const TP* uq = u + q * f;
     const float* dq = dh + q * f;
     const float rs = row_scale ? row_scale[q] : 1.0f;
     TD* out = dgu + q * ld + col0;
     for (int j = threadIdx.x; j < f; j += 256) {
-      const float a = gq[j], b = uq[j], d = dq[j] * rs;
+      const float a = Elem<TP>::load(gq + j), b = Elem<TP>::load(uq + j), d = dq[j] * rs;
       const float tg = tanh_fast(a * ib1), tu = tanh_fast(b * ib2);
       const float sg = rcp_fast(1.0f + __expf(-a));
       const float gate = beta1 * tg * sg, up = beta2 * tu;
@@ -313,23 +314,32 @@ __global__ __launch_bounds__(256) void inverse_order_kernel(const int32_t* __res
   if (i < pairs) inv[order[i]] = (int32_t)i;
 }
 
-// dz[n] (row stride ld) = sum over slots j (in slot order) of rows[inv[n k + j]],
-// one workgroup per token; top_k <= 64.  16-byte row loads where rows and
-// ell allow them.
-template <typename TD>
-__global__ __launch_bounds__(256) void pair_sum_kernel(const float* __restrict__ rows, const int32_t* __restrict__ inv,
+// dz[n] (row stride ld) = sum over slots j (in slot order) of rows[inv[n k + j]]
+// (rows of type TS, summed in fp32), one workgroup per token; top_k <= 64.
+// Four-element row loads where rows and ell allow them.
+template <typename TS, typename TD>
+__global__ __launch_bounds__(256) void pair_sum_kernel(const TS* __restrict__ rows, const int32_t* __restrict__ inv,
                                                        int top_k, int ell, TD* __restrict__ dz, int64_t ld) {
   const int64_t n = blockIdx.x;
   __shared__ int64_t src[64];  // first element of each slot's row
   if ((int)threadIdx.x < top_k) src[threadIdx.x] = (int64_t)inv[n * top_k + threadIdx.x] * ell;
   __syncthreads();
   TD* out = dz + n * ld;
-  if ((((uintptr_t)rows) & 15) == 0 && (ell & 3) == 0) {  // uniform
+  if ((((uintptr_t)rows) & (4 * sizeof(TS) - 1)) == 0 && (ell & 3) == 0) {  // uniform
     for (int c = 4 * (int)threadIdx.x; c < ell; c += 4 * 256) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
       for (int j = 0; j < top_k; ++j) {
-        const f32x4 v = *(const f32x4*)(rows + src[j] + c);
+        const TS* p = rows + src[j] + c;
+        f32x4 v;
+        if constexpr (sizeof(TS) == 4) {
+          v = *(const f32x4*)p;
+        } else {
+          TS t4[4];
+          *(u32x2*)t4 = *(const u32x2*)p;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] = Elem<TS>::load(t4 + q);
+        }
 #pragma unroll
         for (int q = 0; q < 4; ++q) acc[q] += v[q];
       }
@@ -339,7 +349,7 @@ __global__ __launch_bounds__(256) void pair_sum_kernel(const float* __restrict__
   } else {
     for (int c = threadIdx.x; c < ell; c += 256) {
       float acc = 0.f;
-      for (int j = 0; j < top_k; ++j) acc += rows[src[j] + c];
+      for (int j = 0; j < top_k; ++j) acc += Elem<TS>::load(rows + src[j] + c);
       Elem<TD>::store(out + c, acc);
     }
   }

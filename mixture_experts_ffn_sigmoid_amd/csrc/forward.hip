@@ -136,11 +136,11 @@ lmoe_status run_forward(const Plan& p, const lmoe_dims* dm, const lmoe_weights* 
   // not a memset node, so a captured forward replays correctly)
   set_ints_kernel<<<1, 64, 0, st>>>(w.meta, 0, 0, 0, 0);
   LMOE_HIP(hipGetLastError());
-  // The shared experts depend on x only.  For small batches (whose GEMMs
-  // leave most CUs idle) and without timing marks they run on a second
-  // stream, next to steps 1-3 and the routed experts; the merge GEMM waits
-  // for both.  Large batches fill the chip with each GEMM alone, and their
-  // 128-132 KB LDS tiles cannot share a CU, so there they run in order.
+  // The shared experts depend on x only.  For small products (whose GEMMs
+  // leave CUs idle; shared_overlaps) and without timing marks they run on a
+  // second stream, next to steps 1-3 and the routed experts; the merge GEMM
+  // waits for both.  Large ones fill the chip with each GEMM alone, and their
+  // 128-144 KB LDS tiles cannot share a CU, so there they run in order.
   hipStream_t side = st;
   struct Events {
     hipEvent_t fork = nullptr, join = nullptr;
@@ -149,7 +149,7 @@ lmoe_status run_forward(const Plan& p, const lmoe_dims* dm, const lmoe_weights* 
       if (join) (void)hipEventDestroy(join);
     }
   } evs;
-  const bool overlap = ev == nullptr && !one_stream && p.ns > 0 && p.N <= kOverlapMaxTokens;
+  const bool overlap = ev == nullptr && !one_stream && shared_overlaps(p);
   if (overlap) {
     LMOE_TRY(side_stream(&side));
     LMOE_HIP(hipEventCreateWithFlags(&evs.fork, hipEventDisableTiming));

@@ -38,7 +38,8 @@
 //   E_STORE   plain store (fp32 or storage dtype), masked to valid rows/cols
 //   E_SITU    SiTU-GLU hidden of the (gate, up) accumulator pair, stored as OutT
 //   E_PRE     E_SITU that also stores the gate and up accumulators themselves
-//             (fp32 pre-activations at pre_g / pre_u, rows like the hidden's)
+//             (pre-activations at pre_g / pre_u in the hidden's type, rows like
+//             the hidden's)
 //   E_SLOTS   p-weighted result of sorted pair q written to its own slot row q
 // Runtime options (A_DENSE with E_STORE):
 //   split K (ksplit > 1): the grid also runs over K slices of kslice steps,
@@ -119,7 +120,7 @@ struct GemmArgs {
   int64_t ldo;  // bytes per output row (E_SLOTS: per slot row)
   const float* probs;
   float beta1, beta2;
-  // E_PRE: fp32 gate / up pre-activations, row stride pre_ld bytes
+  // E_PRE: gate / up pre-activations (type OutT), row stride pre_ld bytes
   char* pre_g;
   char* pre_u;
   int64_t pre_ld;
@@ -806,9 +807,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_kernel(const GemmArgs arg
         for (int v = 0; v < 16; ++v) {
           const int r = wm * WTM + i * 32 + 8 * (v >> 2) + 4 * lh + (v & 3);
           if (r >= rows_valid) continue;
-          const int64_t o = out_row(r) * args.pre_ld + (int64_t)col * 4;
-          *(float*)(args.pre_g + o) = acc[i][j][v];
-          *(float*)(args.pre_u + o) = acc[i][j + TN / 2][v];
+          const int64_t o = out_row(r) * args.pre_ld + (int64_t)col * (int64_t)sizeof(OutT);
+          Elem<OutT>::store((OutT*)(args.pre_g + o), acc[i][j][v]);
+          Elem<OutT>::store((OutT*)(args.pre_u + o), acc[i][j + TN / 2][v]);
         }
       }
   }

@@ -322,7 +322,9 @@ size_t carve_forward(const Plan& p, char* b, ForwardWs* w) {
 // of kr_len).
 struct RoutedBwdWs {
   int32_t *counts, *offsets, *order, *chunk_hist, *chunk_bad, *meta, *tile_list, *inv, *kr_off, *kr_len;
-  float *g, *up, *o, *dh;  // o: the layer backward's slot rows, then the dz rows; dh: v = W_o^T du per pair
+  char *g, *up;  // gate / up pre-activations (intermediate type)
+  char* o;       // the layer backward's slot rows, then the dz rows (intermediate type)
+  float* dh;     // v = W_o^T du per pair
   float* sp;               // probs of the sorted pairs
   char* du16;              // du in the intermediate type (16-bit operands of v)
   char *hs, *dout, *dgu;   // intermediate type
@@ -344,9 +346,9 @@ size_t carve_routed_backward(const Plan& p, char* b, RoutedBwdWs* w) {
   w->inv = c.take<int32_t>((size_t)P * 4);
   w->kr_off = c.take<int32_t>((size_t)p.R * 4);
   w->kr_len = c.take<int32_t>((size_t)p.R * 4);
-  w->g = c.take<float>((size_t)P * p.fr * 4);
-  w->up = c.take<float>((size_t)P * p.fr * 4);
-  w->o = c.take<float>((size_t)P * p.l * 4);
+  w->g = c.take<char>((size_t)P * p.fr * ei);
+  w->up = c.take<char>((size_t)P * p.fr * ei);
+  w->o = c.take<char>((size_t)P * p.l * ei);
   w->dh = c.take<float>((size_t)P * p.fr * 4);
   w->sp = c.take<float>((size_t)P * 4);
   w->du16 = c.take<char>(ei == 2 ? (size_t)p.N * p.l * ei : 0);
@@ -373,7 +375,8 @@ struct LayerBwdWs {
   RoutedBwdWs rw;
   int64_t rpad, nsf, kcat, npad, rms_chunk;
   char *z, *rn, *hs, *dcat;            // intermediate type
-  float *logits, *u, *ag, *au, *dr, *dhs, *du, *rho, *dprobs, *rms_part;
+  float *logits, *u, *dr, *dhs, *du, *rho, *dprobs, *rms_part;
+  char *ag, *au;  // shared gate / up pre-activations (intermediate type)
   char *w_upT, *shoT, *w_downT, *w_rT, *sgT, *suT;  // storage type
   int32_t* seg;
   char *dyT, *rnT, *hsT, *dcatT, *xT;  // intermediate type
@@ -396,8 +399,8 @@ size_t carve_layer_backward(const Plan& p, char* b, LayerBwdWs* w) {
   w->dcat = c.take<char>((size_t)N * w->kcat * ei);
   w->logits = c.take<float>((size_t)N * p.R * 4);
   w->u = c.take<float>((size_t)N * p.l * 4);
-  w->ag = c.take<float>((size_t)N * w->nsf * 4);
-  w->au = c.take<float>((size_t)N * w->nsf * 4);
+  w->ag = c.take<char>((size_t)N * w->nsf * p.es);
+  w->au = c.take<char>((size_t)N * w->nsf * p.es);
   w->dr = c.take<float>((size_t)N * p.l * 4);
   w->dhs = c.take<float>((size_t)N * w->nsf * 4);
   w->du = c.take<float>((size_t)N * p.l * 4);
@@ -428,8 +431,15 @@ size_t carve_layer_backward(const Plan& p, char* b, LayerBwdWs* w) {
 // fp16 intermediate of the forward left fp16's range).
 constexpr int kMetaC = 0, kMetaTiles = 1, kMetaBadIds = 2, kMetaRange = 3;
 
-// Largest batch whose shared-expert GEMM runs on the second stream.
-constexpr int64_t kOverlapMaxTokens = 2048;
+// The shared-expert gate/up GEMM runs on the second stream while its
+// multiply-adds N d n_s f_s stay at or below those of 2048 tokens at the
+// full-K3 widths (d = 7168, one shared expert of f_s = 18432): up to there the
+// layer's GEMMs leave compute units idle between launches; past it each fills
+// the chip alone and their 128-144 KB LDS tiles cannot share a CU.
+constexpr double kOverlapMaxSharedMacs = 2048.0 * 7168.0 * 18432.0;
+inline bool shared_overlaps(const Plan& p) {
+  return p.ns > 0 && (double)p.N * p.d * p.ns * p.fs <= kOverlapMaxSharedMacs;
+}
 
 // A second stream on which the shared-expert GEMM overlaps the routed
 // experts: default priority, non-blocking, created on first use for each

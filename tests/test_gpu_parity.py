@@ -250,16 +250,17 @@ def _ids_case(rng, N, R, k, skew=False):
     return ids.astype(np.int32)
 
 
-@pytest.mark.parametrize("name", ["b05_n4096", "toy_n128"])
+@pytest.mark.parametrize("name", ["k3full_n8192", "toy_n128"])
 def test_forward_graph_replay_matches_eager(name):
     """Without the capacity read-back the forward is launches only (no host
     sync, no memset, no allocation), so a caller can capture it in a HIP graph.
     Captured once and replayed three times, with eager work and
     synchronisations between the replays and the outputs poisoned before each:
     every replay equals the eager forward bit for bit (the kernels are
-    deterministic).  At N = 4096 the capture holds one stream; at N = 128 the
-    shared experts run on the library's second stream, forked and joined with
-    events inside the capture."""
+    deterministic).  At the full-K3 prefill size (8192 tokens) the capture
+    holds one stream; on the toy layer the shared experts run on the
+    library's second stream, forked and joined with events inside the
+    capture."""
     cfg = S.CONFIGS[name]
     _say(f"[graph] {cfg.name}")
     dev = G.device_layer_inputs(cfg)
@@ -293,9 +294,10 @@ def test_forward_graph_replay_matches_eager(name):
 
 
 def test_forward_capture_alongside_another_thread():
-    """The overlapped path (N <= 2048) forks onto a second stream per host
-    thread: while thread A captures the forward into a graph (thread-local
-    capture mode), thread B keeps running eager forwards on its own stream.
+    """The overlapped path (small shared products) forks onto a second stream
+    per host thread: while thread A captures the forward into a graph
+    (thread-local capture mode), thread B keeps running eager forwards on its
+    own stream.
     B's results and every replay of A's graph equal the eager reference."""
     import threading
 
