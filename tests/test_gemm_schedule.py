@@ -17,8 +17,9 @@ The one-barrier schedule of gemm_kernel (dense 16-bit products on two-stage
 rings): the prologue issues step 0 into stage 0 and waits for it; step kt
 reads stage kt % 2, issues step kt + 1 (past the end: a reload of step KT - 1)
 into the other stage and ends with vmcnt(0) and the barrier.
-wgrad_kernel (csrc/wgrad_kernel.h): the A strip and B(0), then per column tile
-t: wait for B(t), issue B(t+1) into the other buffer, multiply, stage, 8 stores.
+wgrad_kernel (csrc/wgrad_kernel.h): the A strip in two halves (each waited for
+and read before the next), then B(0); per column tile t: wait for B(t), issue
+B(t+1) into the other buffer, multiply, stage, 8 stores.
 
 The tail split of the dense 256 x 256 products (gemm_kernel's tsplit,
 tail_split_plan and tail_reduce_kernel in csrc/lmoe_host.h and
@@ -113,14 +114,15 @@ def onebar_schedule(KT, A_W, B_W, wait_delta=0):
             assert landed(kt + 1, wait_delta), (KT, kt)
 
 
-def wgrad_schedule(KG, NT, wait_delta=0, stores=8, nwave=8):
-    """Replays wgrad_kernel's issue order per wave: the A strip's two 128-row
-    blocks (into B buffer 1 and the staging buffer), B tile 0 (into B buffer
-    0), a wait for the strip; per column tile t: wait for B(t), B tile t+1 into
+def wgrad_schedule(KG, NT, wait_delta=0, stores=8, nwave=4):
+    """Replays wgrad_kernel's issue order per wave: the A strip's two 128-column
+    halves in turn (each into the space of both B buffers, waited for with
+    vmcnt(0) and read into registers before the next is issued), B tile 0
+    (into B buffer 0); per column tile t: wait for B(t), B tile t+1 into
     buffer (t+1) % 2, multiply from buffer t % 2, stage, the stores of tile t.
     Also checks that no DMA still in flight targets a buffer being read or
     staged into."""
-    dma = KG * (8 // nwave)  # DMA instructions per 128-row block per wave
+    dma = KG * (4 // nwave)  # DMA instructions per B tile per wave (an A half: 2 dma)
     issued, last = [], {}    # issued: (tag, target buffer or None)
 
     def issue(tag, n, buf=None):
@@ -130,12 +132,11 @@ def wgrad_schedule(KG, NT, wait_delta=0, stores=8, nwave=8):
     def in_flight(n):  # what may still be outstanding after vmcnt(n)
         return issued[len(issued) - n:] if n > 0 else []
 
-    issue(("A", 0), dma, 1)
-    issue(("A", 1), dma, "S")
+    for h in range(2):
+        issue(("A", h), 2 * dma, "AB")
+        n = wait_delta
+        assert last[("A", h)] < len(issued) - n, (KG, NT, h)  # the half is read
     issue(("B", 0), dma, 0)
-    n = dma + wait_delta
-    assert last[("A", 1)] < len(issued) - n, (KG, NT)  # the strip is read
-    assert all(b not in (1, "S") for _, b in in_flight(n))
     for t in range(NT):
         n = (0 if t == 0 else stores) + wait_delta
         assert last[("B", t)] < len(issued) - n, (KG, NT, t)
@@ -144,7 +145,7 @@ def wgrad_schedule(KG, NT, wait_delta=0, stores=8, nwave=8):
             issue(("B", t + 1), dma, (t + 1) % 2)
             flying = flying + issued[-dma:]
         # the MFMAs read buffer t % 2 and the staging writes "S"
-        assert all(b not in (t % 2, "S") for _, b in flying), (KG, NT, t)
+        assert all(b not in (t % 2, "S", "AB") for _, b in flying), (KG, NT, t)
         issue(("S", t), stores)
 
 
